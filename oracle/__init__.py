@@ -1,0 +1,148 @@
+"""FP64 CPU oracle of MLA decode over an FP8 E4M3 latent cache (ctypes wrapper of mla_oracle.c).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package. It shares no code with the HIP library.
+
+What it computes, and the passages of the vLLM API pages it follows, is stated in the header of
+``mla_oracle.c``. Modes:
+
+* ``EXACT``  -- the textbook softmax definition (LSE = ln sum exp, o = softmax-weighted V).
+* ``ONLINE`` -- the pages' split / chunked base-2 online softmax and FP32-style merge, P unrounded.
+* ``METHOD`` -- as ``ONLINE`` with P rounded to E4M3 at the 448 anchor of the running maximum.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+EXACT, ONLINE, METHOD = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB = os.path.join(_HERE, "libmla_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile mla_oracle.c with gcc (-O2, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fPIC", "-shared",
+             "-o", tmp, _SRC, "-lpthread", "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        lib.mo_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.mo_e4m3_decode.restype = ctypes.c_double
+        lib.mo_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.mo_e4m3_encode.restype = ctypes.c_uint8
+        lib.mo_bf16_decode.argtypes = [ctypes.c_uint16]
+        lib.mo_bf16_decode.restype = ctypes.c_double
+        lib.mo_dense.argtypes = [P, i32, i32, i32, P, i64, i32, f32, P, i32, P, f32, i32, i32, i32,
+                                 P, i64, i32, P, P]
+        lib.mo_dense.restype = i32
+        lib.mo_sparse.argtypes = [P, i32, i32, i32, P, i64, f32, P, i32, P, f32, i32, i32, i32,
+                                  P, i64, i32, P, P]
+        lib.mo_sparse.restype = i32
+        _lib = lib
+    return _lib
+
+
+def e4m3_decode(code: int) -> float:
+    return _load().mo_e4m3_decode(code)
+
+
+def e4m3_encode(x: float) -> int:
+    return _load().mo_e4m3_encode(float(x))
+
+
+def bf16_decode(bits: int) -> float:
+    return _load().mo_bf16_decode(bits)
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _threads(threads):
+    if threads is not None:
+        return int(threads)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _as(a, dtype):
+    return np.ascontiguousarray(np.asarray(a), dtype=dtype)
+
+
+def _outputs(B, Q, H, sel):
+    n = B * Q * H if sel is None else len(sel)
+    return np.zeros((n, 512), np.float64), np.zeros((n,), np.float64)
+
+
+def _sel(sel):
+    return None if sel is None else _as(sel, np.int64)
+
+
+def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=METHOD, splits=1,
+          chunk=128, sel=None, threads=None):
+    """Paged dense decode. ``q_bits`` uint16 bf16 bits [B,Q,H,576]; ``kv`` uint8 [num_rows,576];
+    ``block_table`` int32 [B,max_pages]; ``seq_lens`` int32 [B].
+
+    Returns ``(o, lse)`` in float64: ``o`` [B,Q,H,512] and ``lse`` [B,Q,H], or [n,512] / [n] for a
+    ``sel`` list of flat rows ``(b*Q+i)*H+h``."""
+    q_bits = _as(q_bits, np.uint16)
+    B, Q, H, D = q_bits.shape
+    assert D == 576
+    kv = _as(kv, np.uint8).reshape(-1, 576)
+    table = _as(block_table, np.int32)
+    seq = _as(seq_lens, np.int32)
+    assert table.shape[0] == B and seq.shape == (B,)
+    sel = _sel(sel)
+    o, lse = _outputs(B, Q, H, sel)
+    rc = _load().mo_dense(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], int(page_size),
+                          float(k_scale), _ptr(table), table.shape[1], _ptr(seq), float(scale),
+                          int(mode), int(splits), int(chunk), _ptr(sel),
+                          0 if sel is None else len(sel), _threads(threads), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle: bad arguments")
+    if sel is None:
+        return o.reshape(B, Q, H, 512), lse.reshape(B, Q, H)
+    return o, lse
+
+
+def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, chunk=128, sel=None,
+           threads=None):
+    """Top-k sparse decode. ``rows`` int32 [B,Q,K] flat cache rows; ``valid`` int32 [B,Q]."""
+    q_bits = _as(q_bits, np.uint16)
+    B, Q, H, D = q_bits.shape
+    assert D == 576
+    kv = _as(kv, np.uint8).reshape(-1, 576)
+    rows = _as(rows, np.int32)
+    valid = _as(valid, np.int32)
+    assert rows.shape[:2] == (B, Q) and valid.shape == (B, Q)
+    sel = _sel(sel)
+    o, lse = _outputs(B, Q, H, sel)
+    rc = _load().mo_sparse(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], float(k_scale),
+                           _ptr(rows), rows.shape[2], _ptr(valid), float(scale), int(mode),
+                           int(splits), int(chunk), _ptr(sel), 0 if sel is None else len(sel),
+                           _threads(threads), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle: bad arguments")
+    if sel is None:
+        return o.reshape(B, Q, H, 512), lse.reshape(B, Q, H)
+    return o, lse

@@ -1,0 +1,429 @@
+/*
+ * mla_oracle.c -- plain FP64 CPU oracle of MLA decode attention over an FP8 E4M3 latent cache.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke entry point and the benchmark's CPU-baseline leg
+ * load this library. It shares no code, header, table or helper with the HIP library; it is slow on
+ * purpose and written to be checked against the pages by eye.
+ *
+ * Sources (vLLM API documentation pages; cited by page title and section):
+ *   [SPARSE]  vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.attn_sparse
+ *             - module docstring: 576-byte cache rows (512 latent bytes = V, then 64 rope bytes);
+ *               the per-chunk online softmax in base 2 with the running maximum; P anchored at 448
+ *               times the exponential of the logit minus the running maximum, rounded to E4M3
+ *               (round to nearest, saturating); FP32 sums of the P before rounding; the merge that
+ *               weights each split by exp2(its max - the top max), divides by the total and scales by
+ *               k_scale, with LSE = max + log2(total / 448) reported in natural log.
+ *             - module docstring, last paragraph: rows with no key write zeros and LSE = -inf.
+ *             - SparseDcpDecode.kernel: a row's count is clamped to [0, width]; split s of SPLIT takes
+ *               keys [s*per, min(n, (s+1)*per)) with per = ceil(n / SPLIT), in chunks of CHUNK keys.
+ *             - SparseDcpDecode.merge: the fixed-order FP32 combine of the splits.
+ *   [AMD]     vllm.models.kimi_k3.amd.specialized_decode.mono.attention.mla_attn
+ *             - module docstring: position i of a request's qlen query rows sees keys up to
+ *               seq_len - qlen + i; a split with no visible key leaves LSE = -inf and o = 0.
+ *             - fp8_unpack4: E4M3 to f32 is exact.
+ *
+ * Three modes of the same computation for one query row (b, i, h):
+ *   MO_EXACT      the textbook definition: LSE = ln sum_j exp(x_j), o = sum_j softmax(x)_j V_j, with
+ *                 x_j = scale * q . K_j, K_j = k_scale * dec(K bytes), V_j = k_scale * dec(V bytes).
+ *   MO_ONLINE     the pages' split / chunked online softmax and merge, P not rounded (equals MO_EXACT
+ *                 up to FP64 rounding for every split plan: the split-merge identity).
+ *   MO_METHOD     MO_ONLINE with each P rounded to E4M3 before it multiplies V. The rounding decision
+ *                 is taken on P rounded to FP32, the precision the pages compute P in.
+ *
+ * Readings of the pages this oracle takes (each also listed in the design notes):
+ *   - the causal bound is inclusive: row i sees n_i = seq_len - qlen + i + 1 keys (clamped to
+ *     [0, seq_len]);
+ *   - dense splits divide the request's seq_len keys (the KV a split streams); a row masks the keys
+ *     past its own causal bound inside them;
+ *   - a key whose cache row falls outside [0, num_rows) (an index outside the cache, a page outside
+ *     the pool) is absent: it contributes nothing and is never read;
+ *   - one per-tensor k_scale dequantizes K (all 576 bytes) and V;
+ *   - the softmax scale multiplies q . K; the LSE excludes the 448 anchor.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define MO_ROW 576    /* bytes of a cache row */
+#define MO_LATENT 512 /* latent bytes = V width */
+
+enum { MO_EXACT = 0, MO_ONLINE = 1, MO_METHOD = 2 };
+
+/* ---- number formats --------------------------------------------------------------------------- */
+
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0 is subnormal (m * 2^-9);
+ * 0x7F / 0xFF are NaN; no infinity. */
+double mo_e4m3_decode(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Round to the nearest E4M3 value, ties to an even mantissa; magnitudes of 448 and above saturate to
+ * 448 (the "satfinite" conversion); NaN maps to 0x7F. */
+uint8_t mo_e4m3_encode(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7F;
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: multiples of 2^-9 */
+        double t = a * 512.0;
+        double r = nearbyint(t); /* default rounding mode: to nearest, ties to even */
+        int m = (int)r;          /* 0..8; 8 is the smallest normal, code 0x08 */
+        return sign | (uint8_t)m;
+    }
+    int e;
+    double f = frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+    int exp_unbiased = e - 1; /* a = (2f) * 2^(e-1), 2f in [1, 2) */
+    double t = (2.0 * f - 1.0) * 8.0; /* mantissa in units of 1/8, in [0, 8) */
+    int m = (int)nearbyint(t);
+    if (m == 8) {
+        m = 0;
+        exp_unbiased += 1;
+    }
+    int be = exp_unbiased + 7;
+    if (be > 15 || (be == 15 && m == 7))
+        return sign | 0x7E; /* only reachable by rounding up to 480: saturate */
+    return sign | (uint8_t)((be << 3) | m);
+}
+
+/* bfloat16 bits -> value (exact) */
+double mo_bf16_decode(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+/* ---- one query row ---------------------------------------------------------------------------- */
+
+typedef struct {
+    int mode;
+    int splits; /* S >= 1 */
+    int chunk;  /* keys per chunk >= 1 */
+} mo_plan;
+
+/* x_j before the softmax scale: q . dec(K_j) over all 576 bytes (k_scale applied by the caller). */
+static double dot_qk(const double* qd, const uint8_t* krow)
+{
+    double acc = 0.0;
+    for (int c = 0; c < MO_ROW; c++)
+        acc += qd[c] * mo_e4m3_decode(krow[c]);
+    return acc;
+}
+
+/*
+ * One query row against its group's ordered key list.
+ *   keyrow[j]  cache row of key j (j < n_group), or -1 when the key is absent;
+ *   n_visible  keys [0, n_visible) may be seen by this row (causal bound), n_visible <= n_group.
+ * Writes o[512] and *lse.
+ */
+static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow, int n_group,
+                     int n_visible, double scale, double k_scale, const mo_plan* plan, double* o,
+                     double* lse)
+{
+    double qd[MO_ROW];
+    for (int c = 0; c < MO_ROW; c++)
+        qd[c] = mo_bf16_decode(q[c]);
+    for (int c = 0; c < MO_LATENT; c++)
+        o[c] = 0.0;
+
+    if (plan->mode == MO_EXACT) {
+        /* textbook softmax over the visible, present keys */
+        double xmax = -INFINITY;
+        int any = 0;
+        double* x = (double*)malloc(sizeof(double) * (n_visible > 0 ? n_visible : 1));
+        for (int j = 0; j < n_visible; j++) {
+            if (keyrow[j] < 0)
+                continue;
+            const uint8_t* kr = kv + (size_t)keyrow[j] * MO_ROW;
+            double qk = 0.0;
+            for (int c = 0; c < MO_ROW; c++)
+                qk += qd[c] * (k_scale * mo_e4m3_decode(kr[c]));
+            x[j] = scale * qk;
+            if (x[j] > xmax)
+                xmax = x[j];
+            any = 1;
+        }
+        if (!any) {
+            *lse = -INFINITY;
+            free(x);
+            return;
+        }
+        double z = 0.0;
+        for (int j = 0; j < n_visible; j++) {
+            if (keyrow[j] < 0)
+                continue;
+            const uint8_t* vr = kv + (size_t)keyrow[j] * MO_ROW;
+            double w = exp(x[j] - xmax);
+            z += w;
+            for (int c = 0; c < MO_LATENT; c++)
+                o[c] += w * (k_scale * mo_e4m3_decode(vr[c]));
+        }
+        for (int c = 0; c < MO_LATENT; c++)
+            o[c] /= z;
+        *lse = xmax + log(z);
+        free(x);
+        return;
+    }
+
+    /* The split / chunked online softmax (MO_ONLINE, MO_METHOD), logits in log2 units. */
+    const double log2e = 1.0 / log(2.0);
+    const double anchor = 448.0;
+    const int S = plan->splits;
+    double* m_s = (double*)malloc(sizeof(double) * S);
+    double* l_s = (double*)malloc(sizeof(double) * S);
+    double* O_s = (double*)calloc((size_t)S * MO_LATENT, sizeof(double));
+    double* x2 = (double*)malloc(sizeof(double) * (plan->chunk > 0 ? plan->chunk : 1));
+    double* p = (double*)malloc(sizeof(double) * (plan->chunk > 0 ? plan->chunk : 1));
+
+    int n = n_group;
+    int per = (n + S - 1) / S;
+    for (int s = 0; s < S; s++) {
+        int first = s * per < n ? s * per : n;
+        int mine = n - first < per ? n - first : per;
+        double m = -INFINITY, l = 0.0;
+        double* O = O_s + (size_t)s * MO_LATENT;
+        for (int base = first; base < first + mine; base += plan->chunk) {
+            int count = first + mine - base < plan->chunk ? first + mine - base : plan->chunk;
+            /* logits of the chunk; -inf for keys the row may not see or that are absent */
+            double cmax = -INFINITY;
+            for (int t = 0; t < count; t++) {
+                int j = base + t;
+                if (j >= n_visible || keyrow[j] < 0) {
+                    x2[t] = -INFINITY;
+                    continue;
+                }
+                const uint8_t* kr = kv + (size_t)keyrow[j] * MO_ROW;
+                x2[t] = scale * k_scale * dot_qk(qd, kr) * log2e;
+                if (x2[t] > cmax)
+                    cmax = x2[t];
+            }
+            double m_new = m > cmax ? m : cmax;
+            if (m_new == -INFINITY)
+                continue; /* nothing visible yet: O and l stay zero */
+            double alpha = (m == -INFINITY) ? 1.0 : exp2(m - m_new);
+            /* P anchored at 448 of the running maximum; the row sum takes the unrounded P (FP32 on
+             * the pages, FP64 here) */
+            double total = 0.0;
+            for (int t = 0; t < count; t++) {
+                p[t] = (x2[t] == -INFINITY) ? 0.0 : anchor * exp2(x2[t] - m_new);
+                total += p[t];
+            }
+            l = l * alpha + total;
+            for (int c = 0; c < MO_LATENT; c++)
+                O[c] *= alpha;
+            for (int t = 0; t < count; t++) {
+                if (p[t] == 0.0)
+                    continue;
+                double pq = p[t];
+                if (plan->mode == MO_METHOD)
+                    pq = mo_e4m3_decode(mo_e4m3_encode((double)(float)p[t]));
+                const uint8_t* vr = kv + (size_t)keyrow[base + t] * MO_ROW;
+                for (int c = 0; c < MO_LATENT; c++)
+                    O[c] += pq * mo_e4m3_decode(vr[c]);
+            }
+            m = m_new;
+        }
+        m_s[s] = m;
+        l_s[s] = l;
+    }
+
+    /* merge of the splits in split order */
+    double top = -INFINITY;
+    for (int s = 0; s < S; s++)
+        if (m_s[s] > top)
+            top = m_s[s];
+    if (top == -INFINITY) {
+        *lse = -INFINITY;
+    } else {
+        double total = 0.0;
+        for (int s = 0; s < S; s++) {
+            double w = (m_s[s] == -INFINITY) ? 0.0 : exp2(m_s[s] - top);
+            total += w * l_s[s];
+            for (int c = 0; c < MO_LATENT; c++)
+                o[c] += w * O_s[(size_t)s * MO_LATENT + c];
+        }
+        for (int c = 0; c < MO_LATENT; c++)
+            o[c] = o[c] * k_scale / total;
+        *lse = (top - log2(anchor) + log2(total)) * log(2.0);
+    }
+    free(m_s);
+    free(l_s);
+    free(O_s);
+    free(x2);
+    free(p);
+}
+
+/* ---- dense (paged) and sparse (index list) front ends ------------------------------------------ */
+
+typedef struct {
+    int dense;
+    const uint16_t* q;
+    int B, Q, H;
+    const uint8_t* kv;
+    int64_t num_rows;
+    int page_size;
+    const int32_t* table;
+    int max_pages;
+    const int32_t* seq_lens;
+    const int32_t* rows;
+    int K;
+    const int32_t* valid;
+    double scale, k_scale;
+    mo_plan plan;
+    const int64_t* sel;
+    int64_t n_items;
+    double* o;
+    double* lse;
+    int nthreads;
+    int tid;
+} mo_job;
+
+static int clampi(long long v, long long lo, long long hi)
+{
+    return (int)(v < lo ? lo : (v > hi ? hi : v));
+}
+
+static void eval_item(const mo_job* jb, int64_t item)
+{
+    int64_t flat = jb->sel ? jb->sel[item] : item; /* (b * Q + i) * H + h */
+    int i = (int)((flat / jb->H) % jb->Q);
+    int b = (int)(flat / ((int64_t)jb->H * jb->Q));
+    const uint16_t* q = jb->q + (size_t)flat * MO_ROW;
+    int n_group, n_visible;
+    int64_t* keyrow;
+    if (jb->dense) {
+        long long cap = (long long)jb->max_pages * jb->page_size;
+        n_group = clampi(jb->seq_lens[b], 0, cap);
+        n_visible = clampi((long long)n_group - jb->Q + i + 1, 0, n_group);
+        keyrow = (int64_t*)malloc(sizeof(int64_t) * (n_group > 0 ? n_group : 1));
+        for (int j = 0; j < n_group; j++) {
+            int32_t page = jb->table[(size_t)b * jb->max_pages + j / jb->page_size];
+            int64_t r = (int64_t)page * jb->page_size + j % jb->page_size;
+            keyrow[j] = (page >= 0 && r < jb->num_rows) ? r : -1;
+        }
+    } else {
+        n_group = clampi(jb->valid[(size_t)b * jb->Q + i], 0, jb->K);
+        n_visible = n_group;
+        keyrow = (int64_t*)malloc(sizeof(int64_t) * (n_group > 0 ? n_group : 1));
+        for (int j = 0; j < n_group; j++) {
+            int32_t r = jb->rows[((size_t)b * jb->Q + i) * jb->K + j];
+            keyrow[j] = (r >= 0 && r < jb->num_rows) ? r : -1;
+        }
+    }
+    row_eval(q, jb->kv, keyrow, n_group, n_visible, jb->scale, jb->k_scale, &jb->plan,
+             jb->o + (size_t)item * MO_LATENT, jb->lse + item);
+    free(keyrow);
+}
+
+static void* worker(void* arg)
+{
+    const mo_job* jb = (const mo_job*)arg;
+    for (int64_t it = jb->tid; it < jb->n_items; it += jb->nthreads)
+        eval_item(jb, it);
+    return NULL;
+}
+
+static int run_job(mo_job* base)
+{
+    int nt = base->nthreads < 1 ? 1 : base->nthreads;
+    if (base->plan.mode != MO_EXACT && (base->plan.splits < 1 || base->plan.chunk < 1))
+        return -1;
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nt);
+    mo_job* jobs = (mo_job*)malloc(sizeof(mo_job) * nt);
+    for (int t = 0; t < nt; t++) {
+        jobs[t] = *base;
+        jobs[t].nthreads = nt;
+        jobs[t].tid = t;
+        pthread_create(&th[t], NULL, worker, &jobs[t]);
+    }
+    for (int t = 0; t < nt; t++)
+        pthread_join(th[t], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
+
+/*
+ * Dense paged decode. q [B,Q,H,576] bf16 bits; kv [num_rows,576] E4M3 bytes; table [B,max_pages];
+ * seq_lens [B]. sel: optional list of flat rows (b*Q+i)*H+h (n_sel of them); NULL means every row.
+ * o [items,512] and lse [items] in FP64.
+ */
+int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t num_rows,
+             int page_size, float k_scale, const int32_t* table, int max_pages,
+             const int32_t* seq_lens, float scale, int mode, int splits, int chunk,
+             const int64_t* sel, int64_t n_sel, int threads, double* o, double* lse)
+{
+    if (page_size < 1)
+        return -1;
+    mo_job jb = {0};
+    jb.dense = 1;
+    jb.q = q;
+    jb.B = B;
+    jb.Q = Q;
+    jb.H = H;
+    jb.kv = kv;
+    jb.num_rows = num_rows;
+    jb.page_size = page_size;
+    jb.table = table;
+    jb.max_pages = max_pages;
+    jb.seq_lens = seq_lens;
+    jb.scale = scale;
+    jb.k_scale = k_scale;
+    jb.plan.mode = mode;
+    jb.plan.splits = splits;
+    jb.plan.chunk = chunk;
+    jb.sel = sel;
+    jb.n_items = sel ? n_sel : (int64_t)B * Q * H;
+    jb.o = o;
+    jb.lse = lse;
+    jb.nthreads = threads;
+    return run_job(&jb);
+}
+
+/*
+ * Sparse (top-k list) decode. rows [B,Q,K] flat cache rows, valid [B,Q] counts (clamped to [0,K]).
+ */
+int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t num_rows,
+              float k_scale, const int32_t* rows, int K, const int32_t* valid, float scale,
+              int mode, int splits, int chunk, const int64_t* sel, int64_t n_sel, int threads,
+              double* o, double* lse)
+{
+    mo_job jb = {0};
+    jb.dense = 0;
+    jb.q = q;
+    jb.B = B;
+    jb.Q = Q;
+    jb.H = H;
+    jb.kv = kv;
+    jb.num_rows = num_rows;
+    jb.rows = rows;
+    jb.K = K;
+    jb.valid = valid;
+    jb.scale = scale;
+    jb.k_scale = k_scale;
+    jb.plan.mode = mode;
+    jb.plan.splits = splits;
+    jb.plan.chunk = chunk;
+    jb.sel = sel;
+    jb.n_items = sel ? n_sel : (int64_t)B * Q * H;
+    jb.o = o;
+    jb.lse = lse;
+    jb.nthreads = threads;
+    return run_job(&jb);
+}
