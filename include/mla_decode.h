@@ -1,0 +1,125 @@
+/*
+ * mla_decode.h -- C ABI of an MI355X (gfx950) MLA decode attention library over an FP8 E4M3 latent
+ * KV cache.
+ *
+ * The operation (vLLM API pages, cited by title and section):
+ *   - vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.attn_sparse, module docstring: every
+ *     query head attends a list of 576-byte E4M3 cache rows (bytes [0,512) are the latent, which is
+ *     V and the first 512 columns of K; bytes [512,576) are the rope part of K), with one per-tensor
+ *     k_scale; a row's keys are split into partials, each an online softmax in base 2 with P taken
+ *     at 448 of the running maximum and rounded to E4M3, the partials merged in FP32 into a BF16
+ *     latent output and a natural-log LSE; rows with no key give o = 0 and LSE = -inf.
+ *   - the same page, SparseDcpDecode.kernel / run_sparse: the top-k form reads keys through a list
+ *     of flat cache row ids and a per-row count clamped to [0, K].
+ *   - vllm.models.kimi_k3.amd.specialized_decode.mono.attention.mla_attn, module docstring: the dense
+ *     form reads a request's paged KV; position i of the request's Q query rows sees keys
+ *     0 .. seq_len - Q + i.
+ *
+ * All pointers named "device" are HIP device pointers; the caller owns every buffer (inputs,
+ * outputs, workspace). The library allocates nothing on the decode path and keeps no per-call
+ * state. Calls are asynchronous on the given HIP stream (a hipStream_t passed as void*, NULL is the
+ * default stream) and never synchronize. Errors found on the host return a status and launch
+ * nothing; no exception crosses the ABI.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+    MLA_ERR_SHAPE = 2,       /* B, Q, H, K, max_pages or page_size out of range (H % 16 != 0 ...) */
+    MLA_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+    MLA_ERR_WORKSPACE = 4,   /* the workspace is missing or smaller than mla_workspace_bytes() */
+    MLA_ERR_UNSUPPORTED = 5, /* a plan the kernels do not implement (tiles not 1/2/4 or not
+                                dividing the row tiles, splits < 1) */
+    MLA_ERR_LAUNCH = 6       /* the kernel launch failed (HIP error) */
+} mla_status_t;
+
+/* The E4M3 cache. data: device, num_rows rows of 576 bytes each (OCP E4M3FN codes), 16-byte
+ * aligned. Dense: row r = page * page_size + slot. Sparse: page_size is ignored. k_scale: the
+ * per-tensor dequantization scale of K and V (value = k_scale * E4M3 value). */
+typedef struct {
+    const void* data;
+    int64_t num_rows;
+    int32_t page_size;
+    float k_scale;
+} mla_kv_t;
+
+/* A launch plan. splits: S >= 1, the number of contiguous parts each key group's keys are divided
+ * into (part s holds keys [s*per, min(n, (s+1)*per)), per = ceil(n / S)); tiles: 16-row query tiles
+ * per workgroup (1, 2 or 4), which must divide the row tiles of a key group (dense: Q*H/16,
+ * sparse: H/16). The result depends on splits (where P is anchored and rounded) but is bit-identical
+ * for any tiles. */
+typedef struct {
+    int32_t splits;
+    int32_t tiles;
+} mla_plan_t;
+
+/* A plan chosen from shapes only (never from device data): fills *plan. Returns MLA_ERR_NULL or
+ * MLA_ERR_SHAPE for bad arguments. Dense: max_keys = max_pages * page_size; sparse: max_keys = K. */
+mla_status_t mla_plan_dense(int B, int Q, int H, int max_pages, int page_size, mla_plan_t* plan);
+mla_status_t mla_plan_sparse(int B, int Q, int H, int K, mla_plan_t* plan);
+
+/* Workspace bytes a call with these shapes and this many splits needs: 0 for splits == 1, else one
+ * arrival counter per 16-row tile (first), then the FP32 split partials (B*Q*H*splits rows of
+ * 514 floats). */
+size_t mla_workspace_bytes(int B, int Q, int H, int splits);
+
+/* The leading bytes of the workspace that must be zero when a call starts (its arrival counters);
+ * the call leaves them zero again (the last arriving workgroup of each tile resets its counter) and
+ * leaves the rest of the workspace undefined. A workspace that served a call whose zero prefix was
+ * at least as long can serve the next call as is; otherwise zero the longer prefix first. Calls that
+ * share a workspace must be ordered on one stream. */
+size_t mla_workspace_zero_bytes(int B, int Q, int H, int splits);
+
+/*
+ * Dense paged decode.
+ *   q            device bf16 [B, Q, H, 576], row-major, 16-byte aligned: query rows of position i of
+ *                request b, head h.
+ *   kv           the cache (see mla_kv_t); page_size >= 1.
+ *   block_table  device int32 [B, max_pages]: page ids of request b's keys; key j is cache row
+ *                block_table[b, j / page_size] * page_size + j % page_size. Only entries covering
+ *                keys < seq_len are read. A page id whose row falls outside [0, num_rows) makes its
+ *                keys absent (they contribute nothing and are not read).
+ *   seq_lens     device int32 [B]: keys of request b, clamped to [0, max_pages * page_size].
+ *   scale        softmax scale multiplying q . K (k_scale is applied on top).
+ *   plan         NULL for mla_plan_dense()'s choice.
+ *   o            device bf16 [B, Q, H, 512] (8-byte aligned): softmax-weighted latent, RNE.
+ *   lse          device float [B, Q, H]: natural-log sum of exp(scale * q . K) over the row's keys.
+ *   Position i sees keys j < seq_len - Q + i + 1; a row with none gets o = +0 and lse = -inf.
+ *   workspace    device, >= mla_workspace_bytes(B, Q, H, splits) bytes, 256-byte aligned (may be
+ *                NULL when splits == 1).
+ */
+mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* block_table,
+                              int max_pages, const int32_t* seq_lens, float scale, int B, int Q,
+                              int H, const mla_plan_t* plan, void* o, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Top-k sparse decode.
+ *   rows   device int32 [B, Q, K]: flat cache rows of the keys of position i of request b; the
+ *          first valid[b, i] entries are used (in order); an entry outside [0, num_rows) is an
+ *          absent key (contributes nothing, is not read). Duplicate entries count once each.
+ *   valid  device int32 [B, Q]: the count of each list, clamped to [0, K].
+ *   Other arguments as for mla_decode_dense; all H heads of (b, i) share the list.
+ */
+mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t* rows, int K,
+                               const int32_t* valid, float scale, int B, int Q, int H,
+                               const mla_plan_t* plan, void* o, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* A static, human-readable name of a status. */
+const char* mla_status_string(mla_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

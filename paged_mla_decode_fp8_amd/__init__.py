@@ -1,0 +1,198 @@
+"""Python binding of libmla_decode.so: MLA decode attention over an FP8 E4M3 latent cache on
+MI355X (gfx950).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels behind the C ABI
+declared in include/mla_decode.h. PyTorch provides device memory and the current stream. There is
+no fallback: without the built library (``python -m paged_mla_decode_fp8_amd._build``) every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple
+
+import torch
+
+from ._build import LIB
+
+__all__ = ["MlaError", "Plan", "dense", "sparse", "plan_dense", "plan_sparse", "workspace_bytes",
+           "workspace_zero_bytes", "library_path"]
+
+MLA_OK = 0
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"mla_decode status {status}: {msg}")
+        self.status = status
+
+
+class Plan(NamedTuple):
+    splits: int
+    tiles: int
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("num_rows", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("k_scale", ctypes.c_float)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("splits", ctypes.c_int32), ("tiles", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built; run python -m paged_mla_decode_fp8_amd._build")
+        lib = ctypes.CDLL(LIB)
+        P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.mla_status_string.argtypes = [i32]
+        lib.mla_status_string.restype = ctypes.c_char_p
+        lib.mla_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.mla_workspace_bytes.restype = sz
+        lib.mla_workspace_zero_bytes.argtypes = [i32, i32, i32, i32]
+        lib.mla_workspace_zero_bytes.restype = sz
+        lib.mla_plan_dense.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Plan)]
+        lib.mla_plan_dense.restype = i32
+        lib.mla_plan_sparse.argtypes = [i32, i32, i32, i32, ctypes.POINTER(_Plan)]
+        lib.mla_plan_sparse.restype = i32
+        lib.mla_decode_dense.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32, i32,
+                                         ctypes.POINTER(_Plan), P, P, P, sz, P]
+        lib.mla_decode_dense.restype = i32
+        lib.mla_decode_sparse.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32, i32,
+                                          ctypes.POINTER(_Plan), P, P, P, sz, P]
+        lib.mla_decode_sparse.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MlaError(status, _load().mla_status_string(status).decode())
+
+
+def plan_dense(B: int, Q: int, H: int, max_pages: int, page_size: int) -> Plan:
+    p = _Plan()
+    _check(_load().mla_plan_dense(B, Q, H, max_pages, page_size, ctypes.byref(p)))
+    return Plan(p.splits, p.tiles)
+
+
+def plan_sparse(B: int, Q: int, H: int, K: int) -> Plan:
+    p = _Plan()
+    _check(_load().mla_plan_sparse(B, Q, H, K, ctypes.byref(p)))
+    return Plan(p.splits, p.tiles)
+
+
+def workspace_bytes(B: int, Q: int, H: int, splits: int) -> int:
+    return int(_load().mla_workspace_bytes(B, Q, H, splits))
+
+
+def workspace_zero_bytes(B: int, Q: int, H: int, splits: int) -> int:
+    return int(_load().mla_workspace_zero_bytes(B, Q, H, splits))
+
+
+# One workspace per (device, stream) and the length of its prefix known to be zero: a call needs
+# its counter prefix zero and leaves exactly that prefix zero (the rest holds partials).
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, stream: int, B, Q, H, splits) -> torch.Tensor | None:
+    nbytes = workspace_bytes(B, Q, H, splits)
+    if nbytes == 0:
+        return None
+    need_zero = workspace_zero_bytes(B, Q, H, splits)
+    key = (device.index, stream)
+    ws, zero = _workspaces.get(key, (None, 0))
+    if ws is None or ws.numel() < nbytes:
+        ws, zero = torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
+    elif zero < need_zero:
+        ws[:need_zero].zero_()   # a fill kernel on the current stream
+    _workspaces[key] = (ws, need_zero)
+    return ws
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _outputs(q, o, lse):
+    B, Q, H, _ = q.shape
+    if o is None:
+        o = torch.empty((B, Q, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
+    return o, lse
+
+
+def _check_tensor(name, t, dtype, device):
+    if t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor on {device}")
+
+
+def _plan_arg(plan):
+    if plan is None:
+        return None
+    splits, tiles = plan
+    return ctypes.byref(_Plan(int(splits), int(tiles)))
+
+
+def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+          scale: float, k_scale: float, page_size: int, *, plan=None, o=None, lse=None,
+          workspace: torch.Tensor | None = None):
+    """Paged dense decode (C ABI mla_decode_dense). q bf16 [B,Q,H,576]; kv uint8 [rows,576] (or
+    [pages,page_size,576]); block_table int32 [B,max_pages]; seq_lens int32 [B]. Returns
+    (o bf16 [B,Q,H,512], lse f32 [B,Q,H]) on the current stream."""
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, dev)
+    _check_tensor("kv", kv, torch.uint8, dev)
+    _check_tensor("block_table", block_table, torch.int32, dev)
+    _check_tensor("seq_lens", seq_lens, torch.int32, dev)
+    B, Q, H, D = q.shape
+    assert D == 576
+    o, lse = _outputs(q, o, lse)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pl = plan if plan is not None else plan_dense(B, Q, H, block_table.shape[1], page_size)
+    if workspace is None:
+        workspace = _workspace(dev, stream, B, Q, H, pl[0])
+    kvs = _KV(kv.data_ptr(), kv.numel() // 576, int(page_size), float(k_scale))
+    _check(_load().mla_decode_dense(
+        _ptr(q), ctypes.byref(kvs), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        float(scale), B, Q, H, _plan_arg(pl), _ptr(o), _ptr(lse), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream)))
+    return o, lse
+
+
+def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.Tensor,
+           scale: float, k_scale: float, *, plan=None, o=None, lse=None,
+           workspace: torch.Tensor | None = None):
+    """Top-k sparse decode (C ABI mla_decode_sparse). rows int32 [B,Q,K] flat cache rows; valid
+    int32 [B,Q]."""
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, dev)
+    _check_tensor("kv", kv, torch.uint8, dev)
+    _check_tensor("rows", rows, torch.int32, dev)
+    _check_tensor("valid", valid, torch.int32, dev)
+    B, Q, H, D = q.shape
+    assert D == 576
+    K = rows.shape[2]
+    o, lse = _outputs(q, o, lse)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pl = plan if plan is not None else plan_sparse(B, Q, H, K)
+    if workspace is None:
+        workspace = _workspace(dev, stream, B, Q, H, pl[0])
+    kvs = _KV(kv.data_ptr(), kv.numel() // 576, 1, float(k_scale))
+    _check(_load().mla_decode_sparse(
+        _ptr(q), ctypes.byref(kvs), _ptr(rows), K, _ptr(valid), float(scale), B, Q, H,
+        _plan_arg(pl), _ptr(o), _ptr(lse), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream)))
+    return o, lse

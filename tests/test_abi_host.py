@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/mla_decode.h declares, and rejects bad arguments with the documented status before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_mla_decode_fp8_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = mla._load()
+    names = declared_functions()
+    assert {"mla_decode_dense", "mla_decode_sparse", "mla_plan_dense", "mla_plan_sparse",
+            "mla_workspace_bytes", "mla_workspace_zero_bytes", "mla_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = mla._load()
+    for s in range(7):
+        assert lib.mla_status_string(s)
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def _kv(ptr=0x1000, rows=100, page=64):
+    return mla._KV(ptr, rows, page, 0.05)
+
+
+def _dense(q=0x1000, kv=None, table=0x2000, max_pages=4, seq=0x3000, B=2, Q=1, H=16, plan=None,
+           o=0x4000, lse=0x5000, ws=None, ws_bytes=0):
+    lib = mla._load()
+    kvs = kv if kv is not None else _kv()
+    return lib.mla_decode_dense(q, ctypes.byref(kvs), table, max_pages, seq, 0.07, B, Q, H, plan,
+                                o, lse, ws, ws_bytes, None)
+
+
+def _sparse(q=0x1000, kv=None, rows=0x2000, K=8, valid=0x3000, B=2, Q=1, H=16, plan=None,
+            o=0x4000, lse=0x5000, ws=None, ws_bytes=0):
+    lib = mla._load()
+    kvs = kv if kv is not None else _kv()
+    return lib.mla_decode_sparse(q, ctypes.byref(kvs), rows, K, valid, 0.07, B, Q, H, plan,
+                                 o, lse, ws, ws_bytes, None)
+
+
+def test_bad_arguments_return_status_without_launching():
+    P = lambda s, t: ctypes.byref(mla._Plan(s, t))  # noqa: E731
+    assert _dense(q=None) == NULL
+    assert _dense(table=None) == NULL
+    assert _dense(kv=_kv(ptr=0)) == NULL
+    assert _dense(H=24) == SHAPE
+    assert _dense(H=8) == SHAPE
+    assert _dense(Q=0) == SHAPE
+    assert _dense(max_pages=0) == SHAPE
+    assert _dense(kv=_kv(page=0)) == SHAPE
+    assert _dense(q=0x1008) == ALIGN
+    assert _dense(kv=_kv(ptr=0x1004)) == ALIGN
+    assert _dense(o=0x4002) == ALIGN
+    assert _dense(plan=P(0, 1)) == UNSUPPORTED
+    assert _dense(plan=P(1, 3)) == UNSUPPORTED
+    assert _dense(plan=P(1, 2)) == UNSUPPORTED       # 1 row tile per group: tiles must divide it
+    assert _dense(plan=P(2, 1)) == WORKSPACE         # splits > 1 need a workspace
+    need = mla.workspace_bytes(2, 1, 16, 2)
+    assert _dense(plan=P(2, 1), ws=0x10000, ws_bytes=need - 1) == WORKSPACE
+    assert _dense(plan=P(2, 1), ws=0x10010, ws_bytes=need) == ALIGN
+    assert _sparse(K=0) == SHAPE
+    assert _sparse(valid=None) == NULL
+    assert _sparse(rows=0x2002) == ALIGN
+    assert _sparse(B=0) == OK                        # nothing to do, nothing launched
+
+
+def test_workspace_sizes_and_plans():
+    assert mla.workspace_bytes(4, 5, 16, 1) == 0
+    assert mla.workspace_zero_bytes(4, 5, 16, 1) == 0
+    n = mla.workspace_bytes(4, 5, 16, 3)
+    z = mla.workspace_zero_bytes(4, 5, 16, 3)
+    rows = 4 * 5 * 16
+    assert 0 < z < n and z % 256 == 0 and n % 256 == 0
+    assert n >= rows * 3 * (512 + 2) * 4 + rows // 16 * 4
+    for B, Q, H, K in ((2, 1, 16, 64), (4, 5, 16, 256), (32, 5, 64, 2048)):
+        p = mla.plan_sparse(B, Q, H, K)
+        assert p.splits >= 1 and p.tiles in (1, 2, 4) and (H // 16) % p.tiles == 0
+    for B, Q, H, mp in ((64, 1, 128, 128), (8, 4, 128, 2048)):
+        p = mla.plan_dense(B, Q, H, mp, 64)
+        assert p.splits >= 1 and (Q * H // 16) % p.tiles == 0
+    with pytest.raises(mla.MlaError):
+        mla.plan_dense(1, 1, 20, 4, 64)

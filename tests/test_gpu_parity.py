@@ -1,0 +1,223 @@
+"""GPU parity of the HIP library (called through its C ABI) against the FP64 oracle in METHOD
+mode with the same split plan, plus the bit-level properties of the kernels (determinism, tiles
+invariance, sparse == dense, page permutation, poisoning, empty rows, single key)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import (assert_parity, bits, run_gpu, run_oracle, say, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(x, splits, tiles, what, sel=None):
+    say(what, x.kind, "B,Q,H =", x.B, x.Q, x.H, "plan", (splits, tiles))
+    dev = upload(x)
+    o, lse = run_gpu(x, dev, (splits, tiles))
+    o_ref, lse_ref = run_oracle(x, splits, sel=sel)
+    return assert_parity(o, lse, o_ref, lse_ref, sel=sel, what=what), o, lse
+
+
+# ---- the small named workloads, whole ----------------------------------------------------------
+
+@pytest.mark.parametrize("splits", [1, 2, 3])
+def test_tiny_sparse(splits):
+    _parity(wl.tiny_sparse(), splits, 1, f"tiny_sparse S={splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4])
+def test_latency_sparse(splits):
+    _parity(wl.latency_sparse(), splits, 1, f"latency_sparse S={splits}")
+
+
+# ---- shape fuzz: ragged counts around the 16-key subtile and 128-key block ---------------------
+
+SPARSE_CASES = [
+    # B, Q, H, K, valid pattern, cache rows, plan
+    (1, 1, 16, 1, [[1]], 64, (1, 1)),
+    (2, 3, 16, 33, [[0, 1, 15], [16, 17, 33]], 200, (1, 1)),
+    (2, 2, 32, 129, [[127, 128], [129, 31]], 500, (2, 2)),
+    (3, 2, 64, 300, [[300, 257, 0], [1, 2, 255]], 4096, (3, 4)),
+    (1, 5, 16, 256, [[200, 256, 231, 255, 129]], 65536, (5, 1)),
+    (2, 1, 128, 1000, [[1000], [999]], 8000, (4, 4)),
+    (1, 1, 48, 77, [[77]], 100, (2, 1)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPARSE_CASES)))
+def test_sparse_fuzz(case):
+    B, Q, H, K, valid, N, plan = SPARSE_CASES[case]
+    valid = np.array(valid, np.int32).reshape(-1)[: B * Q].reshape(B, Q)
+    x = wl.sparse_case(B, Q, H, K, valid, N, seed=500 + case)
+    _parity(x, plan[0], plan[1], f"sparse fuzz {case}")
+
+
+DENSE_CASES = [
+    # B, Q, H, seq_lens, page_size, plan
+    (1, 1, 16, [1], 64, (1, 1)),
+    (2, 1, 16, [127, 129], 64, (1, 1)),
+    (2, 4, 16, [130, 3], 16, (2, 2)),
+    (3, 2, 32, [500, 64, 1], 64, (3, 4)),
+    (1, 5, 16, [1031], 1, (4, 1)),
+    (2, 3, 64, [0, 700], 32, (2, 4)),
+    (1, 2, 128, [2100], 64, (5, 4)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DENSE_CASES)))
+def test_dense_fuzz(case):
+    B, Q, H, seq, ps, plan = DENSE_CASES[case]
+    x = wl.dense_case(B, Q, H, seq, page_size=ps, seed=600 + case, extra_pages=3)
+    _parity(x, plan[0], plan[1], f"dense fuzz {case}")
+
+
+# ---- exact properties ----------------------------------------------------------------------
+
+def test_single_key_gives_v_row_bits_exactly():
+    """n = 1: P = 448 exactly, O / l = v exactly, so o = BF16_RNE(fp32(k_scale * v))."""
+    x = wl.sparse_case(3, 2, 32, 4, [[1, 1], [1, 1], [1, 1]], 300, seed=700)
+    dev = upload(x)
+    o, lse = run_gpu(x, dev, (1, 2))
+    v = torch.from_numpy(x.kv[x.rows[:, :, 0]][..., :512]).view(torch.float8_e4m3fn).float()
+    ref = (v * torch.tensor(x.k_scale, dtype=torch.float32)).to(torch.bfloat16)
+    ref = ref[:, :, None, :].expand(3, 2, 32, 512).contiguous()
+    assert np.array_equal(bits(o), ref.view(torch.int16).numpy().view(np.uint16))
+
+
+def _case_for_bits():
+    return wl.sparse_case(2, 2, 64, 700, [[700, 513], [0, 257]], 3000, seed=800)
+
+
+def test_determinism_three_runs_bit_equal():
+    x = _case_for_bits()
+    dev = upload(x)
+    runs = [run_gpu(x, dev, (5, 2)) for _ in range(3)]
+    for o, lse in runs[1:]:
+        assert np.array_equal(bits(o), bits(runs[0][0]))
+        assert np.array_equal(lse.cpu().numpy().view(np.uint32), runs[0][1].cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_tiles_per_workgroup_do_not_change_bits(splits):
+    x = _case_for_bits()
+    dev = upload(x)
+    ref = run_gpu(x, dev, (splits, 1))
+    for tiles in (2, 4):
+        o, lse = run_gpu(x, dev, (splits, tiles))
+        assert np.array_equal(bits(o), bits(ref[0])), tiles
+        assert np.array_equal(lse.cpu().numpy(), ref[1].cpu().numpy()), tiles
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_sparse_over_all_keys_bit_equals_dense(splits):
+    d = wl.dense_case(3, 1, 32, [700, 129, 1], page_size=64, seed=900, extra_pages=2)
+    K = 700
+    rows = np.zeros((3, 1, K), np.int32)
+    for b in range(3):
+        for j in range(d.seq_lens[b]):
+            rows[b, 0, j] = d.block_table[b, j // 64] * 64 + j % 64
+    s = wl.Inputs("sparse", d.q_bits, d.kv, d.k_scale, d.scale, rows=rows,
+                  valid=d.seq_lens.reshape(3, 1).copy())
+    od, ld = run_gpu(d, upload(d), (splits, 2))
+    os_, ls = run_gpu(s, upload(s), (splits, 2))
+    assert np.array_equal(bits(od), bits(os_))
+    assert np.array_equal(ld.cpu().numpy(), ls.cpu().numpy())
+
+
+def test_page_permutation_bit_invariance():
+    d = wl.dense_case(2, 3, 16, [900, 333], page_size=16, seed=1000, extra_pages=7)
+    ref = run_gpu(d, upload(d), (3, 1))
+    pool = d.kv.shape[0] // 16
+    perm = np.random.default_rng(1).permutation(pool)
+    kv2 = np.empty_like(d.kv).reshape(pool, 16, 576)
+    kv2[perm] = d.kv.reshape(pool, 16, 576)
+    t2 = d.block_table.copy()
+    used = t2 != wl.INT32_MAX
+    t2[used] = perm[t2[used]]
+    d2 = wl.Inputs("dense", d.q_bits, kv2.reshape(-1, 576), d.k_scale, d.scale, page_size=16,
+                   block_table=t2, seq_lens=d.seq_lens)
+    got = run_gpu(d2, upload(d2), (3, 1))
+    assert np.array_equal(bits(got[0]), bits(ref[0]))
+    assert np.array_equal(got[1].cpu().numpy(), ref[1].cpu().numpy())
+
+
+def test_poisoned_unread_memory_leaves_bits_unchanged():
+    """NaN (0x7F) in every cache row no key reads, INT32_MAX table entries past seq_len, and
+    index entries past valid pointing outside the cache: outputs stay bit-equal."""
+    # sparse
+    x = wl.sparse_case(2, 2, 32, 300, [[300, 17], [0, 129]], 4000, seed=1100)
+    ref = run_gpu(x, upload(x), (2, 2))
+    read = set()
+    for b in range(2):
+        for i in range(2):
+            read.update(x.rows[b, i, : x.valid[b, i]].tolist())
+    kv = x.kv.copy()
+    unread = np.setdiff1d(np.arange(kv.shape[0]), np.array(sorted(read)))
+    kv[unread] = 0x7F
+    rows = x.rows.copy()
+    for b in range(2):
+        for i in range(2):
+            rows[b, i, x.valid[b, i]:] = 2**31 - 1
+    xp = wl.Inputs("sparse", x.q_bits, kv, x.k_scale, x.scale, rows=rows, valid=x.valid)
+    got = run_gpu(xp, upload(xp), (2, 2))
+    assert np.array_equal(bits(got[0]), bits(ref[0]))
+    assert np.array_equal(got[1].cpu().numpy(), ref[1].cpu().numpy())
+    # dense
+    d = wl.dense_case(2, 2, 16, [300, 70], page_size=32, seed=1101, extra_pages=6)
+    ref = run_gpu(d, upload(d), (3, 1))
+    kv = d.kv.copy().reshape(-1, 32, 576)
+    used_rows = np.zeros(kv.shape[0] * 32, bool)
+    for b in range(2):
+        for j in range(d.seq_lens[b]):
+            used_rows[d.block_table[b, j // 32] * 32 + j % 32] = True
+    kv = kv.reshape(-1, 576)
+    kv[~used_rows] = 0x7F
+    dp = wl.Inputs("dense", d.q_bits, kv, d.k_scale, d.scale, page_size=32,
+                   block_table=d.block_table, seq_lens=d.seq_lens)
+    got = run_gpu(dp, upload(dp), (3, 1))
+    assert np.array_equal(bits(got[0]), bits(ref[0]))
+    assert np.array_equal(got[1].cpu().numpy(), ref[1].cpu().numpy())
+
+
+def test_absent_keys_and_clamped_counts_match_oracle():
+    x = wl.sparse_case(2, 2, 16, 200, [[10**6, -3], [150, 200]], 1000, seed=1200)
+    x.rows[1, 0, [0, 5, 149]] = [-1, 1000, 2**31 - 1]
+    x.rows[1, 1, 100:120] = -7
+    _parity(x, 2, 1, "absent keys")
+
+
+# ---- full-size named workloads, sampled rows ---------------------------------------------------
+
+@pytest.mark.parametrize("name", ["dense_paged", "topk_sparse", "long_dense"])
+def test_full_size_workloads_sampled(name):
+    w = wl.WORKLOADS[name]
+    x = w.make()
+    rng = np.random.default_rng(3)
+    n_rows = x.B * x.Q * x.H
+    sel = np.unique(np.concatenate([rng.choice(n_rows, 24, replace=False), [0, n_rows - 1]]))
+    if name == "topk_sparse":
+        empty = np.flatnonzero(x.valid.reshape(-1) == 0)[:2]
+        sel = np.unique(np.concatenate([sel, empty * x.H, empty * x.H + x.H - 1]))
+    _parity(x, w.splits, w.tiles, f"{name} sampled", sel=sel)
+
+
+def test_workspace_reused_across_shapes_with_zero_prefix_contract():
+    """One caller-owned workspace serves a large split call and then a call of another shape whose
+    counters overlap the first call's partials, once its counter prefix is zeroed."""
+    import paged_mla_decode_fp8_amd as mla
+    a = wl.latency_sparse()
+    b = wl.sparse_case(2, 2, 32, 129, [[127, 128], [129, 31]], 500, seed=502)
+    need = max(mla.workspace_bytes(4, 5, 16, 4), mla.workspace_bytes(2, 2, 32, 3))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    for x, plan in ((a, (4, 1)), (b, (3, 2)), (a, (4, 1))):
+        say("workspace reuse", x.B, x.Q, x.H, plan)
+        ws[: mla.workspace_zero_bytes(x.B, x.Q, x.H, plan[0])].zero_()
+        dev = upload(x)
+        o, lse = mla.sparse(dev["q"], dev["kv"], dev["rows"], dev["valid"], x.scale, x.k_scale,
+                            plan=plan, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = run_oracle(x, plan[0])
+        assert_parity(o, lse, o_ref, lse_ref, what="workspace reuse")
+        # the call left its counter prefix zero
+        assert int(ws[: mla.workspace_zero_bytes(x.B, x.Q, x.H, plan[0])].count_nonzero()) == 0
