@@ -1,0 +1,288 @@
+"""Benchmark of MLA decode over an FP8 E4M3 latent cache on one MI355X.
+
+One step = one decode call (mla_decode_dense / mla_decode_sparse through the C ABI) over one batch
+of the workload: Q-stage, KV gather, QK, softmax, PV, split emit and FP32 merge all run inside it.
+The headline line is the dense paged workload (B=64, Q=1, H=128, page 64, seq_len U[1024, 8192]);
+the other four workloads are timed the same way and reported under "workloads".
+
+Timing is cold with respect to the 256 MB Infinity Cache: the timed calls rotate over several
+copies of the KV cache (together well above 256 MB), all resident in HBM before timing starts.
+HIP events on the stream the kernel runs on bracket the K timed calls.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12        # B/s, MI355X
+FP8_PEAK = 5.0e15        # dense FP8 MFMA flop/s, MI355X
+FLOP_PER_HEAD_KEY = 2 * 2 * 576 + 2 * 512   # QK with the hi + lo query (two E4M3 passes) + PV
+HEADLINE = "dense_paged"
+METRIC = ("µs/call and KV HBM GB/s (fraction of 8 TB/s peak), dense + top-k sparse MLA "
+          "decode")
+KERNEL_SRC = os.path.join(ROOT, "paged_mla_decode_fp8_amd", "csrc", "mla_decode.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(x):
+    """Algorithmic HBM bytes and MFMA flops of one call: every gathered KV row once per key group,
+    Q read once, o and lse written once, indices / block-table entries read once."""
+    rows = x.B * x.Q * x.H
+    q_bytes = rows * 576 * 2
+    o_bytes = rows * 512 * 2 + rows * 4
+    if x.kind == "dense":
+        cap = x.block_table.shape[1] * x.page_size
+        seq = np.clip(x.seq_lens.astype(np.int64), 0, cap)
+        kv_rows = int(seq.sum())
+        idx_bytes = int(np.ceil(seq / x.page_size).sum()) * 4 + x.B * 4
+        head_keys = 0
+        for i in range(x.Q):
+            head_keys += int(np.clip(seq - x.Q + i + 1, 0, seq).sum()) * x.H
+    else:
+        cnt = np.clip(x.valid.astype(np.int64), 0, x.rows.shape[2])
+        kv_rows = int(cnt.sum())
+        idx_bytes = kv_rows * 4 + x.B * x.Q * 4
+        head_keys = kv_rows * x.H
+    kv_bytes = kv_rows * 576
+    return {
+        "kv_bytes": kv_bytes,
+        "bytes": kv_bytes + q_bytes + o_bytes + idx_bytes,
+        "flops": head_keys * FLOP_PER_HEAD_KEY,
+        "head_keys": head_keys,
+    }
+
+
+def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20):
+    import torch
+
+    import paged_mla_decode_fp8_amd as mla
+    import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    x = w.make()
+    alg = algorithmic(x)
+    dev = torch.device("cuda:0")
+    plan = (w.splits, w.tiles)
+    kv_host = torch.from_numpy(x.kv)
+    copies = max(1, min(8, math.ceil(min_rotation_bytes / max(1, x.kv.nbytes))))
+    kvs = [kv_host.to(dev) for _ in range(copies)]
+    q = torch.from_numpy(x.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    o = torch.empty((x.B, x.Q, x.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((x.B, x.Q, x.H), dtype=torch.float32, device=dev)
+    nbytes = mla.workspace_bytes(x.B, x.Q, x.H, plan[0])
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+    if x.kind == "dense":
+        table = torch.from_numpy(x.block_table).to(dev)
+        seq = torch.from_numpy(x.seq_lens).to(dev)
+
+        def call(k):
+            mla.dense(q, kvs[k % copies], table, seq, x.scale, x.k_scale, x.page_size, plan=plan,
+                      o=o, lse=lse, workspace=ws)
+    else:
+        rows = torch.from_numpy(x.rows).to(dev)
+        valid = torch.from_numpy(x.valid).to(dev)
+
+        def call(k):
+            mla.sparse(q, kvs[k % copies], rows, valid, x.scale, x.k_scale, plan=plan, o=o,
+                       lse=lse, workspace=ws)
+
+    for k in range(warmup):
+        call(k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        call(warmup + k)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    sec = ms * 1e-3
+    res = {
+        "workload": name,
+        "description": w.description,
+        "plan": {"splits": plan[0], "tiles": plan[1]},
+        "us_per_call": round(ms * 1e3, 3),
+        "kv_bytes": alg["kv_bytes"],
+        "alg_bytes": alg["bytes"],
+        "alg_flops": alg["flops"],
+        "kv_GBps": round(alg["kv_bytes"] / sec / 1e9, 2),
+        "hbm_frac": round(alg["bytes"] / sec / HBM_PEAK, 4),
+        "mfma_frac": round(alg["flops"] / sec / FP8_PEAK, 4),
+        "hbm_floor_us": round(alg["bytes"] / HBM_PEAK * 1e6, 3),
+        "mfma_floor_us": round(alg["flops"] / FP8_PEAK * 1e6, 3),
+        "kv_copies_rotated": copies,
+    }
+    res["bound"] = "hbm" if res["hbm_floor_us"] >= res["mfma_floor_us"] else "mfma"
+    del kvs
+    torch.cuda.empty_cache()
+    return res, x
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"mla_decode_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(x, splits, budget_rows=1024, seed=0):
+    """The FP64 oracle (as it stands, METHOD mode with the benchmark's split plan) on a random
+    sample of the workload's query rows, on every core of this process's affinity mask; the time
+    per full call is scaled from the sample by the rows' key counts."""
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    n_rows = x.B * x.Q * x.H
+    rng = np.random.default_rng(seed)
+    sel = np.sort(rng.choice(n_rows, min(budget_rows, n_rows), replace=False))
+    if x.kind == "dense":
+        seq = np.clip(x.seq_lens.astype(np.int64), 0, x.block_table.shape[1] * x.page_size)
+        keys_of = lambda r: seq[r // (x.Q * x.H)]  # noqa: E731
+    else:
+        cnt = np.clip(x.valid.astype(np.int64), 0, x.rows.shape[2]).reshape(-1)
+        keys_of = lambda r: cnt[r // x.H]  # noqa: E731
+    all_keys = sum(int(keys_of(r)) for r in range(n_rows))
+    sample_keys = sum(int(keys_of(r)) for r in sel)
+    t0 = time.perf_counter()
+    if x.kind == "dense":
+        oracle.dense(x.q_bits, x.kv, x.page_size, x.k_scale, x.block_table, x.seq_lens, x.scale,
+                     mode=oracle.METHOD, splits=splits, sel=sel, threads=threads)
+    else:
+        oracle.sparse(x.q_bits, x.kv, x.k_scale, x.rows, x.valid, x.scale, mode=oracle.METHOD,
+                      splits=splits, sel=sel, threads=threads)
+    dt = time.perf_counter() - t0
+    per_call = dt * all_keys / max(1, sample_keys)
+    kv_bytes = algorithmic(x)["kv_bytes"]
+    return {
+        "value": round(kv_bytes / per_call / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(sel)} of {n_rows} query rows (uniform random, seed {seed}); "
+                   f"{dt:.2f} s measured, scaled by key counts to {per_call:.2f} s per call"),
+        "us_per_call": round(per_call * 1e6, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="all",
+                    help="comma-separated workload names, or 'all' (headline first)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="query rows of the headline workload the CPU oracle is timed on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy (a known-size reference for "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU (the decode is measured on one GPU's "
+              "share; no multi-GPU path is built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as wl
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    names = list(wl.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
+    if HEADLINE in names:
+        names.remove(HEADLINE)
+    names = [HEADLINE] + names
+
+    results = {}
+    head_x = None
+    for name in names:
+        res, x = bench_workload(name, args.steps, args.warmup)
+        results[name] = res
+        print(f"[bench] {name}: {res['us_per_call']} us/call, {res['kv_GBps']} KV GB/s, "
+              f"hbm {res['hbm_frac']:.3f}, mfma {res['mfma_frac']:.3f}", file=sys.stderr,
+              flush=True)
+        if name == HEADLINE:
+            head_x = x
+        else:
+            del x
+
+    h = results[HEADLINE]
+    sec = h["us_per_call"] * 1e-6
+    if h["bound"] == "hbm":
+        achieved, peak, unit = h["alg_bytes"] / sec / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = h["alg_flops"] / sec / 1e12, FP8_PEAK / 1e12, "TFLOP/s"
+    roofline = {
+        "bound": h["bound"],
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": unit,
+        "frac": round(achieved / peak, 4),
+        "traffic": read_traffic(HEADLINE),
+        "kernel": "mla_decode_kernel<4, dense>",
+        "hbm_frac": h["hbm_frac"],
+        "mfma_frac": h["mfma_frac"],
+    }
+    cpu = None
+    if not args.no_cpu:
+        w = wl.WORKLOADS[HEADLINE]
+        cpu = cpu_baseline(head_x, w.splits, budget_rows=args.cpu_rows)
+    line = {
+        "metric": METRIC,
+        "value": h["kv_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["us_per_call"] / 1e3, 6),
+        "us_per_call": h["us_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded; E4M3 cache of N(0,1)/0.05, bf16 N(0,1) queries)",
+        "config": {"workload": HEADLINE, "B": 64, "Q": 1, "H": 128, "page_size": 64,
+                   "seq_len": "U[1024,8192]", "kv_bytes": h["kv_bytes"],
+                   "plan": h["plan"], "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": results,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -18,20 +18,24 @@
 //     cross-workgroup merge through a global workspace with a per-row arrival counter (the last
 //     arriver merges in a fixed order and resets the counter), so results do not depend on timing.
 //
-// Workgroup = (key group, split, set of T 16-row tiles), 512 threads = 8 waves. Per 128-key block:
-//   DMA    wave w gathers keys 16w..16w+15 of the next block into the other LDS slot (9 x 1 KB
+// Workgroup = (key group, split, set of T 16-row tiles), 256 threads = 4 waves, one wave per SIMD
+// (up to 512 registers per lane). Per 128-key block:
+//   DMA    wave w gathers keys 32w..32w+31 of the next block into the other LDS slot (18 x 1 KB
 //          global_load_lds_dwordx4); absent keys read a zero row.
-//   QK     wave w: tile w % T, key subtiles (w / T) * T .. + T - 1; 9 MFMAs per subtile (4 latent steps
-//          x {hi, lo} + 1 rope step packing rope hi | rope lo against rope | rope).
-//   softmax  row max over the 8 subtiles through LDS; P -> E4M3 into LDS; per-subtile row sums
-//          through LDS, added in subtile order 0..7 (so the result does not depend on T).
-//   PV     wave w: latent columns 64w..64w+63 of every tile; O^T += V^T P^T, 4 MFMAs per tile.
+//   QK     wave w < T owns tile w: S^T of all 128 keys x its 16 rows, 9 MFMAs per 16-key subtile
+//          (4 latent steps x {hi, lo} + 1 rope step packing rope hi | rope lo against rope | rope),
+//          K fragments streamed from LDS through a register ring a few fragments ahead.
+//   softmax  entirely inside the tile's wave: row max, running max, P = 448 exp2(x - max) -> E4M3,
+//          row sums of the unrounded P in a fixed order; P and the rescale factor go to LDS.
+//   PV     wave w: latent columns 128w..128w+127 of every tile; O^T += V^T P^T (V^T by
+//          ds_read_b64_tr_b8, read once per block for all tiles).
+// Two barriers per block: "block b landed, slot b+1 free" and "P of block b published".
 //
-// LDS slot layout (73728 B = 8 subtiles x 9216 B): within a 16-key subtile the 16-byte unit
-// (chunk c of the 36 in a row, key k) sits at (c * 16 + k) * 16. Consecutive lanes of a DMA
-// instruction then fill consecutive units (lane l: key l % 16, chunk 4i + l / 16), the QK operand
-// read of 16 keys x one chunk is 256 contiguous bytes, and the transposed V reads of 8 keys x 16
-// columns are 128 contiguous bytes.
+// LDS slot layout (73728 B = 8 subtiles x 9216 B). Within a 16-key subtile, the 16-byte unit of
+// key k and latent chunk c (c < 32) sits at unit 32 k + (c ^ k), and rope chunk c (32..35) at
+// unit 512 + 16 (c - 32) + k. A latent DMA instruction then moves two keys x 512 contiguous bytes
+// (whole cache lines), and the XOR keeps both the QK operand read (16 keys x one chunk) and the
+// transposed V read (8 keys x 16 columns) free of bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,8 +47,8 @@ constexpr int ROW = 576;
 constexpr int LATENT = 512;
 constexpr int BLK = 128;             // keys per block
 constexpr int NSUB = 8;              // 16-key subtiles per block
-constexpr int WAVES = 8;
-constexpr int THREADS = 512;
+constexpr int WAVES = 4;
+constexpr int THREADS = 256;
 constexpr int SLOT = BLK * ROW;      // 73728
 constexpr int SUBB = 16 * ROW;       // 9216
 constexpr int PPITCH = 144;          // bytes per P row in LDS (128 keys + 16 pad)
@@ -93,14 +97,14 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero_row[ROW];
 template <int T>
 struct Smem {
     static constexpr int OFF_KV = 0;
-    static constexpr int OFF_P = 2 * SLOT;
-    static constexpr int OFF_XM = OFF_P + T * PTILE;           // float [NSUB][T*16]
-    static constexpr int OFF_XS = OFF_XM + NSUB * T * 16 * 4;  // float [NSUB][T*16]
-    static constexpr int OFF_ALPHA = OFF_XS + NSUB * T * 16 * 4;  // float [T*16]
+    static constexpr int OFF_P = 2 * SLOT;                     // E4M3 P [T][16][PPITCH]
+    static constexpr int OFF_ALPHA = OFF_P + T * PTILE;        // float [T*16]
     static constexpr int OFF_FM = OFF_ALPHA + T * 16 * 4;      // float [T*16]
     static constexpr int OFF_FL = OFF_FM + T * 16 * 4;         // float [T*16]
-    static constexpr int OFF_FLAG = OFF_FL + T * 16 * 4;       // uint8 [2][BLK]
-    static constexpr int OFF_MISC = OFF_FLAG + 2 * BLK;        // int [4]
+    static constexpr int OFF_KMASK = OFF_FL + T * 16 * 4;      // uint32 [2][4] key presence bits
+    static constexpr int OFF_IDX = OFF_KMASK + 2 * 16;         // int32 [2][BLK] raw key indices
+    static constexpr int OFF_RP = OFF_IDX + 2 * BLK * 4;       // uint64 [2][BLK] key row pointers
+    static constexpr int OFF_MISC = OFF_RP + 2 * BLK * 8;      // int [4]
     static constexpr int BYTES = OFF_MISC + 16;
 };
 static_assert(Smem<4>::BYTES <= 163840, "LDS budget");
@@ -170,8 +174,8 @@ __device__ inline uint32_t lds_addr(const uint8_t* ptr)
 // One global_load_lds_dwordx4: 16 bytes at this lane's gsrc -> LDS byte lds_base + 16 * lane.
 // Written in asm so that the compiler's wait-count pass does not treat every later LDS read as
 // depending on this DMA (it would wait for the next block's DMA before reading the current one);
-// the kernel waits for the DMA itself (vmcnt(0)) before the barrier that publishes a block. M0 is
-// saved and restored around the instruction.
+// the kernel waits for its DMAs itself (vmcnt(0)) before the barrier that publishes a block. M0
+// is saved and restored.
 __device__ inline void dma16(const uint8_t* gsrc, uint32_t lds_base)
 {
     uint32_t saved;
@@ -186,40 +190,56 @@ __device__ inline void dma16(const uint8_t* gsrc, uint32_t lds_base)
         : "memory");
 }
 
-template <bool DENSE>
-__device__ inline int32_t fetch_index(const Params& p, int g, int64_t jabs, bool inrange)
+// One global_load_lds_dword: 4 bytes at this lane's gsrc -> LDS byte lds_base + 4 * lane (asm
+// for the same reasons as dma16).
+__device__ inline void dma4(const void* gsrc, uint32_t lds_base)
 {
-    if (!inrange)
-        return -1;
-    if (DENSE)
-        return __builtin_nontemporal_load(p.table + (int64_t)g * p.max_pages + jabs / p.page_size);
-    return __builtin_nontemporal_load(p.rows + (int64_t)g * p.K + jabs);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(gsrc)
+        : "memory");
 }
 
-// Issue the 9 DMAs of this wave's 16 keys of a block into LDS slot `slot` and record each key's
-// presence flag. `idx` is the raw index fetched for this lane's key (-1 past the block's count).
 template <bool DENSE>
-__device__ inline void issue_block(const Params& p, uint8_t* smem, int slot, int wave, int lane,
-                                   int64_t jabs, bool inrange, int32_t idx, int flag_off)
+__device__ inline const int32_t* index_ptr(const Params& p, int g, int64_t jabs)
+{
+    if (DENSE)
+        return p.table + (int64_t)g * p.max_pages + (uint32_t)jabs / (uint32_t)p.page_size;
+    return p.rows + (int64_t)g * p.K + jabs;
+}
+
+// The cache row of a key (or -1 when absent) from its raw index (page id or row id).
+template <bool DENSE>
+__device__ inline int64_t key_row(const Params& p, int64_t jabs, bool inrange, int32_t idx)
 {
     int64_t row = -1;
     if (inrange) {
         if (DENSE) {
             if (idx >= 0)
-                row = (int64_t)idx * p.page_size + jabs % p.page_size;
+                row = (int64_t)idx * p.page_size + (int64_t)((uint32_t)jabs % (uint32_t)p.page_size);
         } else {
             row = idx;
         }
     }
-    const bool ok = row >= 0 && row < p.num_rows;
-    const uint8_t* src = ok ? p.kv + row * ROW : g_zero_row;
-    src += 16 * (lane >> 4);
-    const uint32_t dst = lds_addr(smem + slot * SLOT + wave * SUBB);
-#pragma unroll
-    for (int i = 0; i < 9; i++)
-        dma16(src + 64 * i, dst + 1024 * i);
-    if ((lane >> 4) == 0)
-        smem[flag_off + slot * BLK + wave * 16 + (lane & 15)] = ok ? 1 : 0;
+    return (row >= 0 && row < p.num_rows) ? row : -1;
+}
+
+// Source address of DMA instruction i (0..8) of a subtile for this lane, from the row pointers of
+// the subtile's 16 keys (rp: 16 x u64 in LDS). Latent instruction i: key 2i + lane / 32, chunk
+// (lane % 32) ^ key; rope instruction 8: key lane % 16, chunk 32 + lane / 16.
+__device__ inline const uint8_t* dma_src(const uint64_t* rp, int i, int lane)
+{
+    if (i < 8) {
+        const int k = 2 * i + (lane >> 5);
+        return reinterpret_cast<const uint8_t*>(rp[k]) + 16 * ((lane & 31) ^ k);
+    }
+    return reinterpret_cast<const uint8_t*>(rp[lane & 15]) + 512 + 16 * (lane >> 4);
 }
 
 template <int T, bool DENSE>
@@ -260,57 +280,93 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
     const int64_t mine = (n_grp - first) < per ? (n_grp - first) : per;
     const int nblk = (int)((mine + BLK - 1) / BLK);
 
-    // ---- this wave's QK tile and keys ----
-    const int qt = wave % T;              // tile within the set
-    const int kw = wave / T;              // which T-subtile slice of the block
-    const int tile = ts * T + qt;         // tile within the key group
-    int64_t lim;                          // keys [0, lim) of the group are visible to this tile
+    // ---- this wave's QK tile (waves >= T only gather and do PV) ----
+    const bool qk_wave = wave < T;
+    const int qt = qk_wave ? wave : 0;
+    const int tile = ts * T + qt;
+    int64_t lim;   // keys [0, lim) of the group are visible to this tile
     if (DENSE) {
         const int pos = (16 * tile) / p.H;
-        int64_t c = n_grp - p.Q + pos + 1;
+        const int64_t c = n_grp - p.Q + pos + 1;
         lim = c < 0 ? 0 : (c > n_grp ? n_grp : c);
     } else {
         lim = n_grp;
     }
     const int64_t row_base = (int64_t)g * p.rows_per_group;  // first output row of the group
 
-    // ---- the DMA prologue: block 0 now, block 1's index in flight ----
-    const int dkey = 16 * wave + n16;
-    int32_t idx_next = -1;
+    // ---- gather plumbing ----
+    // Wave w gathers keys 32w..32w+31 (subtiles 2w, 2w+1) of every block. Per block: the raw
+    // indices (page ids or row ids) arrive in an LDS slot by DMA one block earlier; lanes 0..31
+    // turn them into row pointers (the zero row when absent) and a presence word; the wave then
+    // issues its 18 row DMAs.
+    int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
+    uint64_t* rpt = reinterpret_cast<uint64_t*>(smem + L::OFF_RP);
+    auto dma_indices = [&](int blk) {  // raw indices of block blk -> idx slot blk % 2
+        const int kk = 32 * wave + lane;
+        const int64_t left = mine - (int64_t)blk * BLK;
+        if (lane < 32 && kk < left)
+            dma4(index_ptr<DENSE>(p, g, first + (int64_t)blk * BLK + kk),
+                 lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * wave * 4));
+    };
+    auto prepare_rows = [&](int blk, int32_t idx) {  // idx: raw index of key 32 wave + lane
+        const int kk = 32 * wave + lane;
+        const int64_t left = mine - (int64_t)blk * BLK;
+        const bool in = lane < 32 && kk < left;
+        const int64_t row = key_row<DENSE>(p, first + (int64_t)blk * BLK + kk, in, idx);
+        const uint64_t ptr = row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW)
+                                      : (uint64_t)(uintptr_t)g_zero_row;
+        if (lane < 32)
+            rpt[(blk & 1) * BLK + kk] = ptr;
+        const uint32_t word = (uint32_t)__ballot(row >= 0);   // lanes 0..31: keys 32w + lane
+        if (lane == 0)
+            *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 1) * 16 + 4 * wave) = word;
+    };
+    // DMA i (0..17) of this wave for block blk: subtile 2w + i / 9, instruction i % 9
+    auto dma_source = [&](int blk, int i) {
+        return dma_src(rpt + (blk & 1) * BLK + 16 * (2 * wave + i / 9), i % 9, lane);
+    };
+    auto dma_one = [&](int blk, const uint8_t* src, int i) {
+        const int sub = 2 * wave + i / 9;
+        dma16(src, lds_addr(smem + (blk & 1) * SLOT + sub * SUBB + 1024 * (i % 9)));
+    };
     if (nblk > 0) {
-        const int64_t j0 = first + dkey;
-        const bool in0 = dkey < mine;
-        const int32_t i0 = fetch_index<DENSE>(p, g, j0, in0);
-        issue_block<DENSE>(p, smem, 0, wave, lane, j0, in0, i0, L::OFF_FLAG);
-        if (nblk > 1) {
-            const int64_t j1 = first + BLK + dkey;
-            idx_next = fetch_index<DENSE>(p, g, j1, dkey < mine - BLK);
-        }
+        int32_t idx0 = -1;
+        if (lane < 32 && 32 * wave + lane < mine)
+            idx0 = *index_ptr<DENSE>(p, g, first + 32 * wave + lane);
+        prepare_rows(0, idx0);
+#pragma unroll
+        for (int i = 0; i < 18; i++) dma_one(0, dma_source(0, i), i);
+        if (nblk > 1)
+            dma_indices(1);
     }
+
+    // per-lane LDS byte offsets within a subtile: the QK operand reads (step st, half h) and the
+    // transposed V reads (column chunk 8 wave + c, key half rb)
+    auto koff = [&](int st, int h) {
+        return st < 4 ? 16 * (32 * n16 + ((8 * st + 2 * grp + h) ^ n16))
+                      : 16 * (512 + 16 * (2 * (grp & 1) + h) + n16);
+    };
+    auto voff = [&](int c, int rb) {
+        const int kk = 8 * rb + (n16 >> 1), cc = 8 * wave + c;
+        return 2 * grp * SUBB + 16 * (32 * kk + (cc ^ kk)) + 8 * (n16 & 1);
+    };
 
     // ---- Q of this wave's tile -> exact E4M3 hi + lo of q * 2^k (B operands) ----
     v8i qhi[4], qlo[4], qrope;
     float row_scale = 0.f;  // scale_log2 * 2^-k for row n16 of tile qt
-    if (nblk > 0) {
+    if (nblk > 0 && qk_wave) {
         const uint16_t* qrow = p.q + (row_base + 16 * tile + n16) * ROW;
-        v4i raw[10];  // 8 bf16 per v4i: [p*2 + h] latent step p half h; [8], [9] rope
+        // 32 bf16 per operand step st: values q[128 st + 32 grp + 0..31] (rope: 512 + 32 (grp & 1))
+        v4i raw[10], rawb[10];
 #pragma unroll
-        for (int st = 0; st < 4; st++) {
-            raw[2 * st] = *reinterpret_cast<const v4i*>(qrow + 128 * st + 32 * grp);
-            raw[2 * st + 1] = *reinterpret_cast<const v4i*>(qrow + 128 * st + 32 * grp + 8);
+        for (int st = 0; st < 5; st++) {
+            const uint16_t* src = st < 4 ? qrow + 128 * st + 32 * grp : qrow + 512 + 32 * (grp & 1);
+            raw[2 * st] = *reinterpret_cast<const v4i*>(src);
+            raw[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 8);
+            rawb[2 * st] = *reinterpret_cast<const v4i*>(src + 16);
+            rawb[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 24);
         }
-        // (32 bf16 per step = 4 x v4i; loaded in two passes below to bound registers)
         float amax = 0.f;
-        v4i rawb[10];
-#pragma unroll
-        for (int st = 0; st < 4; st++) {
-            rawb[2 * st] = *reinterpret_cast<const v4i*>(qrow + 128 * st + 32 * grp + 16);
-            rawb[2 * st + 1] = *reinterpret_cast<const v4i*>(qrow + 128 * st + 32 * grp + 24);
-        }
-        raw[8] = *reinterpret_cast<const v4i*>(qrow + 512 + 32 * (grp & 1));
-        raw[9] = *reinterpret_cast<const v4i*>(qrow + 512 + 32 * (grp & 1) + 8);
-        rawb[8] = *reinterpret_cast<const v4i*>(qrow + 512 + 32 * (grp & 1) + 16);
-        rawb[9] = *reinterpret_cast<const v4i*>(qrow + 512 + 32 * (grp & 1) + 24);
 #pragma unroll
         for (int i = 0; i < 10; i++) {
 #pragma unroll
@@ -328,14 +384,10 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
         if (amax > 0.f) {
             int e;
             const float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
-            // amax = (2m) 2^(e-1); (2m) 2^(e-1+k) <= 1.75 * 2^8
-            k = (2.f * m <= 1.75f) ? (8 - (e - 1)) : (7 - (e - 1));
+            k = (2.f * m <= 1.75f) ? (9 - e) : (8 - e);
         }
         row_scale = ldexpf(p.scale_log2, -k);
-        auto split8 = [&](v4i a, v4i b, int word, uint32_t& hi, uint32_t& lo) {
-            // word 0..3 of the 8-dword operand: a holds dwords 0..3 (bf16 0..7), b dwords 4..7
-            const uint32_t w0 = (uint32_t)(word < 2 ? a[2 * word] : b[2 * (word - 2)]);
-            const uint32_t w1 = (uint32_t)(word < 2 ? a[2 * word + 1] : b[2 * (word - 2) + 1]);
+        auto split4 = [&](uint32_t w0, uint32_t w1, uint32_t& hi, uint32_t& lo) {
             const float x0 = ldexpf(bf16_to_f32(w0 & 0xFFFF), k);
             const float x1 = ldexpf(bf16_to_f32(w0 >> 16), k);
             const float x2 = ldexpf(bf16_to_f32(w1 & 0xFFFF), k);
@@ -347,25 +399,23 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             const float h3 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 3);
             lo = pack_e4m3(x0 - h0, x1 - h1, x2 - h2, x3 - h3);
         };
-        // operand step st: 32 bytes = 32 values q[128 st + 32 grp + 0..31]; raw[2st] holds values
-        // 0..7, raw[2st+1] 8..15, rawb[2st] 16..23, rawb[2st+1] 24..31
 #pragma unroll
         for (int st = 0; st < 5; st++) {
-            const v4i r0 = raw[2 * st], r1 = raw[2 * st + 1], r2 = rawb[2 * st], r3 = rawb[2 * st + 1];
-            uint32_t h[8], l[8];
-            split8(r0, r1, 0, h[0], l[0]);
-            split8(r0, r1, 1, h[1], l[1]);
-            split8(r0, r1, 2, h[2], l[2]);
-            split8(r0, r1, 3, h[3], l[3]);
-            split8(r2, r3, 0, h[4], l[4]);
-            split8(r2, r3, 1, h[5], l[5]);
-            split8(r2, r3, 2, h[6], l[6]);
-            split8(r2, r3, 3, h[7], l[7]);
+            // dword e of the operand holds values 4e..4e+3
+            const uint32_t w[16] = {
+                (uint32_t)raw[2 * st][0], (uint32_t)raw[2 * st][1], (uint32_t)raw[2 * st][2],
+                (uint32_t)raw[2 * st][3], (uint32_t)raw[2 * st + 1][0], (uint32_t)raw[2 * st + 1][1],
+                (uint32_t)raw[2 * st + 1][2], (uint32_t)raw[2 * st + 1][3], (uint32_t)rawb[2 * st][0],
+                (uint32_t)rawb[2 * st][1], (uint32_t)rawb[2 * st][2], (uint32_t)rawb[2 * st][3],
+                (uint32_t)rawb[2 * st + 1][0], (uint32_t)rawb[2 * st + 1][1],
+                (uint32_t)rawb[2 * st + 1][2], (uint32_t)rawb[2 * st + 1][3]};
             v8i vh, vl;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                vh[e] = (int)h[e];
-                vl[e] = (int)l[e];
+                uint32_t h, l;
+                split4(w[2 * e], w[2 * e + 1], h, l);
+                vh[e] = (int)h;
+                vl[e] = (int)l;
             }
             if (st < 4) {
                 qhi[st] = vh;
@@ -378,140 +428,165 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
 
     // ---- the block loop ----
     float m_run = -INFINITY;   // running max (log2 units) of row n16 of tile qt
-    float l_run = 0.f;         // running sum (leader waves kw == 0 only)
-    v4f O[T][4];
+    float l_run = 0.f;         // running sum of the unrounded P of that row
+    v4f O[T][8];               // O^T of columns 128 wave + 16 c + 4 grp + j, rows n16, per tile
 #pragma unroll
     for (int t = 0; t < T; t++)
 #pragma unroll
-        for (int c = 0; c < 4; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const float neg_inf = -INFINITY;
-    float* xm = reinterpret_cast<float*>(smem + L::OFF_XM);
-    float* xs = reinterpret_cast<float*>(smem + L::OFF_XS);
     float* xalpha = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
 
     for (int b = 0; b < nblk; b++) {
         const int slot = b & 1;
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's DMA of block b (and index) landed
-        lds_sync();                          // every wave's DMA landed; slot ^ 1 is free
-        if (b + 1 < nblk) {
-            const int64_t j = first + (int64_t)(b + 1) * BLK + dkey;
-            const bool in = dkey < mine - (int64_t)(b + 1) * BLK;
-            issue_block<DENSE>(p, smem, slot ^ 1, wave, lane, j, in, idx_next, L::OFF_FLAG);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < nblk) {
-            const int64_t j = first + (int64_t)(b + 2) * BLK + dkey;
-            idx_next = fetch_index<DENSE>(p, g, j, dkey < mine - (int64_t)(b + 2) * BLK);
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's DMA of block b (and indices)
+        lds_sync();                          // every wave's DMA landed; slot ^ 1 and P are free
+        const bool have_next = b + 1 < nblk;
+        if (have_next)
+            prepare_rows(b + 1, lane < 32 ? idx_lds[((b + 1) & 1) * BLK + 32 * wave + lane] : -1);
+        if (b + 2 < nblk)
+            dma_indices(b + 2);
+        if (have_next && !qk_wave) {
+#pragma unroll
+            for (int i = 0; i < 18; i++) dma_one(b + 1, dma_source(b + 1, i), i);
         }
 
-        // ---- QK: S^T of this wave's T subtiles ----
         const uint8_t* kslot = smem + slot * SLOT;
-        v4f acc[T];
+        if (qk_wave) {
+            // ---- QK: S^T of all 8 subtiles, K fragments through a ring of RING ahead ----
+            v4f acc[NSUB];
 #pragma unroll
-        for (int u = 0; u < T; u++) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < NSUB; u++) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+            constexpr int NFRAG = 5 * NSUB;  // fragment f: step f / 8, subtile f % 8
+            constexpr int AHEAD = 3, RING = AHEAD + 1;
+            v8i kf[RING];
+            auto load_frag = [&](int f) {
+                const int st = f / NSUB, sub = f % NSUB;
+                return cat(lds_read16(kslot, sub * SUBB + koff(st, 0)),
+                           lds_read16(kslot, sub * SUBB + koff(st, 1)));
+            };
 #pragma unroll
-        for (int st = 0; st < 5; st++) {
-            const int c0 = st < 4 ? 8 * st + 2 * grp : 32 + 2 * (grp & 1);
+            for (int f = 0; f < AHEAD; f++) kf[f % RING] = load_frag(f);
+            // the next block's 18 DMAs, spread over the MFMAs: DMA j's source is read at
+            // fragment 2j and the DMA issued at fragment 2j + 2
+            const uint8_t* dsrc[2] = {nullptr, nullptr};
 #pragma unroll
-            for (int u = 0; u < T; u++) {
-                const int sub = kw * T + u;
-                const int off = sub * SUBB + (c0 * 16 + n16) * 16;
-                const v8i a = cat(lds_read16(kslot, off), lds_read16(kslot, off + 256));
+            for (int f = 0; f < NFRAG; f++) {
+                if (have_next && (f & 1) == 0) {
+                    const int j = f / 2;
+                    if (j >= 1 && j <= 18)
+                        dma_one(b + 1, dsrc[(j - 1) & 1], j - 1);
+                    if (j < 18)
+                        dsrc[j & 1] = dma_source(b + 1, j);
+                }
+                if (f + AHEAD < NFRAG)
+                    kf[(f + AHEAD) % RING] = load_frag(f + AHEAD);
+                const int st = f / NSUB, sub = f % NSUB;
                 if (st < 4) {
-                    acc[u] = mfma(a, qhi[st], acc[u]);
-                    acc[u] = mfma(a, qlo[st], acc[u]);
+                    acc[sub] = mfma(kf[f % RING], qhi[st], acc[sub]);
+                    acc[sub] = mfma(kf[f % RING], qlo[st], acc[sub]);
                 } else {
-                    acc[u] = mfma(a, qrope, acc[u]);
+                    acc[sub] = mfma(kf[f % RING], qrope, acc[sub]);
                 }
             }
-        }
 
-        // ---- scale, mask, row max over this wave's keys ----
-        const int64_t kbase = first + (int64_t)b * BLK;
-        float x[T][4];
-        float wmax = neg_inf;
+            // ---- visibility of this lane's 32 keys: bit 4u + j <-> key 16u + 4 grp + j ----
+            const int64_t kbase = first + (int64_t)b * BLK;
+            const int64_t lr = lim - kbase;      // keys of the block before the tile's bound
+            const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
+            const v4i mw = lds_read16(smem, L::OFF_KMASK + slot * 16);
+            uint32_t vis = 0;
 #pragma unroll
-        for (int u = 0; u < T; u++) {
-            const int sub = kw * T + u;
-            const int kin = 16 * sub + 4 * grp;  // first of this lane's 4 keys in the block
-            const uint32_t fl = *reinterpret_cast<const uint32_t*>(smem + L::OFF_FLAG + slot * BLK + kin);
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const bool vis = ((fl >> (8 * j)) & 0xFF) && (kbase + kin + j < lim);
-                x[u][j] = vis ? acc[u][j] * row_scale : neg_inf;
-                wmax = fmaxf(wmax, x[u][j]);
+            for (int u = 0; u < NSUB; u++) {
+                const int sh = 16 * (u & 1) + 4 * grp;
+                uint32_t nib = ((uint32_t)mw[u >> 1] >> sh) & 0xFu;
+                const int kfirst = 16 * u + 4 * grp;          // key of bit 0 of the nibble
+                const int keep = lim_rel - kfirst;            // how many of the 4 are in bound
+                nib &= keep >= 4 ? 0xFu : (keep <= 0 ? 0u : ((1u << keep) - 1u));
+                vis |= nib << (4 * u);
             }
-        }
-        wmax = wave_max16(wmax);
-        if (grp == 0)
-            xm[kw * T * 16 + qt * 16 + n16] = wmax;
-        lds_sync();
+            // ---- scale, mask, row max over the block (in-lane, then across the 4 k-groups) ----
+            float bmax = neg_inf;
+            if (__all(vis == 0xFFFFFFFFu)) {
+#pragma unroll
+                for (int u = 0; u < NSUB; u++) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) acc[u][j] = acc[u][j] * row_scale;
+                    bmax = fmaxf(bmax, fmaxf(fmaxf(acc[u][0], acc[u][1]), fmaxf(acc[u][2], acc[u][3])));
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < NSUB; u++) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc[u][j] = ((vis >> (4 * u + j)) & 1u) ? acc[u][j] * row_scale : neg_inf;
+                    bmax = fmaxf(bmax, fmaxf(fmaxf(acc[u][0], acc[u][1]), fmaxf(acc[u][2], acc[u][3])));
+                }
+            }
+            bmax = wave_max16(bmax);
+            const float m_new = fmaxf(m_run, bmax);
+            const float alpha = (m_run == neg_inf) ? 1.f : exp2f(m_run - m_new);
+            const float m_use = (m_new == neg_inf) ? 0.f : m_new;   // exp2(-inf - m_use) = 0
 
-        // ---- running max, P (E4M3 at 448), per-subtile row sums ----
-        float bmax = neg_inf;
-#pragma unroll
-        for (int w = 0; w < WAVES / T; w++) bmax = fmaxf(bmax, xm[w * T * 16 + qt * 16 + n16]);
-        const float m_new = fmaxf(m_run, bmax);
-        const float alpha = (m_run == neg_inf) ? 1.f : exp2f(m_run - m_new);
-#pragma unroll
-        for (int u = 0; u < T; u++) {
-            const int sub = kw * T + u;
-            float pr[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                pr[j] = (x[u][j] == neg_inf) ? 0.f : ANCHOR * exp2f(x[u][j] - m_new);
-            const uint32_t packed = pack_e4m3(pr[0], pr[1], pr[2], pr[3]);
-            *reinterpret_cast<uint32_t*>(smem + L::OFF_P + qt * PTILE + n16 * PPITCH + 16 * sub +
-                                         4 * grp) = packed;
-            float ssum = ((pr[0] + pr[1]) + pr[2]) + pr[3];
-            ssum = wave_sum16(ssum);
-            if (grp == 0)
-                xs[sub * T * 16 + qt * 16 + n16] = ssum;
-        }
-        if (kw == 0 && grp == 0)
-            xalpha[qt * 16 + n16] = alpha;
-        m_run = m_new;
-        lds_sync();
-
-        // ---- l update (leader waves): block sum in subtile order ----
-        if (kw == 0) {
+            // ---- P = 448 exp2(x - m) -> E4M3 into LDS (P <= 448: no clamp); row sum of the
+            // unrounded P in a fixed order ----
             float bsum = 0.f;
 #pragma unroll
-            for (int sub = 0; sub < NSUB; sub++) bsum = bsum + xs[sub * T * 16 + qt * 16 + n16];
+            for (int u = 0; u < NSUB; u++) {
+                float pr[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) pr[j] = ANCHOR * exp2f(acc[u][j] - m_use);
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
+                *reinterpret_cast<uint32_t*>(smem + L::OFF_P + qt * PTILE + n16 * PPITCH +
+                                             16 * u + 4 * grp) = (uint32_t)w;
+                bsum = bsum + (((pr[0] + pr[1]) + pr[2]) + pr[3]);
+            }
+            bsum = wave_sum16(bsum);
             l_run = l_run * alpha + bsum;
+            m_run = m_new;
+            if (grp == 0)
+                xalpha[qt * 16 + n16] = alpha;
         }
+        lds_sync();   // P and the rescale factors of every tile are published
 
-        // ---- PV: O^T[64 columns of this wave] += V^T P^T for every tile ----
+        // ---- PV: O^T[128 columns of this wave] += V^T P^T for every tile ----
         v8i pb[T];
 #pragma unroll
         for (int t = 0; t < T; t++) {
             const float a = xalpha[t * 16 + n16];
+            if (!__all(a == 1.f)) {
 #pragma unroll
-            for (int c = 0; c < 4; c++) O[t][c] *= a;
+                for (int c = 0; c < 8; c++) O[t][c] *= a;
+            }
             const int off = L::OFF_P + t * PTILE + n16 * PPITCH + 32 * grp;
             pb[t] = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
         }
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const int chunk = 4 * wave + c;
+        auto load_vt = [&](int c) {
             v2i tr[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int off = slot * SLOT + (2 * grp + (r >> 1)) * SUBB +
-                                (chunk * 16 + 8 * (r & 1) + (n16 >> 1)) * 16 + 8 * (n16 & 1);
+                const int off = slot * SLOT + (r >> 1) * SUBB + voff(c, r & 1);
                 tr[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(smem + off));
             }
-            const v8i va = v8i{tr[0].x, tr[0].y, tr[1].x, tr[1].y, tr[2].x, tr[2].y, tr[3].x, tr[3].y};
+            return v8i{tr[0].x, tr[0].y, tr[1].x, tr[1].y, tr[2].x, tr[2].y, tr[3].x, tr[3].y};
+        };
+        v8i va[2];
+        va[0] = load_vt(0);
 #pragma unroll
-            for (int t = 0; t < T; t++) O[t][c] = mfma(va, pb[t], O[t][c]);
+        for (int c = 0; c < 8; c++) {
+            if (c + 1 < 8)
+                va[(c + 1) & 1] = load_vt(c + 1);
+#pragma unroll
+            for (int t = 0; t < T; t++) O[t][c] = mfma(va[c & 1], pb[t], O[t][c]);
         }
     }
 
     // ---- per-row (m, l) to LDS for the column owners ----
     float* fm = reinterpret_cast<float*>(smem + L::OFF_FM);
     float* fl = reinterpret_cast<float*>(smem + L::OFF_FL);
-    if (kw == 0 && grp == 0) {
+    if (qk_wave && grp == 0) {
         fm[qt * 16 + n16] = m_run;
         fl[qt * 16 + n16] = l_run;
     }
@@ -524,8 +599,8 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             const float lt = fl[t * 16 + n16];
             const int64_t orow = row_base + 16 * (ts * T + t) + n16;
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const int col = 64 * wave + 16 * c + 4 * grp;
+            for (int c = 0; c < 8; c++) {
+                const int col = 128 * wave + 16 * c + 4 * grp;
                 uint32_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
                 if (lt > 0.f) {
                     b0 = f32_to_bf16_rne(O[t][c][0] / lt * p.k_scale);
@@ -537,7 +612,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
                 *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) = w;
             }
         }
-        if (kw == 0 && grp == 0) {
+        if (qk_wave && grp == 0) {
             const int64_t orow = row_base + 16 * tile + n16;
             p.lse[orow] = (l_run > 0.f) ? (m_run - LOG2_ANCHOR + log2f(l_run)) * LN2 : neg_inf;
         }
@@ -549,28 +624,31 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
     for (int t = 0; t < T; t++) {
         const int64_t orow = row_base + 16 * (ts * T + t) + n16;
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const int col = 64 * wave + 16 * c + 4 * grp;
+        for (int c = 0; c < 8; c++) {
+            const int col = 128 * wave + 16 * c + 4 * grp;
             *reinterpret_cast<v4f*>(p.ws_o + (orow * p.S + s) * LATENT + col) = O[t][c];
         }
     }
-    if (kw == 0 && grp == 0) {
+    if (qk_wave && grp == 0) {
         const int64_t orow = row_base + 16 * tile + n16;
         p.ws_ml[(orow * p.S + s) * 2 + 0] = m_run;
         p.ws_ml[(orow * p.S + s) * 2 + 1] = l_run;
     }
-    __threadfence();   // release this thread's partial at agent scope
+    // Every thread's partial stores have completed (vmcnt(0)) before the barrier; one thread then
+    // releases them at agent scope and counts this split in.
+    __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();
     int* misc = reinterpret_cast<int*>(smem + L::OFF_MISC);
     uint32_t* cnt = p.ws_cnt + (int64_t)g * p.tilesets + ts;
     if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         misc[0] = (old == (uint32_t)(p.S - 1)) ? 1 : 0;
     }
     __syncthreads();
     if (misc[0] == 0)
         return;
-    __threadfence();   // acquire the other splits' partials
 
     // merge: T*16 rows x 32 column chunks of 16; thread -> (row, chunk) items
     for (int item = tid; item < T * 16 * 32; item += THREADS) {
@@ -651,12 +729,13 @@ int choose_tiles(int tiles_per_group)
     return 1;
 }
 
-// Splits from shapes only: enough workgroups to cover the 256 CUs about twice, each with at least
-// two 128-key blocks of its group's key capacity.
+// Splits from shapes only: enough workgroups to cover the 256 CUs once (one workgroup fills a CU's
+// LDS), each with at least two 128-key blocks of its group's key capacity; every extra split adds
+// a partial per row and a merge.
 int choose_splits(int groups, int tilesets, int64_t max_keys)
 {
     const int64_t wgs = (int64_t)groups * tilesets;
-    int64_t s = (512 + wgs - 1) / wgs;
+    int64_t s = 256 / wgs;
     const int64_t cap = max_keys / (2 * BLK);
     if (s > cap)
         s = cap;

@@ -99,3 +99,19 @@ def test_workspace_sizes_and_plans():
         assert p.splits >= 1 and (Q * H // 16) % p.tiles == 0
     with pytest.raises(mla.MlaError):
         mla.plan_dense(1, 1, 20, 4, 64)
+
+
+def test_chooser_picks_the_benchmark_plans():
+    """The shapes-only plan chooser agrees with the plans the benchmark launches."""
+    import workloads as wl
+    shapes = {
+        "tiny_sparse": ("sparse", 2, 1, 16, 64),
+        "dense_paged": ("dense", 64, 1, 128, 128),
+        "latency_sparse": ("sparse", 4, 5, 16, 256),
+        "topk_sparse": ("sparse", 32, 5, 64, 2048),
+        "long_dense": ("dense", 8, 4, 128, 2048),
+    }
+    for name, (kind, B, Q, H, n) in shapes.items():
+        p = mla.plan_dense(B, Q, H, n, 64) if kind == "dense" else mla.plan_sparse(B, Q, H, n)
+        w = wl.WORKLOADS[name]
+        assert (p.splits, p.tiles) == (w.splits, w.tiles), name
