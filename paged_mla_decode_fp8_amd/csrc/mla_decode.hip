@@ -18,18 +18,23 @@
 //     cross-workgroup merge through a global workspace with a per-row arrival counter (the last
 //     arriver merges in a fixed order and resets the counter), so results do not depend on timing.
 //
-// Workgroup = (key group, split, set of T 16-row tiles), 256 threads = 4 waves, one wave per SIMD
-// (up to 512 registers per lane). Per 128-key block:
-//   DMA    wave w gathers keys 32w..32w+31 of the next block into the other LDS slot (18 x 1 KB
-//          global_load_lds_dwordx4); absent keys read a zero row.
-//   QK     wave w < T owns tile w: S^T of all 128 keys x its 16 rows, 9 MFMAs per 16-key subtile
-//          (4 latent steps x {hi, lo} + 1 rope step packing rope hi | rope lo against rope | rope),
-//          K fragments streamed from LDS through a register ring a few fragments ahead.
-//   softmax  entirely inside the tile's wave: row max, running max, P = 448 exp2(x - max) -> E4M3,
-//          row sums of the unrounded P in a fixed order; P and the rescale factor go to LDS.
-//   PV     wave w: latent columns 128w..128w+127 of every tile; O^T += V^T P^T (V^T by
-//          ds_read_b64_tr_b8, read once per block for all tiles).
-// Two barriers per block: "block b landed, slot b+1 free" and "P of block b published".
+// Workgroup = (key group, split, set of T 16-row tiles), 512 threads = 8 waves, two per SIMD,
+// specialised as on the AMD page (QK waves and PV waves). Wave i runs on SIMD i % 4:
+//   QK waves 0..3: wave t owns tile t. Per 128-key block: S^T of all 128 keys x 16 rows by 9
+//          16x16x128 MFMAs per 16-key subtile (4 latent steps x {hi, lo} + 1 rope step packing
+//          rope hi | rope lo against rope | rope), K fragments streamed from LDS through a register
+//          ring; then the whole softmax inside the wave: row max, running max, P = 448 exp2(x - max)
+//          -> E4M3 into LDS, row sums of the unrounded P in a fixed order, rescale factor to LDS.
+//   PV waves 4..7: wave 4 + c owns latent columns 128c..128c+127 of every tile. They run one block
+//          behind: O^T += V^T P^T of block i - 1 while the QK waves work on block i, so on each
+//          SIMD one wave's softmax VALU overlaps the other's MFMAs. They also do the gather: raw
+//          indices DMA'd into LDS two blocks ahead, row pointers, 18 row DMAs per wave one block
+//          ahead into the other LDS slot, and they copy each block's V^T (ds_read_b64_tr_b8) into
+//          registers while its slot is valid, so two slots suffice.
+// Three barriers per block: B1 "block i landed, P of block i - 1 published", B2 "the QK waves have
+// issued the MFMAs of block i" (the PV waves' MFMAs of block i - 1 then overlap the QK waves'
+// softmax) and B3 "the PV waves hold P of block i - 1 and V^T of block i in registers" (the QK
+// waves then write P of block i).
 //
 // LDS slot layout (73728 B = 8 subtiles x 9216 B). Within a 16-key subtile, the 16-byte unit of
 // key k and latent chunk c (c < 32) sits at unit 32 k + (c ^ k), and rope chunk c (32..35) at
@@ -47,8 +52,8 @@ constexpr int ROW = 576;
 constexpr int LATENT = 512;
 constexpr int BLK = 128;             // keys per block
 constexpr int NSUB = 8;              // 16-key subtiles per block
-constexpr int WAVES = 4;
-constexpr int THREADS = 256;
+constexpr int WAVES = 8;
+constexpr int THREADS = 512;
 constexpr int SLOT = BLK * ROW;      // 73728
 constexpr int SUBB = 16 * ROW;       // 9216
 constexpr int PPITCH = 144;          // bytes per P row in LDS (128 keys + 16 pad)
@@ -151,18 +156,24 @@ __device__ inline void lds_sync()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one MFMA row / column held in the four
+// k-groups), with gfx950's row-swap permutes: after a 32-lane swap each half holds the other
+// half's value, after a 16-lane swap each 16-lane row the neighbouring row's. Every lane ends with
+// the same value, combined in the same order.
 __device__ inline float wave_max16(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ inline float wave_sum16(float v)
 {
-    v = v + __shfl_xor(v, 16);
-    v = v + __shfl_xor(v, 32);
-    return v;
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // The 32-bit LDS address of a pointer into __shared__ memory (wave-uniform by construction).
@@ -242,120 +253,68 @@ __device__ inline const uint8_t* dma_src(const uint64_t* rp, int i, int lane)
     return reinterpret_cast<const uint8_t*>(rp[lane & 15]) + 512 + 16 * (lane >> 4);
 }
 
-template <int T, bool DENSE>
-__global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
-{
-    using L = Smem<T>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+// The work of one workgroup: key group g, split s of S, tile set ts; the split's keys
+// [first, first + mine) of the group's n_grp, in nblk blocks of 128.
+struct Work {
+    int g, s, ts, nblk;
+    int64_t n_grp, first, mine, row_base;
+};
 
-    // ---- which (key group, split, tile set): a split's tile sets share one XCD (blockIdx % 8) ----
+template <bool DENSE>
+__device__ inline bool decode_work(const Params& p, Work& w)
+{
+    // a split's tile sets share one XCD (blockIdx % 8)
     const int bid = blockIdx.x;
     const int xcd = bid & 7;
     const int slotid = bid >> 3;
-    const int ts = slotid % p.tilesets;
+    w.ts = slotid % p.tilesets;
     const int gs = (slotid / p.tilesets) * 8 + xcd;
     if (gs >= p.gs_count)
-        return;
-    const int s = gs / p.groups;
-    const int g = gs % p.groups;
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int n16 = lane & 15;   // MFMA row / column within 16
-    const int grp = lane >> 4;   // MFMA k-group 0..3
-
-    // ---- key range of this split (the pages' per / first / mine) ----
-    int64_t n_grp;
+        return false;
+    w.s = gs / p.groups;
+    w.g = gs % p.groups;
     if (DENSE) {
         const int64_t cap = (int64_t)p.max_pages * p.page_size;
-        const int64_t sl = p.seq_lens[g];
-        n_grp = sl < 0 ? 0 : (sl > cap ? cap : sl);
+        const int64_t sl = p.seq_lens[w.g];
+        w.n_grp = sl < 0 ? 0 : (sl > cap ? cap : sl);
     } else {
-        const int64_t v = p.valid[g];
-        n_grp = v < 0 ? 0 : (v > p.K ? p.K : v);
+        const int64_t v = p.valid[w.g];
+        w.n_grp = v < 0 ? 0 : (v > p.K ? p.K : v);
     }
-    const int64_t per = (n_grp + p.S - 1) / p.S;
-    const int64_t first = (int64_t)s * per < n_grp ? (int64_t)s * per : n_grp;
-    const int64_t mine = (n_grp - first) < per ? (n_grp - first) : per;
-    const int nblk = (int)((mine + BLK - 1) / BLK);
+    // the pages' per / first / mine
+    const int64_t per = (w.n_grp + p.S - 1) / p.S;
+    w.first = (int64_t)w.s * per < w.n_grp ? (int64_t)w.s * per : w.n_grp;
+    w.mine = (w.n_grp - w.first) < per ? (w.n_grp - w.first) : per;
+    w.nblk = (int)((w.mine + BLK - 1) / BLK);
+    w.row_base = (int64_t)w.g * p.rows_per_group;
+    return true;
+}
 
-    // ---- this wave's QK tile (waves >= T only gather and do PV) ----
-    const bool qk_wave = wave < T;
-    const int qt = qk_wave ? wave : 0;
-    const int tile = ts * T + qt;
+// ---- QK waves: Q stage, S^T = K (hi + lo)^T, softmax; P and the rescale factors to LDS ----
+template <int T, bool DENSE>
+__device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Work& w, int qw,
+                                        int lane)
+{
+    using L = Smem<T>;
+    const int n16 = lane & 15;   // MFMA row / column within 16
+    const int grp = lane >> 4;   // MFMA k-group 0..3
+    const bool active = qw < T;
+    const int qt = active ? qw : 0;
+    const int tile = w.ts * T + qt;
     int64_t lim;   // keys [0, lim) of the group are visible to this tile
     if (DENSE) {
         const int pos = (16 * tile) / p.H;
-        const int64_t c = n_grp - p.Q + pos + 1;
-        lim = c < 0 ? 0 : (c > n_grp ? n_grp : c);
+        const int64_t c = w.n_grp - p.Q + pos + 1;
+        lim = c < 0 ? 0 : (c > w.n_grp ? w.n_grp : c);
     } else {
-        lim = n_grp;
-    }
-    const int64_t row_base = (int64_t)g * p.rows_per_group;  // first output row of the group
-
-    // ---- gather plumbing ----
-    // Wave w gathers keys 32w..32w+31 (subtiles 2w, 2w+1) of every block. Per block: the raw
-    // indices (page ids or row ids) arrive in an LDS slot by DMA one block earlier; lanes 0..31
-    // turn them into row pointers (the zero row when absent) and a presence word; the wave then
-    // issues its 18 row DMAs.
-    int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
-    uint64_t* rpt = reinterpret_cast<uint64_t*>(smem + L::OFF_RP);
-    auto dma_indices = [&](int blk) {  // raw indices of block blk -> idx slot blk % 2
-        const int kk = 32 * wave + lane;
-        const int64_t left = mine - (int64_t)blk * BLK;
-        if (lane < 32 && kk < left)
-            dma4(index_ptr<DENSE>(p, g, first + (int64_t)blk * BLK + kk),
-                 lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * wave * 4));
-    };
-    auto prepare_rows = [&](int blk, int32_t idx) {  // idx: raw index of key 32 wave + lane
-        const int kk = 32 * wave + lane;
-        const int64_t left = mine - (int64_t)blk * BLK;
-        const bool in = lane < 32 && kk < left;
-        const int64_t row = key_row<DENSE>(p, first + (int64_t)blk * BLK + kk, in, idx);
-        const uint64_t ptr = row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW)
-                                      : (uint64_t)(uintptr_t)g_zero_row;
-        if (lane < 32)
-            rpt[(blk & 1) * BLK + kk] = ptr;
-        const uint32_t word = (uint32_t)__ballot(row >= 0);   // lanes 0..31: keys 32w + lane
-        if (lane == 0)
-            *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 1) * 16 + 4 * wave) = word;
-    };
-    // DMA i (0..17) of this wave for block blk: subtile 2w + i / 9, instruction i % 9
-    auto dma_source = [&](int blk, int i) {
-        return dma_src(rpt + (blk & 1) * BLK + 16 * (2 * wave + i / 9), i % 9, lane);
-    };
-    auto dma_one = [&](int blk, const uint8_t* src, int i) {
-        const int sub = 2 * wave + i / 9;
-        dma16(src, lds_addr(smem + (blk & 1) * SLOT + sub * SUBB + 1024 * (i % 9)));
-    };
-    if (nblk > 0) {
-        int32_t idx0 = -1;
-        if (lane < 32 && 32 * wave + lane < mine)
-            idx0 = *index_ptr<DENSE>(p, g, first + 32 * wave + lane);
-        prepare_rows(0, idx0);
-#pragma unroll
-        for (int i = 0; i < 18; i++) dma_one(0, dma_source(0, i), i);
-        if (nblk > 1)
-            dma_indices(1);
+        lim = w.n_grp;
     }
 
-    // per-lane LDS byte offsets within a subtile: the QK operand reads (step st, half h) and the
-    // transposed V reads (column chunk 8 wave + c, key half rb)
-    auto koff = [&](int st, int h) {
-        return st < 4 ? 16 * (32 * n16 + ((8 * st + 2 * grp + h) ^ n16))
-                      : 16 * (512 + 16 * (2 * (grp & 1) + h) + n16);
-    };
-    auto voff = [&](int c, int rb) {
-        const int kk = 8 * rb + (n16 >> 1), cc = 8 * wave + c;
-        return 2 * grp * SUBB + 16 * (32 * kk + (cc ^ kk)) + 8 * (n16 & 1);
-    };
-
-    // ---- Q of this wave's tile -> exact E4M3 hi + lo of q * 2^k (B operands) ----
+    // ---- Q of this tile -> exact E4M3 hi + lo of q * 2^k (B operands) ----
     v8i qhi[4], qlo[4], qrope;
-    float row_scale = 0.f;  // scale_log2 * 2^-k for row n16 of tile qt
-    if (nblk > 0 && qk_wave) {
-        const uint16_t* qrow = p.q + (row_base + 16 * tile + n16) * ROW;
+    float row_scale = 0.f;  // scale_log2 * 2^-k for row n16
+    if (w.nblk > 0 && active) {
+        const uint16_t* qrow = p.q + (w.row_base + 16 * tile + n16) * ROW;
         // 32 bf16 per operand step st: values q[128 st + 32 grp + 0..31] (rope: 512 + 32 (grp & 1))
         v4i raw[10], rawb[10];
 #pragma unroll
@@ -402,7 +361,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
 #pragma unroll
         for (int st = 0; st < 5; st++) {
             // dword e of the operand holds values 4e..4e+3
-            const uint32_t w[16] = {
+            const uint32_t wd[16] = {
                 (uint32_t)raw[2 * st][0], (uint32_t)raw[2 * st][1], (uint32_t)raw[2 * st][2],
                 (uint32_t)raw[2 * st][3], (uint32_t)raw[2 * st + 1][0], (uint32_t)raw[2 * st + 1][1],
                 (uint32_t)raw[2 * st + 1][2], (uint32_t)raw[2 * st + 1][3], (uint32_t)rawb[2 * st][0],
@@ -413,7 +372,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
 #pragma unroll
             for (int e = 0; e < 8; e++) {
                 uint32_t h, l;
-                split4(w[2 * e], w[2 * e + 1], h, l);
+                split4(wd[2 * e], wd[2 * e + 1], h, l);
                 vh[e] = (int)h;
                 vl[e] = (int)l;
             }
@@ -426,40 +385,31 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
         }
     }
 
-    // ---- the block loop ----
-    float m_run = -INFINITY;   // running max (log2 units) of row n16 of tile qt
-    float l_run = 0.f;         // running sum of the unrounded P of that row
-    v4f O[T][8];               // O^T of columns 128 wave + 16 c + 4 grp + j, rows n16, per tile
-#pragma unroll
-    for (int t = 0; t < T; t++)
-#pragma unroll
-        for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
-
+    // this lane's LDS byte offset within a subtile of its operand read (step st, half h)
+    auto koff = [&](int st, int h) {
+        return st < 4 ? 16 * (32 * n16 + ((8 * st + 2 * grp + h) ^ n16))
+                      : 16 * (512 + 16 * (2 * (grp & 1) + h) + n16);
+    };
     const float neg_inf = -INFINITY;
+    float m_run = neg_inf;   // running max (log2 units) of row n16
+    float l_run = 0.f;       // running sum of the unrounded P of that row
     float* xalpha = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
 
-    for (int b = 0; b < nblk; b++) {
-        const int slot = b & 1;
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's DMA of block b (and indices)
-        lds_sync();                          // every wave's DMA landed; slot ^ 1 and P are free
-        const bool have_next = b + 1 < nblk;
-        if (have_next)
-            prepare_rows(b + 1, lane < 32 ? idx_lds[((b + 1) & 1) * BLK + 32 * wave + lane] : -1);
-        if (b + 2 < nblk)
-            dma_indices(b + 2);
-        if (have_next && !qk_wave) {
-#pragma unroll
-            for (int i = 0; i < 18; i++) dma_one(b + 1, dma_source(b + 1, i), i);
-        }
-
-        const uint8_t* kslot = smem + slot * SLOT;
-        if (qk_wave) {
-            // ---- QK: S^T of all 8 subtiles, K fragments through a ring of RING ahead ----
-            v4f acc[NSUB];
+    // iteration i: QK and softmax of block i (the PV waves work on block i - 1)
+    for (int i = 0; i <= w.nblk; i++) {
+        const int slot = i & 1;
+        lds_sync();   // B1: block i landed; P of block i - 1 published
+        const bool work = active && i < w.nblk;
+        v4f acc[NSUB];
+        if (work) {
+            const uint8_t* kslot = smem + slot * SLOT;
 #pragma unroll
             for (int u = 0; u < NSUB; u++) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
-            constexpr int NFRAG = 5 * NSUB;  // fragment f: step f / 8, subtile f % 8
-            constexpr int AHEAD = 3, RING = AHEAD + 1;
+            // Fragment f: step f / 8, subtile f % 8. Step f issues the hi MFMA of fragment f (or its
+            // packed rope MFMA) and the lo MFMA of fragment f - 1, so no MFMA waits on the one just
+            // issued; a fragment stays in the ring until its lo MFMA.
+            constexpr int NFRAG = 5 * NSUB;
+            constexpr int AHEAD = 2, RING = AHEAD + 2;
             v8i kf[RING];
             auto load_frag = [&](int f) {
                 const int st = f / NSUB, sub = f % NSUB;
@@ -468,139 +418,222 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             };
 #pragma unroll
             for (int f = 0; f < AHEAD; f++) kf[f % RING] = load_frag(f);
-            // the next block's 18 DMAs, spread over the MFMAs: DMA j's source is read at
-            // fragment 2j and the DMA issued at fragment 2j + 2
-            const uint8_t* dsrc[2] = {nullptr, nullptr};
 #pragma unroll
-            for (int f = 0; f < NFRAG; f++) {
-                if (have_next && (f & 1) == 0) {
-                    const int j = f / 2;
-                    if (j >= 1 && j <= 18)
-                        dma_one(b + 1, dsrc[(j - 1) & 1], j - 1);
-                    if (j < 18)
-                        dsrc[j & 1] = dma_source(b + 1, j);
-                }
+            for (int f = 0; f <= NFRAG; f++) {
                 if (f + AHEAD < NFRAG)
                     kf[(f + AHEAD) % RING] = load_frag(f + AHEAD);
-                const int st = f / NSUB, sub = f % NSUB;
-                if (st < 4) {
-                    acc[sub] = mfma(kf[f % RING], qhi[st], acc[sub]);
-                    acc[sub] = mfma(kf[f % RING], qlo[st], acc[sub]);
-                } else {
-                    acc[sub] = mfma(kf[f % RING], qrope, acc[sub]);
+                if (f < NFRAG) {
+                    const int st = f / NSUB, sub = f % NSUB;
+                    acc[sub] = mfma(kf[f % RING], st < 4 ? qhi[st] : qrope, acc[sub]);
+                }
+                if (f >= 1 && f - 1 < 4 * NSUB) {
+                    const int st = (f - 1) / NSUB, sub = (f - 1) % NSUB;
+                    acc[sub] = mfma(kf[(f - 1) % RING], qlo[st], acc[sub]);
                 }
             }
-
+        }
+        lds_sync();   // B2: the PV waves start on block i - 1
+        uint32_t pk[NSUB];   // E4M3 P of this lane's 4 keys of each subtile
+        float alpha = 1.f;
+        if (work) {
             // ---- visibility of this lane's 32 keys: bit 4u + j <-> key 16u + 4 grp + j ----
-            const int64_t kbase = first + (int64_t)b * BLK;
+            const int64_t kbase = w.first + (int64_t)i * BLK;
             const int64_t lr = lim - kbase;      // keys of the block before the tile's bound
             const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
             const v4i mw = lds_read16(smem, L::OFF_KMASK + slot * 16);
             uint32_t vis = 0;
 #pragma unroll
             for (int u = 0; u < NSUB; u++) {
-                const int sh = 16 * (u & 1) + 4 * grp;
-                uint32_t nib = ((uint32_t)mw[u >> 1] >> sh) & 0xFu;
-                const int kfirst = 16 * u + 4 * grp;          // key of bit 0 of the nibble
-                const int keep = lim_rel - kfirst;            // how many of the 4 are in bound
+                uint32_t nib = ((uint32_t)mw[u >> 1] >> (16 * (u & 1) + 4 * grp)) & 0xFu;
+                const int keep = lim_rel - (16 * u + 4 * grp);   // how many of the 4 are in bound
                 nib &= keep >= 4 ? 0xFu : (keep <= 0 ? 0u : ((1u << keep) - 1u));
                 vis |= nib << (4 * u);
             }
-            // ---- scale, mask, row max over the block (in-lane, then across the 4 k-groups) ----
+            // ---- mask, row max over the block (in-lane, then across the 4 k-groups). The row
+            // scale is positive, so max(s * scale) = scale * max(s) exactly. ----
             float bmax = neg_inf;
-            if (__all(vis == 0xFFFFFFFFu)) {
+            if (!__all(vis == 0xFFFFFFFFu)) {
 #pragma unroll
-                for (int u = 0; u < NSUB; u++) {
-#pragma unroll
-                    for (int j = 0; j < 4; j++) acc[u][j] = acc[u][j] * row_scale;
-                    bmax = fmaxf(bmax, fmaxf(fmaxf(acc[u][0], acc[u][1]), fmaxf(acc[u][2], acc[u][3])));
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < NSUB; u++) {
+                for (int u = 0; u < NSUB; u++)
 #pragma unroll
                     for (int j = 0; j < 4; j++)
-                        acc[u][j] = ((vis >> (4 * u + j)) & 1u) ? acc[u][j] * row_scale : neg_inf;
-                    bmax = fmaxf(bmax, fmaxf(fmaxf(acc[u][0], acc[u][1]), fmaxf(acc[u][2], acc[u][3])));
-                }
+                        acc[u][j] = ((vis >> (4 * u + j)) & 1u) ? acc[u][j] : neg_inf;
             }
-            bmax = wave_max16(bmax);
+#pragma unroll
+            for (int u = 0; u < NSUB; u++)
+                bmax = fmaxf(bmax, fmaxf(fmaxf(acc[u][0], acc[u][1]), fmaxf(acc[u][2], acc[u][3])));
+            bmax = wave_max16(bmax) * row_scale;
             const float m_new = fmaxf(m_run, bmax);
-            const float alpha = (m_run == neg_inf) ? 1.f : exp2f(m_run - m_new);
+            alpha = (m_run == neg_inf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             const float m_use = (m_new == neg_inf) ? 0.f : m_new;   // exp2(-inf - m_use) = 0
-
-            // ---- P = 448 exp2(x - m) -> E4M3 into LDS (P <= 448: no clamp); row sum of the
+            // ---- P = 448 exp2(s * scale - m) -> E4M3 (P <= 448: no clamp); row sum of the
             // unrounded P in a fixed order ----
             float bsum = 0.f;
 #pragma unroll
             for (int u = 0; u < NSUB; u++) {
                 float pr[4];
 #pragma unroll
-                for (int j = 0; j < 4; j++) pr[j] = ANCHOR * exp2f(acc[u][j] - m_use);
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
-                w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
-                *reinterpret_cast<uint32_t*>(smem + L::OFF_P + qt * PTILE + n16 * PPITCH +
-                                             16 * u + 4 * grp) = (uint32_t)w;
+                for (int j = 0; j < 4; j++)
+                    pr[j] = ANCHOR * __builtin_amdgcn_exp2f(fmaf(acc[u][j], row_scale, -m_use));
+                int wp = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+                pk[u] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], wp, true);
                 bsum = bsum + (((pr[0] + pr[1]) + pr[2]) + pr[3]);
             }
             bsum = wave_sum16(bsum);
             l_run = l_run * alpha + bsum;
             m_run = m_new;
+        }
+        lds_sync();   // B3: the PV waves have taken P of block i - 1 into registers
+        if (work) {
+#pragma unroll
+            for (int u = 0; u < NSUB; u++)
+                *reinterpret_cast<uint32_t*>(smem + L::OFF_P + qt * PTILE + n16 * PPITCH + 16 * u +
+                                             4 * grp) = pk[u];
             if (grp == 0)
                 xalpha[qt * 16 + n16] = alpha;
         }
-        lds_sync();   // P and the rescale factors of every tile are published
-
-        // ---- PV: O^T[128 columns of this wave] += V^T P^T for every tile ----
-        v8i pb[T];
-#pragma unroll
-        for (int t = 0; t < T; t++) {
-            const float a = xalpha[t * 16 + n16];
-            if (!__all(a == 1.f)) {
-#pragma unroll
-                for (int c = 0; c < 8; c++) O[t][c] *= a;
-            }
-            const int off = L::OFF_P + t * PTILE + n16 * PPITCH + 32 * grp;
-            pb[t] = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
-        }
-        auto load_vt = [&](int c) {
-            v2i tr[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int off = slot * SLOT + (r >> 1) * SUBB + voff(c, r & 1);
-                tr[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(smem + off));
-            }
-            return v8i{tr[0].x, tr[0].y, tr[1].x, tr[1].y, tr[2].x, tr[2].y, tr[3].x, tr[3].y};
-        };
-        v8i va[2];
-        va[0] = load_vt(0);
-#pragma unroll
-        for (int c = 0; c < 8; c++) {
-            if (c + 1 < 8)
-                va[(c + 1) & 1] = load_vt(c + 1);
-#pragma unroll
-            for (int t = 0; t < T; t++) O[t][c] = mfma(va[c & 1], pb[t], O[t][c]);
-        }
     }
 
-    // ---- per-row (m, l) to LDS for the column owners ----
+    // ---- epilogue: (m, l) to the column owners, LSE ----
     float* fm = reinterpret_cast<float*>(smem + L::OFF_FM);
     float* fl = reinterpret_cast<float*>(smem + L::OFF_FL);
-    if (qk_wave && grp == 0) {
+    if (active && grp == 0) {
         fm[qt * 16 + n16] = m_run;
         fl[qt * 16 + n16] = l_run;
     }
-    __syncthreads();
+    __syncthreads();   // E1
+    const int64_t orow = w.row_base + 16 * tile + n16;
+    if (p.S == 1) {
+        if (active && grp == 0)
+            p.lse[orow] = (l_run > 0.f) ? (m_run - LOG2_ANCHOR + log2f(l_run)) * LN2 : neg_inf;
+        return;
+    }
+    if (active && grp == 0) {
+        p.ws_ml[(orow * p.S + w.s) * 2 + 0] = m_run;
+        p.ws_ml[(orow * p.S + w.s) * 2 + 1] = l_run;
+    }
+}
 
+// ---- PV waves: the gather, and O^T += V^T P^T for 128 latent columns of every tile ----
+template <int T, bool DENSE>
+__device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Work& w, int pw,
+                                        int lane, v4f (&O)[T][8])
+{
+    using L = Smem<T>;
+    const int n16 = lane & 15;
+    const int grp = lane >> 4;
+
+    // Gather: this wave moves keys 32 pw .. 32 pw + 31 (subtiles 2 pw, 2 pw + 1) of every block.
+    // Per block: the raw indices (page ids or row ids) arrive in an LDS slot by DMA one block
+    // earlier; lanes 0..31 turn them into row pointers (the zero row when absent) and a presence
+    // word; the wave then issues its 18 row DMAs.
+    int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
+    uint64_t* rpt = reinterpret_cast<uint64_t*>(smem + L::OFF_RP);
+    auto dma_indices = [&](int blk) {  // raw indices of block blk -> idx slot blk % 2
+        const int kk = 32 * pw + lane;
+        const int64_t left = w.mine - (int64_t)blk * BLK;
+        if (lane < 32 && kk < left)
+            dma4(index_ptr<DENSE>(p, w.g, w.first + (int64_t)blk * BLK + kk),
+                 lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * pw * 4));
+    };
+    auto prepare_rows = [&](int blk, int32_t idx) {  // idx: raw index of key 32 pw + lane
+        const int kk = 32 * pw + lane;
+        const int64_t left = w.mine - (int64_t)blk * BLK;
+        const bool in = lane < 32 && kk < left;
+        const int64_t row = key_row<DENSE>(p, w.first + (int64_t)blk * BLK + kk, in, idx);
+        const uint64_t ptr = row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW)
+                                      : (uint64_t)(uintptr_t)g_zero_row;
+        if (lane < 32)
+            rpt[(blk & 1) * BLK + kk] = ptr;
+        const uint32_t word = (uint32_t)__ballot(row >= 0);   // lanes 0..31: keys 32 pw + lane
+        if (lane == 0)
+            *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 1) * 16 + 4 * pw) = word;
+    };
+    auto issue_block = [&](int blk) {   // this wave's 18 row DMAs of block blk
+#pragma unroll
+        for (int i = 0; i < 18; i++) {
+            const int sub = 2 * pw + i / 9;
+            const uint8_t* src = dma_src(rpt + (blk & 1) * BLK + 16 * sub, i % 9, lane);
+            dma16(src, lds_addr(smem + (blk & 1) * SLOT + sub * SUBB + 1024 * (i % 9)));
+        }
+    };
+    if (w.nblk > 0) {
+        int32_t idx0 = -1;
+        if (lane < 32 && 32 * pw + lane < w.mine)
+            idx0 = *index_ptr<DENSE>(p, w.g, w.first + 32 * pw + lane);
+        prepare_rows(0, idx0);
+        issue_block(0);
+        if (w.nblk > 1)
+            dma_indices(1);
+    }
+
+    // this lane's LDS byte offset within a subtile of its transposed V read (column chunk
+    // 8 pw + c, key half rb)
+    auto voff = [&](int c, int rb) {
+        const int kk = 8 * rb + (n16 >> 1), cc = 8 * pw + c;
+        return 2 * grp * SUBB + 16 * (32 * kk + (cc ^ kk)) + 8 * (n16 & 1);
+    };
+    auto load_vt = [&](int slot, int c) {
+        v2i tr[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int off = slot * SLOT + (r >> 1) * SUBB + voff(c, r & 1);
+            tr[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(smem + off));
+        }
+        return v8i{tr[0].x, tr[0].y, tr[1].x, tr[1].y, tr[2].x, tr[2].y, tr[3].x, tr[3].y};
+    };
+    const float* xalpha = reinterpret_cast<const float*>(smem + L::OFF_ALPHA);
+    v8i vt[8];   // V^T of the block the next iteration multiplies (copied while its slot is valid)
+
+    // iteration i: gather of block i + 1; PV of block i - 1; V^T of block i into registers
+    for (int i = 0; i <= w.nblk; i++) {
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's DMAs of block i (and indices)
+        lds_sync();   // B1: block i landed; P of block i - 1 published
+        if (i + 1 < w.nblk) {
+            prepare_rows(i + 1, lane < 32 ? idx_lds[((i + 1) & 1) * BLK + 32 * pw + lane] : -1);
+            issue_block(i + 1);
+        }
+        if (i + 2 < w.nblk)
+            dma_indices(i + 2);
+        if (i >= 1) {   // rescale O for block i - 1 while the QK waves issue their MFMAs
+#pragma unroll
+            for (int t = 0; t < T; t++) {
+                const float a = xalpha[t * 16 + n16];
+                if (!__all(a == 1.f)) {
+#pragma unroll
+                    for (int c = 0; c < 8; c++) O[t][c] *= a;
+                }
+            }
+        }
+        lds_sync();   // B2: the QK waves have issued their MFMAs of block i
+        if (i >= 1) {
+#pragma unroll
+            for (int t = 0; t < T; t++) {
+                const int off = L::OFF_P + t * PTILE + n16 * PPITCH + 32 * grp;
+                const v8i pb = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
+#pragma unroll
+                for (int c = 0; c < 8; c++) O[t][c] = mfma(vt[c], pb, O[t][c]);
+            }
+        }
+        if (i < w.nblk) {
+#pragma unroll
+            for (int c = 0; c < 8; c++) vt[c] = load_vt(i & 1, c);
+        }
+        lds_sync();   // B3: P of block i - 1 and V^T of block i are in registers
+    }
+
+    // ---- epilogue ----
+    __syncthreads();   // E1: (m, l) of every row in LDS
+    const float* fl = reinterpret_cast<const float*>(smem + L::OFF_FL);
     if (p.S == 1) {
         // o = BF16(O / l * k_scale); the single-split merge (weight exp2(0) = 1) is this exactly
 #pragma unroll
         for (int t = 0; t < T; t++) {
             const float lt = fl[t * 16 + n16];
-            const int64_t orow = row_base + 16 * (ts * T + t) + n16;
+            const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
 #pragma unroll
             for (int c = 0; c < 8; c++) {
-                const int col = 128 * wave + 16 * c + 4 * grp;
+                const int col = 128 * pw + 16 * c + 4 * grp;
                 uint32_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
                 if (lt > 0.f) {
                     b0 = f32_to_bf16_rne(O[t][c][0] / lt * p.k_scale);
@@ -608,53 +641,32 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
                     b2 = f32_to_bf16_rne(O[t][c][2] / lt * p.k_scale);
                     b3 = f32_to_bf16_rne(O[t][c][3] / lt * p.k_scale);
                 }
-                v2i w = v2i{(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
-                *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) = w;
+                v2i wv = v2i{(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
+                *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) = wv;
             }
         }
-        if (qk_wave && grp == 0) {
-            const int64_t orow = row_base + 16 * tile + n16;
-            p.lse[orow] = (l_run > 0.f) ? (m_run - LOG2_ANCHOR + log2f(l_run)) * LN2 : neg_inf;
-        }
         return;
     }
-
-    // ---- S > 1: emit this split's FP32 partial, then the last arriver merges ----
 #pragma unroll
     for (int t = 0; t < T; t++) {
-        const int64_t orow = row_base + 16 * (ts * T + t) + n16;
+        const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
 #pragma unroll
         for (int c = 0; c < 8; c++) {
-            const int col = 128 * wave + 16 * c + 4 * grp;
-            *reinterpret_cast<v4f*>(p.ws_o + (orow * p.S + s) * LATENT + col) = O[t][c];
+            const int col = 128 * pw + 16 * c + 4 * grp;
+            *reinterpret_cast<v4f*>(p.ws_o + (orow * p.S + w.s) * LATENT + col) = O[t][c];
         }
     }
-    if (qk_wave && grp == 0) {
-        const int64_t orow = row_base + 16 * tile + n16;
-        p.ws_ml[(orow * p.S + s) * 2 + 0] = m_run;
-        p.ws_ml[(orow * p.S + s) * 2 + 1] = l_run;
-    }
-    // Every thread's partial stores have completed (vmcnt(0)) before the barrier; one thread then
-    // releases them at agent scope and counts this split in.
-    __builtin_amdgcn_s_waitcnt(0xF70);
-    __syncthreads();
-    int* misc = reinterpret_cast<int*>(smem + L::OFF_MISC);
-    uint32_t* cnt = p.ws_cnt + (int64_t)g * p.tilesets + ts;
-    if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        misc[0] = (old == (uint32_t)(p.S - 1)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (misc[0] == 0)
-        return;
+}
 
-    // merge: T*16 rows x 32 column chunks of 16; thread -> (row, chunk) items
+// The last arriving split of a (group, tile set) merges the FP32 partials in split order.
+template <int T>
+__device__ void merge_splits(const Params& p, const Work& w, int tid)
+{
+    const float neg_inf = -INFINITY;
     for (int item = tid; item < T * 16 * 32; item += THREADS) {
         const int r = item >> 5;
         const int c0 = (item & 31) * 16;
-        const int64_t orow = row_base + 16 * ts * T + r;
+        const int64_t orow = w.row_base + 16 * w.ts * T + r;
         const float* ml = p.ws_ml + orow * p.S * 2;
         float top = neg_inf;
         for (int q = 0; q < p.S; q++) top = fmaxf(top, ml[2 * q]);
@@ -667,14 +679,14 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
                 const float mq = ml[2 * q];
                 if (mq == neg_inf)
                     continue;
-                const float w = exp2f(mq - top);
-                total = total + w * ml[2 * q + 1];
+                const float wq = exp2f(mq - top);
+                total = total + wq * ml[2 * q + 1];
                 const v4f* src = reinterpret_cast<const v4f*>(p.ws_o + (orow * p.S + q) * LATENT + c0);
 #pragma unroll
                 for (int v = 0; v < 4; v++) {
                     const v4f x4 = src[v];
 #pragma unroll
-                    for (int e = 0; e < 4; e++) acc[4 * v + e] = acc[4 * v + e] + w * x4[e];
+                    for (int e = 0; e < 4; e++) acc[4 * v + e] = acc[4 * v + e] + wq * x4[e];
                 }
             }
         }
@@ -690,6 +702,49 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
         if ((item & 31) == 0)
             p.lse[orow] = total > 0.f ? (top - LOG2_ANCHOR + log2f(total)) * LN2 : neg_inf;
     }
+}
+
+template <int T, bool DENSE>
+__global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
+{
+    using L = Smem<T>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+    Work w;
+    if (!decode_work<DENSE>(p, w))
+        return;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    // waves 0..3: QK (tile = wave); waves 4..7: gather + PV (columns 128 (wave - 4) ..); wave i runs
+    // on SIMD i % 4, so each SIMD pairs one QK wave with one PV wave
+    if (wave < 4) {
+        qk_role<T, DENSE>(p, smem, w, wave, lane);
+    } else {
+        v4f O[T][8];
+#pragma unroll
+        for (int t = 0; t < T; t++)
+#pragma unroll
+            for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+        pv_role<T, DENSE>(p, smem, w, wave - 4, lane, O);
+    }
+    if (p.S == 1)
+        return;
+    // S > 1: every thread's partial stores completed (vmcnt(0)) before the barrier; one thread then
+    // releases them at agent scope and counts this split in; the last arriver merges.
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    __syncthreads();   // E2
+    int* misc = reinterpret_cast<int*>(smem + L::OFF_MISC);
+    uint32_t* cnt = p.ws_cnt + (int64_t)w.g * p.tilesets + w.ts;
+    if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        misc[0] = (old == (uint32_t)(p.S - 1)) ? 1 : 0;
+    }
+    __syncthreads();   // E3
+    if (misc[0] == 0)
+        return;
+    merge_splits<T>(p, w, tid);
     if (tid == 0)
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
