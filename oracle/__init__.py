@@ -51,10 +51,10 @@ def _load():
         lib.mo_bf16_decode.argtypes = [ctypes.c_uint16]
         lib.mo_bf16_decode.restype = ctypes.c_double
         lib.mo_dense.argtypes = [P, i32, i32, i32, P, i64, i32, f32, P, i32, P, f32, i32, i32, i32,
-                                 P, i64, i32, P, P]
+                                 P, P, P, i64, i32, P, P]
         lib.mo_dense.restype = i32
         lib.mo_sparse.argtypes = [P, i32, i32, i32, P, i64, f32, P, i32, P, f32, i32, i32, i32,
-                                  P, i64, i32, P, P]
+                                  P, P, P, i64, i32, P, P]
         lib.mo_sparse.restype = i32
         _lib = lib
     return _lib
@@ -98,10 +98,24 @@ def _sel(sel):
     return None if sel is None else _as(sel, np.int64)
 
 
+def _cuts(cuts, groups):
+    """Explicit split starts per key group (a sequence of ``groups`` sequences) -> CSR arrays."""
+    if cuts is None:
+        return None, None
+    assert len(cuts) == groups
+    ptr = np.zeros(groups + 1, np.int64)
+    ptr[1:] = np.cumsum([len(c) for c in cuts])
+    start = np.concatenate([np.asarray(c, np.int64) for c in cuts]) if groups else np.zeros(0, np.int64)
+    return ptr, np.ascontiguousarray(start, np.int64)
+
+
 def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=METHOD, splits=1,
-          chunk=128, sel=None, threads=None):
+          chunk=128, cuts=None, sel=None, threads=None):
     """Paged dense decode. ``q_bits`` uint16 bf16 bits [B,Q,H,576]; ``kv`` uint8 [num_rows,576];
     ``block_table`` int32 [B,max_pages]; ``seq_lens`` int32 [B].
+
+    The split plan: ``splits`` uniform splits per request (per = ceil(n / splits)), or ``cuts``, one
+    sequence of split start keys per request (first 0, non-decreasing, each <= the request's keys).
 
     Returns ``(o, lse)`` in float64: ``o`` [B,Q,H,512] and ``lse`` [B,Q,H], or [n,512] / [n] for a
     ``sel`` list of flat rows ``(b*Q+i)*H+h``."""
@@ -114,9 +128,10 @@ def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=
     assert table.shape[0] == B and seq.shape == (B,)
     sel = _sel(sel)
     o, lse = _outputs(B, Q, H, sel)
+    cp, cs = _cuts(cuts, B)
     rc = _load().mo_dense(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], int(page_size),
                           float(k_scale), _ptr(table), table.shape[1], _ptr(seq), float(scale),
-                          int(mode), int(splits), int(chunk), _ptr(sel),
+                          int(mode), int(splits), int(chunk), _ptr(cp), _ptr(cs), _ptr(sel),
                           0 if sel is None else len(sel), _threads(threads), _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle: bad arguments")
@@ -125,9 +140,10 @@ def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=
     return o, lse
 
 
-def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, chunk=128, sel=None,
-           threads=None):
-    """Top-k sparse decode. ``rows`` int32 [B,Q,K] flat cache rows; ``valid`` int32 [B,Q]."""
+def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, chunk=128, cuts=None,
+           sel=None, threads=None):
+    """Top-k sparse decode. ``rows`` int32 [B,Q,K] flat cache rows; ``valid`` int32 [B,Q]. The
+    split plan as for ``dense``, with ``cuts`` given per (b, i) row list, in order b*Q+i."""
     q_bits = _as(q_bits, np.uint16)
     B, Q, H, D = q_bits.shape
     assert D == 576
@@ -137,9 +153,11 @@ def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, ch
     assert rows.shape[:2] == (B, Q) and valid.shape == (B, Q)
     sel = _sel(sel)
     o, lse = _outputs(B, Q, H, sel)
+    cp, cs = _cuts(cuts, B * Q)
     rc = _load().mo_sparse(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], float(k_scale),
                            _ptr(rows), rows.shape[2], _ptr(valid), float(scale), int(mode),
-                           int(splits), int(chunk), _ptr(sel), 0 if sel is None else len(sel),
+                           int(splits), int(chunk), _ptr(cp), _ptr(cs), _ptr(sel),
+                           0 if sel is None else len(sel),
                            _threads(threads), _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle: bad arguments")

@@ -16,7 +16,9 @@
  *             - module docstring, last paragraph: rows with no key write zeros and LSE = -inf.
  *             - SparseDcpDecode.kernel: a row's count is clamped to [0, width]; split s of SPLIT takes
  *               keys [s*per, min(n, (s+1)*per)) with per = ceil(n / SPLIT), in chunks of CHUNK keys.
- *             - SparseDcpDecode.merge: the fixed-order FP32 combine of the splits.
+ *             - SparseDcpDecode.merge: the fixed-order FP32 combine of the splits. Its identity
+ *               (weights exp2(m_s - top)) holds for any division of the keys into consecutive
+ *               splits, so a plan may also be given as explicit split boundaries per key group.
  *   [AMD]     vllm.models.kimi_k3.amd.specialized_decode.mono.attention.mla_attn
  *             - module docstring: position i of a request's qlen query rows sees keys up to
  *               seq_len - qlen + i; a split with no visible key leaves LSE = -inf and o = 0.
@@ -129,12 +131,15 @@ static double dot_qk(const double* qd, const uint8_t* krow)
 /*
  * One query row against its group's ordered key list.
  *   keyrow[j]  cache row of key j (j < n_group), or -1 when the key is absent;
- *   n_visible  keys [0, n_visible) may be seen by this row (causal bound), n_visible <= n_group.
+ *   n_visible  keys [0, n_visible) may be seen by this row (causal bound), n_visible <= n_group;
+ *   starts     NULL: plan->splits splits of per = ceil(n_group / splits) keys each; else nstart
+ *              split start keys (starts[0] = 0, non-decreasing, <= n_group), split s ending where
+ *              split s + 1 starts (the last at n_group).
  * Writes o[512] and *lse.
  */
 static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow, int n_group,
-                     int n_visible, double scale, double k_scale, const mo_plan* plan, double* o,
-                     double* lse)
+                     int n_visible, double scale, double k_scale, const mo_plan* plan,
+                     const int64_t* starts, int nstart, double* o, double* lse)
 {
     double qd[MO_ROW];
     for (int c = 0; c < MO_ROW; c++)
@@ -184,7 +189,7 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
     /* The split / chunked online softmax (MO_ONLINE, MO_METHOD), logits in log2 units. */
     const double log2e = 1.0 / log(2.0);
     const double anchor = 448.0;
-    const int S = plan->splits;
+    const int S = starts ? nstart : plan->splits;
     double* m_s = (double*)malloc(sizeof(double) * S);
     double* l_s = (double*)malloc(sizeof(double) * S);
     double* O_s = (double*)calloc((size_t)S * MO_LATENT, sizeof(double));
@@ -194,8 +199,14 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
     int n = n_group;
     int per = (n + S - 1) / S;
     for (int s = 0; s < S; s++) {
-        int first = s * per < n ? s * per : n;
-        int mine = n - first < per ? n - first : per;
+        int first, mine;
+        if (starts) {
+            first = (int)starts[s];
+            mine = (int)((s + 1 < S ? starts[s + 1] : n) - first);
+        } else {
+            first = s * per < n ? s * per : n;
+            mine = n - first < per ? n - first : per;
+        }
         double m = -INFINITY, l = 0.0;
         double* O = O_s + (size_t)s * MO_LATENT;
         for (int base = first; base < first + mine; base += plan->chunk) {
@@ -286,6 +297,8 @@ typedef struct {
     const int32_t* valid;
     double scale, k_scale;
     mo_plan plan;
+    const int64_t* cut_ptr;   /* [groups + 1] or NULL; group g's split starts are */
+    const int64_t* cut_start; /* cut_start[cut_ptr[g] .. cut_ptr[g + 1]) */
     const int64_t* sel;
     int64_t n_items;
     double* o;
@@ -326,8 +339,11 @@ static void eval_item(const mo_job* jb, int64_t item)
             keyrow[j] = (r >= 0 && r < jb->num_rows) ? r : -1;
         }
     }
-    row_eval(q, jb->kv, keyrow, n_group, n_visible, jb->scale, jb->k_scale, &jb->plan,
-             jb->o + (size_t)item * MO_LATENT, jb->lse + item);
+    const int64_t g = jb->dense ? b : (int64_t)b * jb->Q + i;
+    const int64_t* starts = jb->cut_ptr ? jb->cut_start + jb->cut_ptr[g] : NULL;
+    const int nstart = jb->cut_ptr ? (int)(jb->cut_ptr[g + 1] - jb->cut_ptr[g]) : 0;
+    row_eval(q, jb->kv, keyrow, n_group, n_visible, jb->scale, jb->k_scale, &jb->plan, starts,
+             nstart, jb->o + (size_t)item * MO_LATENT, jb->lse + item);
     free(keyrow);
 }
 
@@ -339,10 +355,35 @@ static void* worker(void* arg)
     return NULL;
 }
 
+/* Explicit split boundaries must cover each group's keys: at least one split, the first at key 0,
+ * non-decreasing starts, none past the group's key count. */
+static int check_cuts(const mo_job* jb)
+{
+    if (!jb->cut_ptr)
+        return 0;
+    const int64_t groups = jb->dense ? jb->B : (int64_t)jb->B * jb->Q;
+    for (int64_t g = 0; g < groups; g++) {
+        int n;
+        if (jb->dense)
+            n = clampi(jb->seq_lens[g], 0, (long long)jb->max_pages * jb->page_size);
+        else
+            n = clampi(jb->valid[g], 0, jb->K);
+        const int64_t a = jb->cut_ptr[g], e = jb->cut_ptr[g + 1];
+        if (e <= a || jb->cut_start[a] != 0)
+            return -1;
+        for (int64_t k = a; k < e; k++)
+            if (jb->cut_start[k] > n || (k > a && jb->cut_start[k] < jb->cut_start[k - 1]))
+                return -1;
+    }
+    return 0;
+}
+
 static int run_job(mo_job* base)
 {
     int nt = base->nthreads < 1 ? 1 : base->nthreads;
     if (base->plan.mode != MO_EXACT && (base->plan.splits < 1 || base->plan.chunk < 1))
+        return -1;
+    if (check_cuts(base) != 0)
         return -1;
     pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nt);
     mo_job* jobs = (mo_job*)malloc(sizeof(mo_job) * nt);
@@ -362,12 +403,15 @@ static int run_job(mo_job* base)
 /*
  * Dense paged decode. q [B,Q,H,576] bf16 bits; kv [num_rows,576] E4M3 bytes; table [B,max_pages];
  * seq_lens [B]. sel: optional list of flat rows (b*Q+i)*H+h (n_sel of them); NULL means every row.
+ * cut_ptr / cut_start: optional explicit split starts per key group (dense: group b; sparse: group
+ * b*Q+i), which replace the uniform split rule when given.
  * o [items,512] and lse [items] in FP64.
  */
 int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t num_rows,
              int page_size, float k_scale, const int32_t* table, int max_pages,
              const int32_t* seq_lens, float scale, int mode, int splits, int chunk,
-             const int64_t* sel, int64_t n_sel, int threads, double* o, double* lse)
+             const int64_t* cut_ptr, const int64_t* cut_start, const int64_t* sel, int64_t n_sel,
+             int threads, double* o, double* lse)
 {
     if (page_size < 1)
         return -1;
@@ -388,6 +432,8 @@ int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t 
     jb.plan.mode = mode;
     jb.plan.splits = splits;
     jb.plan.chunk = chunk;
+    jb.cut_ptr = cut_ptr;
+    jb.cut_start = cut_start;
     jb.sel = sel;
     jb.n_items = sel ? n_sel : (int64_t)B * Q * H;
     jb.o = o;
@@ -401,8 +447,8 @@ int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t 
  */
 int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t num_rows,
               float k_scale, const int32_t* rows, int K, const int32_t* valid, float scale,
-              int mode, int splits, int chunk, const int64_t* sel, int64_t n_sel, int threads,
-              double* o, double* lse)
+              int mode, int splits, int chunk, const int64_t* cut_ptr, const int64_t* cut_start,
+              const int64_t* sel, int64_t n_sel, int threads, double* o, double* lse)
 {
     mo_job jb = {0};
     jb.dense = 0;
@@ -420,6 +466,8 @@ int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t
     jb.plan.mode = mode;
     jb.plan.splits = splits;
     jb.plan.chunk = chunk;
+    jb.cut_ptr = cut_ptr;
+    jb.cut_start = cut_start;
     jb.sel = sel;
     jb.n_items = sel ? n_sel : (int64_t)B * Q * H;
     jb.o = o;

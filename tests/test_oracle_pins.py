@@ -155,6 +155,53 @@ def test_method_lse_is_the_definition_and_o_within_e4m3_bound(splits, chunk):
         assert np.max(np.abs(o2 - o0)) > 1e-6
 
 
+def _groups_keys(x):
+    """Key count of each key group (dense: request b; sparse: list (b, i))."""
+    if x.kind == "dense":
+        cap = x.block_table.shape[1] * x.page_size
+        return np.clip(x.seq_lens.astype(np.int64), 0, cap)
+    return np.clip(x.valid.reshape(-1).astype(np.int64), 0, x.rows.shape[2])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_online_merge_equals_the_definition_for_any_split_boundaries(seed):
+    """The merge identity does not depend on where the splits fall: random consecutive splits per
+    group (empty ones included, boundaries off the chunk grid) reproduce the definition."""
+    rng = np.random.default_rng(seed)
+    for name, x in _cases():
+        cuts = []
+        for n in _groups_keys(x):
+            k = int(rng.integers(0, 5))
+            inner = np.sort(rng.integers(0, n + 1, size=k)) if n > 0 else np.zeros(k, np.int64)
+            cuts.append(np.concatenate([[0], inner]))
+        o0, l0 = _run(name, x, mode=oracle.EXACT)
+        o1, l1 = _run(name, x, mode=oracle.ONLINE, cuts=cuts, chunk=16)
+        np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12, err_msg=name)
+        np.testing.assert_array_equal(np.isneginf(l1), np.isneginf(l0))
+        fin = np.isfinite(l0)
+        np.testing.assert_allclose(l1[fin], l0[fin], rtol=0, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_cuts_at_the_uniform_boundaries_equal_the_uniform_plan(splits):
+    for name, x in _cases():
+        cuts = []
+        for n in _groups_keys(x):
+            per = -(-int(n) // splits)
+            cuts.append([min(s * per, int(n)) for s in range(splits)])
+        a = _run(name, x, mode=oracle.METHOD, splits=splits, chunk=32)
+        b = _run(name, x, mode=oracle.METHOD, cuts=cuts, chunk=32)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_cuts_that_do_not_cover_the_keys_are_rejected():
+    x = wl.sparse_case(1, 2, 16, 40, [[40, 10]], 100, seed=5)
+    for bad in ([[0], [5]], [[0, 30, 20], [0]], [[0, 41], [0]], [[], [0]]):
+        with pytest.raises(ValueError):
+            _run("sparse", x, mode=oracle.METHOD, cuts=bad)
+
+
 # ---- library softmax on tiny inputs -----------------------------------------------------------
 
 @pytest.mark.parametrize("seed", range(6))
