@@ -9,6 +9,10 @@ What it computes, and the passages of the vLLM API pages it follows, is stated i
 * ``EXACT``  -- the textbook softmax definition (LSE = ln sum exp, o = softmax-weighted V).
 * ``ONLINE`` -- the pages' split / chunked base-2 online softmax and FP32-style merge, P unrounded.
 * ``METHOD`` -- as ``ONLINE`` with P rounded to E4M3 at the 448 anchor of the running maximum.
+
+With ``allowance=True`` the front ends also return, per output element, how far o may move when a
+P that an FP32 implementation can only place to within 2^-13 (relative) of an E4M3 rounding
+midpoint is rounded the other way (METHOD mode; zeros otherwise).
 """
 from __future__ import annotations
 
@@ -51,10 +55,10 @@ def _load():
         lib.mo_bf16_decode.argtypes = [ctypes.c_uint16]
         lib.mo_bf16_decode.restype = ctypes.c_double
         lib.mo_dense.argtypes = [P, i32, i32, i32, P, i64, i32, f32, P, i32, P, f32, i32, i32, i32,
-                                 P, P, P, i64, i32, P, P]
+                                 P, P, P, i64, i32, P, P, P]
         lib.mo_dense.restype = i32
         lib.mo_sparse.argtypes = [P, i32, i32, i32, P, i64, f32, P, i32, P, f32, i32, i32, i32,
-                                  P, P, P, i64, i32, P, P]
+                                  P, P, P, i64, i32, P, P, P]
         lib.mo_sparse.restype = i32
         _lib = lib
     return _lib
@@ -94,6 +98,13 @@ def _outputs(B, Q, H, sel):
     return np.zeros((n, 512), np.float64), np.zeros((n,), np.float64)
 
 
+def _shape(B, Q, H, sel, o, lse, amb):
+    if sel is None:
+        o, lse = o.reshape(B, Q, H, 512), lse.reshape(B, Q, H)
+        amb = None if amb is None else amb.reshape(B, Q, H, 512)
+    return (o, lse) if amb is None else (o, lse, amb)
+
+
 def _sel(sel):
     return None if sel is None else _as(sel, np.int64)
 
@@ -110,7 +121,7 @@ def _cuts(cuts, groups):
 
 
 def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=METHOD, splits=1,
-          chunk=128, cuts=None, sel=None, threads=None):
+          chunk=128, cuts=None, sel=None, threads=None, allowance=False):
     """Paged dense decode. ``q_bits`` uint16 bf16 bits [B,Q,H,576]; ``kv`` uint8 [num_rows,576];
     ``block_table`` int32 [B,max_pages]; ``seq_lens`` int32 [B].
 
@@ -129,19 +140,19 @@ def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=
     sel = _sel(sel)
     o, lse = _outputs(B, Q, H, sel)
     cp, cs = _cuts(cuts, B)
+    amb = np.zeros_like(o) if allowance else None
     rc = _load().mo_dense(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], int(page_size),
                           float(k_scale), _ptr(table), table.shape[1], _ptr(seq), float(scale),
                           int(mode), int(splits), int(chunk), _ptr(cp), _ptr(cs), _ptr(sel),
-                          0 if sel is None else len(sel), _threads(threads), _ptr(o), _ptr(lse))
+                          0 if sel is None else len(sel), _threads(threads), _ptr(o), _ptr(lse),
+                          _ptr(amb))
     if rc != 0:
         raise ValueError("oracle: bad arguments")
-    if sel is None:
-        return o.reshape(B, Q, H, 512), lse.reshape(B, Q, H)
-    return o, lse
+    return _shape(B, Q, H, sel, o, lse, amb)
 
 
 def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, chunk=128, cuts=None,
-           sel=None, threads=None):
+           sel=None, threads=None, allowance=False):
     """Top-k sparse decode. ``rows`` int32 [B,Q,K] flat cache rows; ``valid`` int32 [B,Q]. The
     split plan as for ``dense``, with ``cuts`` given per (b, i) row list, in order b*Q+i."""
     q_bits = _as(q_bits, np.uint16)
@@ -154,13 +165,12 @@ def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, ch
     sel = _sel(sel)
     o, lse = _outputs(B, Q, H, sel)
     cp, cs = _cuts(cuts, B * Q)
+    amb = np.zeros_like(o) if allowance else None
     rc = _load().mo_sparse(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], float(k_scale),
                            _ptr(rows), rows.shape[2], _ptr(valid), float(scale), int(mode),
                            int(splits), int(chunk), _ptr(cp), _ptr(cs), _ptr(sel),
                            0 if sel is None else len(sel),
-                           _threads(threads), _ptr(o), _ptr(lse))
+                           _threads(threads), _ptr(o), _ptr(lse), _ptr(amb))
     if rc != 0:
         raise ValueError("oracle: bad arguments")
-    if sel is None:
-        return o.reshape(B, Q, H, 512), lse.reshape(B, Q, H)
-    return o, lse
+    return _shape(B, Q, H, sel, o, lse, amb)

@@ -31,6 +31,11 @@
  *                 up to FP64 rounding for every split plan: the split-merge identity).
  *   MO_METHOD     MO_ONLINE with each P rounded to E4M3 before it multiplies V. The rounding decision
  *                 is taken on P rounded to FP32, the precision the pages compute P in.
+ *                 Optionally also a per-element allowance: an implementation that forms the logits
+ *                 in FP32 gets P only to a relative accuracy of about MO_P_REL_ERR, and where a P
+ *                 lies that close to an E4M3 rounding midpoint either rounding is a correct result.
+ *                 The allowance is what such keys can move o by: the E4M3 step between the two
+ *                 roundings times |V|, carried through the same rescaling and merge as O.
  *
  * Readings of the pages this oracle takes (each also listed in the design notes):
  *   - the causal bound is inclusive: row i sees n_i = seq_len - qlen + i + 1 keys (clamped to
@@ -113,6 +118,21 @@ double mo_bf16_decode(uint16_t h)
 
 /* ---- one query row ---------------------------------------------------------------------------- */
 
+/* Relative accuracy of P assumed for an FP32 implementation (2^-13: FP32 dot products of 576 terms
+ * and an FP32 exp2 stay well inside it for logits of the sizes seen here). */
+#define MO_P_REL_ERR (1.0 / 8192.0)
+
+/* The largest change of the E4M3 value of P (rounded to FP32) when P moves by up to MO_P_REL_ERR
+ * relative: 0 unless a rounding midpoint lies within that distance. */
+static double rounding_ambiguity(double p)
+{
+    const double c0 = mo_e4m3_decode(mo_e4m3_encode((double)(float)p));
+    const double lo = mo_e4m3_decode(mo_e4m3_encode((double)(float)(p * (1.0 - MO_P_REL_ERR))));
+    const double hi = mo_e4m3_decode(mo_e4m3_encode((double)(float)(p * (1.0 + MO_P_REL_ERR))));
+    const double a = fabs(lo - c0), b = fabs(hi - c0);
+    return a > b ? a : b;
+}
+
 typedef struct {
     int mode;
     int splits; /* S >= 1 */
@@ -139,8 +159,11 @@ static double dot_qk(const double* qd, const uint8_t* krow)
  */
 static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow, int n_group,
                      int n_visible, double scale, double k_scale, const mo_plan* plan,
-                     const int64_t* starts, int nstart, double* o, double* lse)
+                     const int64_t* starts, int nstart, double* o, double* lse, double* amb)
 {
+    if (amb)
+        for (int c = 0; c < MO_LATENT; c++)
+            amb[c] = 0.0;
     double qd[MO_ROW];
     for (int c = 0; c < MO_ROW; c++)
         qd[c] = mo_bf16_decode(q[c]);
@@ -193,6 +216,7 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
     double* m_s = (double*)malloc(sizeof(double) * S);
     double* l_s = (double*)malloc(sizeof(double) * S);
     double* O_s = (double*)calloc((size_t)S * MO_LATENT, sizeof(double));
+    double* A_s = (double*)calloc((size_t)S * MO_LATENT, sizeof(double)); /* allowance */
     double* x2 = (double*)malloc(sizeof(double) * (plan->chunk > 0 ? plan->chunk : 1));
     double* p = (double*)malloc(sizeof(double) * (plan->chunk > 0 ? plan->chunk : 1));
 
@@ -209,6 +233,7 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
         }
         double m = -INFINITY, l = 0.0;
         double* O = O_s + (size_t)s * MO_LATENT;
+        double* A = A_s + (size_t)s * MO_LATENT;
         for (int base = first; base < first + mine; base += plan->chunk) {
             int count = first + mine - base < plan->chunk ? first + mine - base : plan->chunk;
             /* logits of the chunk; -inf for keys the row may not see or that are absent */
@@ -236,8 +261,10 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
                 total += p[t];
             }
             l = l * alpha + total;
-            for (int c = 0; c < MO_LATENT; c++)
+            for (int c = 0; c < MO_LATENT; c++) {
                 O[c] *= alpha;
+                A[c] *= alpha;
+            }
             for (int t = 0; t < count; t++) {
                 if (p[t] == 0.0)
                     continue;
@@ -247,6 +274,10 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
                 const uint8_t* vr = kv + (size_t)keyrow[base + t] * MO_ROW;
                 for (int c = 0; c < MO_LATENT; c++)
                     O[c] += pq * mo_e4m3_decode(vr[c]);
+                const double d = (amb && plan->mode == MO_METHOD) ? rounding_ambiguity(p[t]) : 0.0;
+                if (d > 0.0)
+                    for (int c = 0; c < MO_LATENT; c++)
+                        A[c] += d * fabs(mo_e4m3_decode(vr[c]));
             }
             m = m_new;
         }
@@ -266,16 +297,23 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
         for (int s = 0; s < S; s++) {
             double w = (m_s[s] == -INFINITY) ? 0.0 : exp2(m_s[s] - top);
             total += w * l_s[s];
-            for (int c = 0; c < MO_LATENT; c++)
+            for (int c = 0; c < MO_LATENT; c++) {
                 o[c] += w * O_s[(size_t)s * MO_LATENT + c];
+                if (amb)
+                    amb[c] += w * A_s[(size_t)s * MO_LATENT + c];
+            }
         }
-        for (int c = 0; c < MO_LATENT; c++)
+        for (int c = 0; c < MO_LATENT; c++) {
             o[c] = o[c] * k_scale / total;
+            if (amb)
+                amb[c] = amb[c] * k_scale / total;
+        }
         *lse = (top - log2(anchor) + log2(total)) * log(2.0);
     }
     free(m_s);
     free(l_s);
     free(O_s);
+    free(A_s);
     free(x2);
     free(p);
 }
@@ -303,6 +341,7 @@ typedef struct {
     int64_t n_items;
     double* o;
     double* lse;
+    double* amb;   /* optional [items, 512] */
     int nthreads;
     int tid;
 } mo_job;
@@ -343,7 +382,8 @@ static void eval_item(const mo_job* jb, int64_t item)
     const int64_t* starts = jb->cut_ptr ? jb->cut_start + jb->cut_ptr[g] : NULL;
     const int nstart = jb->cut_ptr ? (int)(jb->cut_ptr[g + 1] - jb->cut_ptr[g]) : 0;
     row_eval(q, jb->kv, keyrow, n_group, n_visible, jb->scale, jb->k_scale, &jb->plan, starts,
-             nstart, jb->o + (size_t)item * MO_LATENT, jb->lse + item);
+             nstart, jb->o + (size_t)item * MO_LATENT, jb->lse + item,
+             jb->amb ? jb->amb + (size_t)item * MO_LATENT : NULL);
     free(keyrow);
 }
 
@@ -405,13 +445,14 @@ static int run_job(mo_job* base)
  * seq_lens [B]. sel: optional list of flat rows (b*Q+i)*H+h (n_sel of them); NULL means every row.
  * cut_ptr / cut_start: optional explicit split starts per key group (dense: group b; sparse: group
  * b*Q+i), which replace the uniform split rule when given.
- * o [items,512] and lse [items] in FP64.
+ * o [items,512] and lse [items] in FP64; amb (optional, METHOD mode) [items,512] the rounding
+ * allowance described at the top.
  */
 int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t num_rows,
              int page_size, float k_scale, const int32_t* table, int max_pages,
              const int32_t* seq_lens, float scale, int mode, int splits, int chunk,
              const int64_t* cut_ptr, const int64_t* cut_start, const int64_t* sel, int64_t n_sel,
-             int threads, double* o, double* lse)
+             int threads, double* o, double* lse, double* amb)
 {
     if (page_size < 1)
         return -1;
@@ -438,6 +479,7 @@ int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t 
     jb.n_items = sel ? n_sel : (int64_t)B * Q * H;
     jb.o = o;
     jb.lse = lse;
+    jb.amb = amb;
     jb.nthreads = threads;
     return run_job(&jb);
 }
@@ -448,7 +490,7 @@ int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t 
 int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t num_rows,
               float k_scale, const int32_t* rows, int K, const int32_t* valid, float scale,
               int mode, int splits, int chunk, const int64_t* cut_ptr, const int64_t* cut_start,
-              const int64_t* sel, int64_t n_sel, int threads, double* o, double* lse)
+              const int64_t* sel, int64_t n_sel, int threads, double* o, double* lse, double* amb)
 {
     mo_job jb = {0};
     jb.dense = 0;
@@ -472,6 +514,7 @@ int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t
     jb.n_items = sel ? n_sel : (int64_t)B * Q * H;
     jb.o = o;
     jb.lse = lse;
+    jb.amb = amb;
     jb.nthreads = threads;
     return run_job(&jb);
 }

@@ -202,6 +202,50 @@ def test_cuts_that_do_not_cover_the_keys_are_rejected():
             _run("sparse", x, mode=oracle.METHOD, cuts=bad)
 
 
+# ---- rounding allowance ------------------------------------------------------------------------
+
+def test_allowance_is_zero_where_rounding_is_unambiguous():
+    x = wl.sparse_case(2, 2, 16, 40, [[1, 1], [0, 1]], 64, seed=31)
+    for mode in (oracle.EXACT, oracle.ONLINE):
+        assert not _run("s", x, mode=mode, allowance=True)[2].any()
+    # one key: P = 448 exactly, far from any midpoint
+    o, lse, amb = _run("s", x, mode=oracle.METHOD, allowance=True)
+    assert not amb.any()
+
+
+def test_allowance_equals_the_effect_of_flipping_each_ambiguous_rounding():
+    """Brute force with torch's E4M3 codec (a library routine): every key whose FP32 P lies within
+    2^-13 of an E4M3 rounding midpoint, rounded the other way, moves o by at most the allowance,
+    and the allowance is the sum of those moves (one split, one chunk)."""
+    x = wl.sparse_case(1, 1, 16, 3000, [[3000]], 3000, seed=32, distinct=True)
+    o, lse, amb = _run("s", x, mode=oracle.METHOD, allowance=True, splits=1, chunk=4096)
+    q = _dec_q(x.q_bits)[0, 0]                       # [16, 576]
+    keys = x.rows[0, 0]
+    kd = _dec_kv(x.kv[keys])                          # [3000, 576] E4M3 values
+    x2 = (q @ kd.T) * x.scale * x.k_scale / math.log(2)   # logits in log2 units, [16, 3000]
+    p = 448.0 * np.exp2(x2 - x2.max(axis=1, keepdims=True))
+
+    def e4m3(v):
+        t = torch.from_numpy(np.clip(v.astype(np.float32), -448, 448))
+        return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    eps = 2.0 ** -13
+    ph = e4m3(p)
+    alt_lo, alt_hi = e4m3(p * (1 - eps)), e4m3(p * (1 + eps))
+    d = np.maximum(np.abs(alt_lo - ph), np.abs(alt_hi - ph))
+    L = p.sum(axis=1, keepdims=True)
+    v = kd[:, :512]
+    amb_py = (d @ np.abs(v)) * x.k_scale / L
+    np.testing.assert_allclose(amb[0, 0], amb_py, rtol=1e-9, atol=1e-15)
+    n_amb = 0
+    for h, j in zip(*np.nonzero(d)):
+        n_amb += 1
+        alt = alt_lo[h, j] if alt_lo[h, j] != ph[h, j] else alt_hi[h, j]
+        moved = np.abs((alt - ph[h, j]) * v[j] * x.k_scale / L[h, 0])
+        assert np.all(moved <= amb[0, 0, h] * (1 + 1e-12))
+    assert n_amb > 0, "the case must contain ambiguous roundings"
+
+
 # ---- library softmax on tiny inputs -----------------------------------------------------------
 
 @pytest.mark.parametrize("seed", range(6))
