@@ -79,14 +79,14 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20):
     x = w.make()
     alg = algorithmic(x)
     dev = torch.device("cuda:0")
-    plan = (w.splits, w.tiles)
+    plan = w.plan
     kv_host = torch.from_numpy(x.kv)
     copies = max(1, min(8, math.ceil(min_rotation_bytes / max(1, x.kv.nbytes))))
     kvs = [kv_host.to(dev) for _ in range(copies)]
     q = torch.from_numpy(x.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     o = torch.empty((x.B, x.Q, x.H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((x.B, x.Q, x.H), dtype=torch.float32, device=dev)
-    nbytes = mla.workspace_bytes(x.B, x.Q, x.H, plan[0])
+    nbytes = mla.workspace_bytes(x.kind == "dense", x.B, x.Q, x.H, plan)
     ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
     if x.kind == "dense":
         table = torch.from_numpy(x.block_table).to(dev)
@@ -119,7 +119,8 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20):
     res = {
         "workload": name,
         "description": w.description,
-        "plan": {"splits": plan[0], "tiles": plan[1]},
+        "plan": {"splits": plan[0], "tiles": plan[1],
+                 "mode": "balanced" if plan[2] == mla.BALANCED else "uniform"},
         "us_per_call": round(ms * 1e3, 3),
         "kv_bytes": alg["kv_bytes"],
         "alg_bytes": alg["bytes"],
@@ -151,10 +152,10 @@ def read_traffic(workload: str):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(x, splits, budget_rows=1024, seed=0):
-    """The FP64 oracle (as it stands, METHOD mode with the benchmark's split plan) on a random
-    sample of the workload's query rows, on every core of this process's affinity mask; the time
-    per full call is scaled from the sample by the rows' key counts."""
+def cpu_baseline(x, budget_rows=1024, seed=0):
+    """The FP64 oracle (as it stands, METHOD mode, one split per row) on a random sample of the
+    workload's query rows, on every core of this process's affinity mask; the time per full call
+    is scaled from the sample by the rows' key counts."""
     import oracle
 
     threads = len(os.sched_getaffinity(0))
@@ -172,10 +173,10 @@ def cpu_baseline(x, splits, budget_rows=1024, seed=0):
     t0 = time.perf_counter()
     if x.kind == "dense":
         oracle.dense(x.q_bits, x.kv, x.page_size, x.k_scale, x.block_table, x.seq_lens, x.scale,
-                     mode=oracle.METHOD, splits=splits, sel=sel, threads=threads)
+                     mode=oracle.METHOD, splits=1, sel=sel, threads=threads)
     else:
         oracle.sparse(x.q_bits, x.kv, x.k_scale, x.rows, x.valid, x.scale, mode=oracle.METHOD,
-                      splits=splits, sel=sel, threads=threads)
+                      splits=1, sel=sel, threads=threads)
     dt = time.perf_counter() - t0
     per_call = dt * all_keys / max(1, sample_keys)
     kv_bytes = algorithmic(x)["kv_bytes"]
@@ -184,7 +185,8 @@ def cpu_baseline(x, splits, budget_rows=1024, seed=0):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{len(sel)} of {n_rows} query rows (uniform random, seed {seed}); "
+        "sample": (f"{len(sel)} of {n_rows} query rows (uniform random, seed {seed}), METHOD "
+                   f"mode, one split per row; "
                    f"{dt:.2f} s measured, scaled by key counts to {per_call:.2f} s per call"),
         "us_per_call": round(per_call * 1e6, 1),
     }
@@ -258,8 +260,7 @@ def main():
     }
     cpu = None
     if not args.no_cpu:
-        w = wl.WORKLOADS[HEADLINE]
-        cpu = cpu_baseline(head_x, w.splits, budget_rows=args.cpu_rows)
+        cpu = cpu_baseline(head_x, budget_rows=args.cpu_rows)
     line = {
         "metric": METRIC,
         "value": h["kv_GBps"],

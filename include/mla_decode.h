@@ -38,7 +38,8 @@ typedef enum {
     MLA_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
     MLA_ERR_WORKSPACE = 4,   /* the workspace is missing or smaller than mla_workspace_bytes() */
     MLA_ERR_UNSUPPORTED = 5, /* a plan the kernels do not implement (tiles not 1/2/4 or not
-                                dividing the row tiles, splits < 1) */
+                                dividing the row tiles, splits outside [1, 4096], an unknown mode,
+                                a balanced plan over more than 36863 groups or 2^31 blocks) */
     MLA_ERR_LAUNCH = 6       /* the kernel launch failed (HIP error) */
 } mla_status_t;
 
@@ -52,14 +53,29 @@ typedef struct {
     float k_scale;
 } mla_kv_t;
 
-/* A launch plan. splits: S >= 1, the number of contiguous parts each key group's keys are divided
- * into (part s holds keys [s*per, min(n, (s+1)*per)), per = ceil(n / S)); tiles: 16-row query tiles
- * per workgroup (1, 2 or 4), which must divide the row tiles of a key group (dense: Q*H/16,
- * sparse: H/16). The result depends on splits (where P is anchored and rounded) but is bit-identical
- * for any tiles. */
+/* How a key group's keys are split among workgroups. A key group is a request b (dense; all its Q*H
+ * query rows) or a list (b, i) (sparse; its H rows); n is its key count and its keys form
+ * ceil(n / 128) blocks of 128.
+ *   MLA_SPLIT_UNIFORM   the pages' rule: every group in `splits` = S parts, part s holding keys
+ *                       [s*per, min(n, (s+1)*per)), per = ceil(n / S).
+ *   MLA_SPLIT_BALANCED  the blocks of all groups, concatenated in group order (U blocks), are cut
+ *                       into `splits` = P pieces of equal size: piece p holds global blocks
+ *                       [floor(p*U/P), floor((p+1)*U/P)). A group is split where a piece boundary
+ *                       falls inside it (so split boundaries are multiples of 128 keys) and each
+ *                       piece goes to one workgroup per tile set, which evens out ragged key counts.
+ *                       A group's result then depends on the key counts of the whole call (still
+ *                       bit-identical for identical inputs). At most 36863 groups, and fewer than
+ *                       2^31 blocks in total (counted at each group's maximum key count). */
+enum { MLA_SPLIT_UNIFORM = 0, MLA_SPLIT_BALANCED = 1 };
+
+/* A launch plan. splits: S >= 1 (see mode); tiles: 16-row query tiles per workgroup (1, 2 or 4),
+ * which must divide the row tiles of a key group (dense: Q*H/16, sparse: H/16). The result depends
+ * on where the splits fall (where P is anchored and rounded; within the tolerance of the
+ * definition) but is bit-identical for any tiles. */
 typedef struct {
     int32_t splits;
     int32_t tiles;
+    int32_t mode;   /* MLA_SPLIT_UNIFORM or MLA_SPLIT_BALANCED */
 } mla_plan_t;
 
 /* A plan chosen from shapes only (never from device data): fills *plan. Returns MLA_ERR_NULL or
@@ -67,17 +83,18 @@ typedef struct {
 mla_status_t mla_plan_dense(int B, int Q, int H, int max_pages, int page_size, mla_plan_t* plan);
 mla_status_t mla_plan_sparse(int B, int Q, int H, int K, mla_plan_t* plan);
 
-/* Workspace bytes a call with these shapes and this many splits needs: 0 for splits == 1, else one
- * arrival counter per 16-row tile (first), then the FP32 split partials (B*Q*H*splits rows of
- * 514 floats). */
-size_t mla_workspace_bytes(int B, int Q, int H, int splits);
+/* Workspace bytes a call of these shapes (dense = 1 for mla_decode_dense, 0 for
+ * mla_decode_sparse) and plan needs: 0 when splits == 1, else one arrival counter per 16-row tile
+ * (first), then FP32 split partials of 514 floats per row: B*Q*H*S rows for a uniform plan, at most
+ * 2*P*(rows of a group) for a balanced one. */
+size_t mla_workspace_bytes(int dense, int B, int Q, int H, const mla_plan_t* plan);
 
 /* The leading bytes of the workspace that must be zero when a call starts (its arrival counters);
  * the call leaves them zero again (the last arriving workgroup of each tile resets its counter) and
  * leaves the rest of the workspace undefined. A workspace that served a call whose zero prefix was
  * at least as long can serve the next call as is; otherwise zero the longer prefix first. Calls that
  * share a workspace must be ordered on one stream. */
-size_t mla_workspace_zero_bytes(int B, int Q, int H, int splits);
+size_t mla_workspace_zero_bytes(int dense, int B, int Q, int H, const mla_plan_t* plan);
 
 /*
  * Dense paged decode.
@@ -94,8 +111,8 @@ size_t mla_workspace_zero_bytes(int B, int Q, int H, int splits);
  *   o            device bf16 [B, Q, H, 512] (8-byte aligned): softmax-weighted latent, RNE.
  *   lse          device float [B, Q, H]: natural-log sum of exp(scale * q . K) over the row's keys.
  *   Position i sees keys j < seq_len - Q + i + 1; a row with none gets o = +0 and lse = -inf.
- *   workspace    device, >= mla_workspace_bytes(B, Q, H, splits) bytes, 256-byte aligned (may be
- *                NULL when splits == 1).
+ *   workspace    device, >= mla_workspace_bytes(1, B, Q, H, plan) bytes, 256-byte aligned (may
+ *                be NULL when splits == 1).
  */
 mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* block_table,
                               int max_pages, const int32_t* seq_lens, float scale, int B, int Q,

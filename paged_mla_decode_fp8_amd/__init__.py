@@ -17,9 +17,10 @@ import torch
 from ._build import LIB
 
 __all__ = ["MlaError", "Plan", "dense", "sparse", "plan_dense", "plan_sparse", "workspace_bytes",
-           "workspace_zero_bytes", "library_path"]
+           "workspace_zero_bytes", "library_path", "UNIFORM", "BALANCED"]
 
 MLA_OK = 0
+UNIFORM, BALANCED = 0, 1   # mla_plan_t.mode
 
 
 class MlaError(RuntimeError):
@@ -31,6 +32,7 @@ class MlaError(RuntimeError):
 class Plan(NamedTuple):
     splits: int
     tiles: int
+    mode: int = UNIFORM
 
 
 class _KV(ctypes.Structure):
@@ -39,7 +41,7 @@ class _KV(ctypes.Structure):
 
 
 class _Plan(ctypes.Structure):
-    _fields_ = [("splits", ctypes.c_int32), ("tiles", ctypes.c_int32)]
+    _fields_ = [("splits", ctypes.c_int32), ("tiles", ctypes.c_int32), ("mode", ctypes.c_int32)]
 
 
 _lib = None
@@ -58,9 +60,9 @@ def _load():
         P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
-        lib.mla_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.mla_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(_Plan)]
         lib.mla_workspace_bytes.restype = sz
-        lib.mla_workspace_zero_bytes.argtypes = [i32, i32, i32, i32]
+        lib.mla_workspace_zero_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(_Plan)]
         lib.mla_workspace_zero_bytes.restype = sz
         lib.mla_plan_dense.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Plan)]
         lib.mla_plan_dense.restype = i32
@@ -84,21 +86,32 @@ def _check(status: int):
 def plan_dense(B: int, Q: int, H: int, max_pages: int, page_size: int) -> Plan:
     p = _Plan()
     _check(_load().mla_plan_dense(B, Q, H, max_pages, page_size, ctypes.byref(p)))
-    return Plan(p.splits, p.tiles)
+    return Plan(p.splits, p.tiles, p.mode)
 
 
 def plan_sparse(B: int, Q: int, H: int, K: int) -> Plan:
     p = _Plan()
     _check(_load().mla_plan_sparse(B, Q, H, K, ctypes.byref(p)))
-    return Plan(p.splits, p.tiles)
+    return Plan(p.splits, p.tiles, p.mode)
 
 
-def workspace_bytes(B: int, Q: int, H: int, splits: int) -> int:
-    return int(_load().mla_workspace_bytes(B, Q, H, splits))
+def _as_plan(plan) -> Plan:
+    return Plan(*plan)
 
 
-def workspace_zero_bytes(B: int, Q: int, H: int, splits: int) -> int:
-    return int(_load().mla_workspace_zero_bytes(B, Q, H, splits))
+def _plan_struct(plan) -> _Plan:
+    pl = _as_plan(plan)
+    return _Plan(int(pl.splits), int(pl.tiles), int(pl.mode))
+
+
+def workspace_bytes(dense: bool, B: int, Q: int, H: int, plan) -> int:
+    """Bytes of workspace a call needs (``plan``: a Plan or a (splits, tiles[, mode]) tuple)."""
+    return int(_load().mla_workspace_bytes(int(dense), B, Q, H, ctypes.byref(_plan_struct(plan))))
+
+
+def workspace_zero_bytes(dense: bool, B: int, Q: int, H: int, plan) -> int:
+    return int(_load().mla_workspace_zero_bytes(int(dense), B, Q, H,
+                                                ctypes.byref(_plan_struct(plan))))
 
 
 # One workspace per (device, stream) and the length of its prefix known to be zero: a call needs
@@ -106,11 +119,11 @@ def workspace_zero_bytes(B: int, Q: int, H: int, splits: int) -> int:
 _workspaces: dict = {}
 
 
-def _workspace(device: torch.device, stream: int, B, Q, H, splits) -> torch.Tensor | None:
-    nbytes = workspace_bytes(B, Q, H, splits)
+def _workspace(device: torch.device, stream: int, dense, B, Q, H, plan) -> torch.Tensor | None:
+    nbytes = workspace_bytes(dense, B, Q, H, plan)
     if nbytes == 0:
         return None
-    need_zero = workspace_zero_bytes(B, Q, H, splits)
+    need_zero = workspace_zero_bytes(dense, B, Q, H, plan)
     key = (device.index, stream)
     ws, zero = _workspaces.get(key, (None, 0))
     if ws is None or ws.numel() < nbytes:
@@ -142,8 +155,7 @@ def _check_tensor(name, t, dtype, device):
 def _plan_arg(plan):
     if plan is None:
         return None
-    splits, tiles = plan
-    return ctypes.byref(_Plan(int(splits), int(tiles)))
+    return ctypes.byref(_plan_struct(plan))
 
 
 def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
@@ -161,9 +173,9 @@ def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens
     assert D == 576
     o, lse = _outputs(q, o, lse)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    pl = plan if plan is not None else plan_dense(B, Q, H, block_table.shape[1], page_size)
+    pl = _as_plan(plan) if plan is not None else plan_dense(B, Q, H, block_table.shape[1], page_size)
     if workspace is None:
-        workspace = _workspace(dev, stream, B, Q, H, pl[0])
+        workspace = _workspace(dev, stream, True, B, Q, H, pl)
     kvs = _KV(kv.data_ptr(), kv.numel() // 576, int(page_size), float(k_scale))
     _check(_load().mla_decode_dense(
         _ptr(q), ctypes.byref(kvs), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
@@ -187,9 +199,9 @@ def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.T
     K = rows.shape[2]
     o, lse = _outputs(q, o, lse)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    pl = plan if plan is not None else plan_sparse(B, Q, H, K)
+    pl = _as_plan(plan) if plan is not None else plan_sparse(B, Q, H, K)
     if workspace is None:
-        workspace = _workspace(dev, stream, B, Q, H, pl[0])
+        workspace = _workspace(dev, stream, False, B, Q, H, pl)
     kvs = _KV(kv.data_ptr(), kv.numel() // 576, 1, float(k_scale))
     _check(_load().mla_decode_sparse(
         _ptr(q), ctypes.byref(kvs), _ptr(rows), K, _ptr(valid), float(scale), B, Q, H,

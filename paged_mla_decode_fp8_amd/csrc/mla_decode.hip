@@ -66,6 +66,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
@@ -83,15 +84,16 @@ struct Params {
     float scale_log2;   // scale * k_scale * log2(e)
     float k_scale;
     int Q, H;
-    int S;
+    int S;               // uniform plan: splits per key group; balanced plan: pieces
+    int balanced;
     int groups;          // dense: B, sparse: B * Q
     int rows_per_group;  // dense: Q * H, sparse: H
     int tilesets;        // (rows_per_group / 16) / T
-    int gs_count;        // groups * S
+    int units;           // uniform: groups * S (group, split) pairs; balanced: S pieces
     uint16_t* o;
     float* lse;
-    float* ws_o;         // [B*Q*H][S][512]
-    float* ws_ml;        // [B*Q*H][S][2]
+    float* ws_o;         // [partial slot][T * 16 rows][512]
+    float* ws_ml;        // [partial slot][T * 16 rows][2]
     uint32_t* ws_cnt;    // [groups * tilesets]
 };
 
@@ -105,8 +107,9 @@ struct Smem {
     static constexpr int OFF_P = 2 * SLOT;                     // E4M3 P [T][16][PPITCH]
     static constexpr int OFF_ALPHA = OFF_P + T * PTILE;        // float [T*16]
     static constexpr int OFF_FM = OFF_ALPHA + T * 16 * 4;      // float [T*16]
-    static constexpr int OFF_FL = OFF_FM + T * 16 * 4;         // float [T*16]
-    static constexpr int OFF_KMASK = OFF_FL + T * 16 * 4;      // uint32 [2][4] key presence bits
+    static constexpr int OFF_FL = OFF_FM + T * 16 * 4;         // float [2][T*16] (key halves)
+    static constexpr int OFF_XMAX = OFF_FL + 2 * T * 16 * 4;   // float [2][T*16] block maxima
+    static constexpr int OFF_KMASK = OFF_XMAX + 2 * T * 16 * 4; // uint32 [2][4] key presence bits
     static constexpr int OFF_IDX = OFF_KMASK + 2 * 16;         // int32 [2][BLK] raw key indices
     static constexpr int OFF_RP = OFF_IDX + 2 * BLK * 4;       // uint64 [2][BLK] key row pointers
     static constexpr int OFF_MISC = OFF_RP + 2 * BLK * 8;      // int [4]
@@ -201,6 +204,48 @@ __device__ inline void dma16(const uint8_t* gsrc, uint32_t lds_base)
         : "memory");
 }
 
+// The nine row DMAs of one 16-key subtile: instruction i moves 16 bytes at this lane's src[i] to
+// LDS byte lds_base + 1024 i + 16 lane. One asm block steps M0 itself, so the destinations cost one
+// scalar register instead of nine (the compiler would keep all of them live).
+__device__ inline void dma_subtile(const uint8_t* const (&src)[9], uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %8, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %9, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %10, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3]), "v"(src[4]),
+          "v"(src[5]), "v"(src[6]), "v"(src[7]), "v"(src[8])
+        : "memory", "scc");
+}
+
 // One global_load_lds_dword: 4 bytes at this lane's gsrc -> LDS byte lds_base + 4 * lane (asm
 // for the same reasons as dma16).
 __device__ inline void dma4(const void* gsrc, uint32_t lds_base)
@@ -253,134 +298,303 @@ __device__ inline const uint8_t* dma_src(const uint64_t* rp, int i, int lane)
     return reinterpret_cast<const uint8_t*>(rp[lane & 15]) + 512 + 16 * (lane >> 4);
 }
 
-// The work of one workgroup: key group g, split s of S, tile set ts; the split's keys
-// [first, first + mine) of the group's n_grp, in nblk blocks of 128.
+// One work item of a workgroup: tile set ts of key group g, the group's keys
+// [first, first + mine) of n_grp, in nblk blocks of 128. The group's keys are divided among
+// `count` items (one per split); count == 1 finishes the rows directly, otherwise the item leaves a
+// partial in workspace slot `slot` and the last of the group's items to arrive merges them.
 struct Work {
-    int g, s, ts, nblk;
+    int g, ts, nblk;
+    int count;   // items (splits) of the group
+    int slot;    // partial slot of this item (tile set folded in)
+    int fp;      // balanced plan: the group's first piece
     int64_t n_grp, first, mine, row_base;
 };
 
 template <bool DENSE>
-__device__ inline bool decode_work(const Params& p, Work& w)
+__device__ inline int64_t group_keys(const Params& p, int g)
 {
-    // a split's tile sets share one XCD (blockIdx % 8)
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int slotid = bid >> 3;
-    w.ts = slotid % p.tilesets;
-    const int gs = (slotid / p.tilesets) * 8 + xcd;
-    if (gs >= p.gs_count)
-        return false;
-    w.s = gs / p.groups;
-    w.g = gs % p.groups;
     if (DENSE) {
         const int64_t cap = (int64_t)p.max_pages * p.page_size;
-        const int64_t sl = p.seq_lens[w.g];
-        w.n_grp = sl < 0 ? 0 : (sl > cap ? cap : sl);
-    } else {
-        const int64_t v = p.valid[w.g];
-        w.n_grp = v < 0 ? 0 : (v > p.K ? p.K : v);
+        const int64_t sl = p.seq_lens[g];
+        return sl < 0 ? 0 : (sl > cap ? cap : sl);
     }
-    // the pages' per / first / mine
+    const int64_t v = p.valid[g];
+    return v < 0 ? 0 : (v > p.K ? p.K : v);
+}
+
+__device__ inline int64_t nblocks(int64_t n) { return (n + BLK - 1) / BLK; }
+
+// Uniform plan (the pages' rule): unit = (split s, group g); the split holds keys
+// [s per, min(n, (s + 1) per)) with per = ceil(n / S).
+template <bool DENSE>
+__device__ inline void decode_uniform(const Params& p, int unit, int ts, Work& w)
+{
+    const int s = unit / p.groups;
+    w.g = unit % p.groups;
+    w.ts = ts;
+    w.n_grp = group_keys<DENSE>(p, w.g);
     const int64_t per = (w.n_grp + p.S - 1) / p.S;
-    w.first = (int64_t)w.s * per < w.n_grp ? (int64_t)w.s * per : w.n_grp;
+    w.first = (int64_t)s * per < w.n_grp ? (int64_t)s * per : w.n_grp;
     w.mine = (w.n_grp - w.first) < per ? (w.n_grp - w.first) : per;
-    w.nblk = (int)((w.mine + BLK - 1) / BLK);
+    w.nblk = (int)nblocks(w.mine);
+    w.count = p.S;
+    w.fp = 0;
+    w.slot = (w.g * p.S + s) * p.tilesets + ts;
     w.row_base = (int64_t)w.g * p.rows_per_group;
-    return true;
+}
+
+// Balanced plan: the groups' 128-key blocks, concatenated in group order (U of them), are cut into
+// S pieces of equal size (piece q = blocks [floor(q U / S), floor((q + 1) U / S))), one per
+// workgroup (and tile set). A group is split where piece boundaries fall inside it; a piece walks
+// the groups it overlaps in order. An empty group belongs to the piece holding the block where it
+// would start (the last piece at the end; with no block at all, piece floor(g S / groups)).
+struct Span {
+    int g_lo, g_hi;   // the piece's groups
+    int64_t pre_lo;   // blocks before group g_lo
+    int64_t U;        // blocks of all groups
+};
+
+__device__ inline int piece_of(int64_t b, int64_t U, int np) { return (int)(((b + 1) * np - 1) / U); }
+
+__device__ inline int first_piece(int64_t pre, int g, int64_t U, int np, int groups)
+{
+    if (U == 0)
+        return (int)((int64_t)g * np / groups);
+    return pre < U ? piece_of(pre, U, np) : np - 1;
+}
+
+__device__ inline int last_piece(int64_t pre, int64_t nb, int g, int64_t U, int np, int groups)
+{
+    return nb > 0 ? piece_of(pre + nb - 1, U, np) : first_piece(pre, g, U, np, groups);
+}
+
+__device__ inline int wave_sum_i32(int v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    return v;
+}
+
+// The piece's groups, by the whole workgroup: a block-wide prefix sum of the groups' block counts
+// into the (still unused) KV slots, then counts of the groups wholly before the piece and of the
+// groups starting at or before it. The host bounds U below 2^31 and the groups by the slots' size.
+// Contains workgroup barriers; every thread returns the same span.
+template <bool DENSE>
+__device__ Span piece_span(const Params& p, uint8_t* smem, int piece, int tid, int lane)
+{
+    const int G = p.groups;
+    const int np = p.S;
+    const int wave = tid >> 6;
+    int32_t* pre = reinterpret_cast<int32_t*>(smem);                 // [G + 1]
+    int32_t* red = reinterpret_cast<int32_t*>(smem + 2 * SLOT);      // [8] wave sums, [2] counts
+    int carry = 0;
+    for (int base = 0; base < G; base += THREADS) {
+        const int g = base + tid;
+        const int nb = g < G ? (int)nblocks(group_keys<DENSE>(p, g)) : 0;
+        int incl = nb;   // inclusive prefix within the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d);
+            if (lane >= d)
+                incl += t;
+        }
+        if (lane == 63)
+            red[wave] = incl;
+        __syncthreads();
+        int before = carry, chunk = 0;
+#pragma unroll
+        for (int k = 0; k < WAVES; k++) {
+            const int v = red[k];
+            before += k < wave ? v : 0;
+            chunk += v;
+        }
+        if (g < G)
+            pre[g] = before + incl - nb;
+        carry += chunk;
+        __syncthreads();   // the wave sums are reused by the next chunk
+    }
+    const int U = carry;
+    if (tid == 0) {
+        pre[G] = U;
+        red[8] = 0;
+        red[9] = 0;
+    }
+    __syncthreads();
+    int lo = 0, hi = 0;
+    for (int g = tid; g < G; g += THREADS) {
+        const int pg = pre[g];
+        const int nb = pre[g + 1] - pg;
+        lo += last_piece(pg, nb, g, U, np, G) < piece ? 1 : 0;
+        hi += first_piece(pg, g, U, np, G) <= piece ? 1 : 0;
+    }
+    lo = wave_sum_i32(lo);
+    hi = wave_sum_i32(hi);
+    if (lane == 0) {
+        atomicAdd(&red[8], lo);
+        atomicAdd(&red[9], hi);
+    }
+    __syncthreads();
+    Span sp;
+    sp.g_lo = __builtin_amdgcn_readfirstlane(red[8]);
+    sp.g_hi = __builtin_amdgcn_readfirstlane(red[9]) - 1;
+    sp.pre_lo = __builtin_amdgcn_readfirstlane(pre[sp.g_lo]);
+    sp.U = U;
+    __syncthreads();   // every wave has read the span before the slots fill
+    return sp;
+}
+
+// Item of group g (whose blocks start at global block pre) in piece `piece`.
+template <bool DENSE>
+__device__ inline void balanced_item(const Params& p, int piece, int ts, int g, int64_t pre,
+                                     const Span& sp, Work& w)
+{
+    const int np = p.S;
+    w.g = g;
+    w.ts = ts;
+    w.n_grp = group_keys<DENSE>(p, g);
+    const int64_t nb = nblocks(w.n_grp);
+    const int fp = first_piece(pre, g, sp.U, np, p.groups);
+    const int lp = last_piece(pre, nb, g, sp.U, np, p.groups);
+    int64_t lo = 0, hi = 0;
+    if (nb > 0) {
+        const int64_t a0 = (int64_t)piece * sp.U / np, a1 = (int64_t)(piece + 1) * sp.U / np;
+        lo = (a0 > pre ? a0 : pre) - pre;
+        hi = (a1 < pre + nb ? a1 : pre + nb) - pre;
+        if (hi < lo)
+            hi = lo;
+    }
+    w.first = lo * BLK;
+    const int64_t end = hi * BLK < w.n_grp ? hi * BLK : w.n_grp;
+    w.mine = end > w.first ? end - w.first : 0;
+    w.nblk = (int)(hi - lo);
+    w.count = lp - fp + 1;
+    w.fp = fp;
+    w.slot = (2 * piece + (piece == fp ? 1 : 0)) * p.tilesets + ts;
+    w.row_base = (int64_t)g * p.rows_per_group;
+}
+
+// Partial slot of the c-th item (split) of the work item's group.
+__device__ inline int contributor_slot(const Params& p, const Work& w, int c)
+{
+    const int unit = p.balanced ? 2 * (w.fp + c) + (c == 0 ? 1 : 0) : w.g * p.S + c;
+    return unit * p.tilesets + w.ts;
+}
+
+// A slot's partial O (T * 16 rows x 512 columns, FP32) is kept in the PV accumulators' own order,
+// [column quarter pw][tile t][column block c][lane][4]: element (row 16 t + lane % 16, column
+// 128 pw + 16 c + 4 (lane / 16) + e). Each store of a PV wave and each load of the merge then
+// moves 1 KB of contiguous memory. Offset in floats.
+template <int T>
+__device__ inline int64_t partial_o_offset(int slot, int pw, int t, int c, int lane)
+{
+    return ((((int64_t)slot * 4 + pw) * T + t) * 8 + c) * 256 + 4 * lane;
 }
 
 // ---- QK waves: Q stage, S^T = K (hi + lo)^T, softmax; P and the rescale factors to LDS ----
+// QK wave qw owns key half kh = qw % 2 (subtiles 4 kh .. 4 kh + 3 of every block) of the tile pair
+// qw / 2: each K fragment read from LDS feeds the MFMAs of both tiles. The two halves of a tile's
+// keys exchange their block maxima through LDS (both then hold the same running maximum) and
+// keep separate row sums, added in a fixed order at the end. The same split is used for every T
+// (T <= 2: waves 0 and 1, one tile pair), so results do not depend on T.
 template <int T, bool DENSE>
 __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Work& w, int qw,
                                         int lane)
 {
     using L = Smem<T>;
+    constexpr int TW = T >= 2 ? 2 : 1;   // tiles per QK wave
+    constexpr int KS = NSUB / 2;          // subtiles per key half
     const int n16 = lane & 15;   // MFMA row / column within 16
     const int grp = lane >> 4;   // MFMA k-group 0..3
-    const bool active = qw < T;
-    const int qt = active ? qw : 0;
-    const int tile = w.ts * T + qt;
-    int64_t lim;   // keys [0, lim) of the group are visible to this tile
-    if (DENSE) {
-        const int pos = (16 * tile) / p.H;
-        const int64_t c = w.n_grp - p.Q + pos + 1;
-        lim = c < 0 ? 0 : (c > w.n_grp ? w.n_grp : c);
-    } else {
-        lim = w.n_grp;
+    const int kh = qw & 1;
+    const bool active = (qw >> 1) * TW < T;
+    const int qt0 = active ? (qw >> 1) * TW : 0;   // first tile of the pair within the tile set
+    int64_t lim[TW];   // keys [0, lim) of the group are visible to tile j
+#pragma unroll
+    for (int j = 0; j < TW; j++) {
+        if (DENSE) {
+            const int pos = (16 * (w.ts * T + qt0 + j)) / p.H;
+            const int64_t c = w.n_grp - p.Q + pos + 1;
+            lim[j] = c < 0 ? 0 : (c > w.n_grp ? w.n_grp : c);
+        } else {
+            lim[j] = w.n_grp;
+        }
     }
 
-    // ---- Q of this tile -> exact E4M3 hi + lo of q * 2^k (B operands) ----
-    v8i qhi[4], qlo[4], qrope;
-    float row_scale = 0.f;  // scale_log2 * 2^-k for row n16
-    if (w.nblk > 0 && active) {
-        const uint16_t* qrow = p.q + (w.row_base + 16 * tile + n16) * ROW;
-        // 32 bf16 per operand step st: values q[128 st + 32 grp + 0..31] (rope: 512 + 32 (grp & 1))
-        v4i raw[10], rawb[10];
+    // ---- Q of the tiles -> exact E4M3 hi + lo of q * 2^k (B operands) ----
+    v8i qhi[TW][4], qlo[TW][4], qrope[TW];
+    float row_scale[TW];  // scale_log2 * 2^-k for row n16
 #pragma unroll
-        for (int st = 0; st < 5; st++) {
-            const uint16_t* src = st < 4 ? qrow + 128 * st + 32 * grp : qrow + 512 + 32 * (grp & 1);
-            raw[2 * st] = *reinterpret_cast<const v4i*>(src);
-            raw[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 8);
-            rawb[2 * st] = *reinterpret_cast<const v4i*>(src + 16);
-            rawb[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 24);
-        }
-        float amax = 0.f;
+    for (int j = 0; j < TW; j++) {
+        row_scale[j] = 0.f;
+        if (w.nblk > 0 && active) {
+            const uint16_t* qrow = p.q + (w.row_base + 16 * (w.ts * T + qt0 + j) + n16) * ROW;
+            // 32 bf16 per operand step st: values q[128 st + 32 grp + 0..31] (rope: 512 + 32 (grp & 1))
+            v4i raw[10], rawb[10];
 #pragma unroll
-        for (int i = 0; i < 10; i++) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const uint32_t wa = (uint32_t)raw[i][e], wb = (uint32_t)rawb[i][e];
-                amax = fmaxf(amax, fabsf(bf16_to_f32(wa & 0xFFFF)));
-                amax = fmaxf(amax, fabsf(bf16_to_f32(wa >> 16)));
-                amax = fmaxf(amax, fabsf(bf16_to_f32(wb & 0xFFFF)));
-                amax = fmaxf(amax, fabsf(bf16_to_f32(wb >> 16)));
+            for (int st = 0; st < 5; st++) {
+                const uint16_t* src = st < 4 ? qrow + 128 * st + 32 * grp : qrow + 512 + 32 * (grp & 1);
+                raw[2 * st] = *reinterpret_cast<const v4i*>(src);
+                raw[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 8);
+                rawb[2 * st] = *reinterpret_cast<const v4i*>(src + 16);
+                rawb[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 24);
             }
-        }
-        amax = wave_max16(amax);
-        // k: the largest integer with amax * 2^k <= 448 (0 for a zero row)
-        int k = 0;
-        if (amax > 0.f) {
-            int e;
-            const float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
-            k = (2.f * m <= 1.75f) ? (9 - e) : (8 - e);
-        }
-        row_scale = ldexpf(p.scale_log2, -k);
-        auto split4 = [&](uint32_t w0, uint32_t w1, uint32_t& hi, uint32_t& lo) {
-            const float x0 = ldexpf(bf16_to_f32(w0 & 0xFFFF), k);
-            const float x1 = ldexpf(bf16_to_f32(w0 >> 16), k);
-            const float x2 = ldexpf(bf16_to_f32(w1 & 0xFFFF), k);
-            const float x3 = ldexpf(bf16_to_f32(w1 >> 16), k);
-            hi = pack_e4m3(x0, x1, x2, x3);
-            const float h0 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 0);
-            const float h1 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 1);
-            const float h2 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 2);
-            const float h3 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 3);
-            lo = pack_e4m3(x0 - h0, x1 - h1, x2 - h2, x3 - h3);
-        };
+            float amax = 0.f;
 #pragma unroll
-        for (int st = 0; st < 5; st++) {
-            // dword e of the operand holds values 4e..4e+3
-            const uint32_t wd[16] = {
-                (uint32_t)raw[2 * st][0], (uint32_t)raw[2 * st][1], (uint32_t)raw[2 * st][2],
-                (uint32_t)raw[2 * st][3], (uint32_t)raw[2 * st + 1][0], (uint32_t)raw[2 * st + 1][1],
-                (uint32_t)raw[2 * st + 1][2], (uint32_t)raw[2 * st + 1][3], (uint32_t)rawb[2 * st][0],
-                (uint32_t)rawb[2 * st][1], (uint32_t)rawb[2 * st][2], (uint32_t)rawb[2 * st][3],
-                (uint32_t)rawb[2 * st + 1][0], (uint32_t)rawb[2 * st + 1][1],
-                (uint32_t)rawb[2 * st + 1][2], (uint32_t)rawb[2 * st + 1][3]};
-            v8i vh, vl;
+            for (int i = 0; i < 10; i++) {
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                uint32_t h, l;
-                split4(wd[2 * e], wd[2 * e + 1], h, l);
-                vh[e] = (int)h;
-                vl[e] = (int)l;
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t wa = (uint32_t)raw[i][e], wb = (uint32_t)rawb[i][e];
+                    amax = fmaxf(amax, fabsf(bf16_to_f32(wa & 0xFFFF)));
+                    amax = fmaxf(amax, fabsf(bf16_to_f32(wa >> 16)));
+                    amax = fmaxf(amax, fabsf(bf16_to_f32(wb & 0xFFFF)));
+                    amax = fmaxf(amax, fabsf(bf16_to_f32(wb >> 16)));
+                }
             }
-            if (st < 4) {
-                qhi[st] = vh;
-                qlo[st] = vl;
-            } else {
-                qrope = grp < 2 ? vh : vl;  // rope step: k-groups 0,1 carry hi, 2,3 carry lo
+            amax = wave_max16(amax);
+            // k: the largest integer with amax * 2^k <= 448 (0 for a zero row)
+            int k = 0;
+            if (amax > 0.f) {
+                int e;
+                const float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
+                k = (2.f * m <= 1.75f) ? (9 - e) : (8 - e);
+            }
+            row_scale[j] = ldexpf(p.scale_log2, -k);
+            auto split4 = [&](uint32_t w0, uint32_t w1, uint32_t& hi, uint32_t& lo) {
+                const float x0 = ldexpf(bf16_to_f32(w0 & 0xFFFF), k);
+                const float x1 = ldexpf(bf16_to_f32(w0 >> 16), k);
+                const float x2 = ldexpf(bf16_to_f32(w1 & 0xFFFF), k);
+                const float x3 = ldexpf(bf16_to_f32(w1 >> 16), k);
+                hi = pack_e4m3(x0, x1, x2, x3);
+                const float h0 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 0);
+                const float h1 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 1);
+                const float h2 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 2);
+                const float h3 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 3);
+                lo = pack_e4m3(x0 - h0, x1 - h1, x2 - h2, x3 - h3);
+            };
+#pragma unroll
+            for (int st = 0; st < 5; st++) {
+                // dword e of the operand holds values 4e..4e+3
+                const uint32_t wd[16] = {
+                    (uint32_t)raw[2 * st][0], (uint32_t)raw[2 * st][1], (uint32_t)raw[2 * st][2],
+                    (uint32_t)raw[2 * st][3], (uint32_t)raw[2 * st + 1][0], (uint32_t)raw[2 * st + 1][1],
+                    (uint32_t)raw[2 * st + 1][2], (uint32_t)raw[2 * st + 1][3], (uint32_t)rawb[2 * st][0],
+                    (uint32_t)rawb[2 * st][1], (uint32_t)rawb[2 * st][2], (uint32_t)rawb[2 * st][3],
+                    (uint32_t)rawb[2 * st + 1][0], (uint32_t)rawb[2 * st + 1][1],
+                    (uint32_t)rawb[2 * st + 1][2], (uint32_t)rawb[2 * st + 1][3]};
+                v8i vh, vl;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    uint32_t h, l;
+                    split4(wd[2 * e], wd[2 * e + 1], h, l);
+                    vh[e] = (int)h;
+                    vl[e] = (int)l;
+                }
+                if (st < 4) {
+                    qhi[j][st] = vh;
+                    qlo[j][st] = vl;
+                } else {
+                    qrope[j] = grp < 2 ? vh : vl;  // rope step: k-groups 0,1 carry hi, 2,3 carry lo
+                }
             }
         }
     }
@@ -391,28 +605,37 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                       : 16 * (512 + 16 * (2 * (grp & 1) + h) + n16);
     };
     const float neg_inf = -INFINITY;
-    float m_run = neg_inf;   // running max (log2 units) of row n16
-    float l_run = 0.f;       // running sum of the unrounded P of that row
+    float m_run[TW], l_run[TW];   // running max (log2 units) and this half's running sum, row n16
+#pragma unroll
+    for (int j = 0; j < TW; j++) {
+        m_run[j] = neg_inf;
+        l_run[j] = 0.f;
+    }
     float* xalpha = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
+    float* xmax = reinterpret_cast<float*>(smem + L::OFF_XMAX);   // [2][T * 16] block maxima
 
     // iteration i: QK and softmax of block i (the PV waves work on block i - 1)
     for (int i = 0; i <= w.nblk; i++) {
         const int slot = i & 1;
         lds_sync();   // B1: block i landed; P of block i - 1 published
         const bool work = active && i < w.nblk;
-        v4f acc[NSUB];
+        v4f acc[TW][KS];
+        float bmax[TW];
+        uint32_t vis[TW];
         if (work) {
-            const uint8_t* kslot = smem + slot * SLOT;
+            const uint8_t* kslot = smem + slot * SLOT + (KS * kh) * SUBB;
 #pragma unroll
-            for (int u = 0; u < NSUB; u++) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
-            // Fragment f: step f / 8, subtile f % 8. Step f issues the hi MFMA of fragment f (or its
-            // packed rope MFMA) and the lo MFMA of fragment f - 1, so no MFMA waits on the one just
-            // issued; a fragment stays in the ring until its lo MFMA.
-            constexpr int NFRAG = 5 * NSUB;
+            for (int j = 0; j < TW; j++)
+#pragma unroll
+                for (int u = 0; u < KS; u++) acc[j][u] = v4f{0.f, 0.f, 0.f, 0.f};
+            // Fragment f: step f / KS, subtile f % KS of this half. Step f issues the hi MFMAs of
+            // fragment f (or its packed rope MFMAs) and the lo MFMAs of fragment f - 1, so no MFMA
+            // waits on the one just issued; a fragment stays in the ring until its lo MFMAs.
+            constexpr int NFRAG = 5 * KS;
             constexpr int AHEAD = 2, RING = AHEAD + 2;
             v8i kf[RING];
             auto load_frag = [&](int f) {
-                const int st = f / NSUB, sub = f % NSUB;
+                const int st = f / KS, sub = f % KS;
                 return cat(lds_read16(kslot, sub * SUBB + koff(st, 0)),
                            lds_read16(kslot, sub * SUBB + koff(st, 1)));
             };
@@ -423,94 +646,126 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                 if (f + AHEAD < NFRAG)
                     kf[(f + AHEAD) % RING] = load_frag(f + AHEAD);
                 if (f < NFRAG) {
-                    const int st = f / NSUB, sub = f % NSUB;
-                    acc[sub] = mfma(kf[f % RING], st < 4 ? qhi[st] : qrope, acc[sub]);
+                    const int st = f / KS, sub = f % KS;
+#pragma unroll
+                    for (int j = 0; j < TW; j++)
+                        acc[j][sub] = mfma(kf[f % RING], st < 4 ? qhi[j][st] : qrope[j], acc[j][sub]);
                 }
-                if (f >= 1 && f - 1 < 4 * NSUB) {
-                    const int st = (f - 1) / NSUB, sub = (f - 1) % NSUB;
-                    acc[sub] = mfma(kf[(f - 1) % RING], qlo[st], acc[sub]);
+                if (f >= 1 && f - 1 < 4 * KS) {
+                    const int st = (f - 1) / KS, sub = (f - 1) % KS;
+#pragma unroll
+                    for (int j = 0; j < TW; j++)
+                        acc[j][sub] = mfma(kf[(f - 1) % RING], qlo[j][st], acc[j][sub]);
                 }
+            }
+            // ---- visibility of this lane's 16 keys: bit 4u + jj <-> key 16 (4 kh + u) + 4 grp + jj
+            const int64_t kbase = w.first + (int64_t)i * BLK;
+            const v4i mw = lds_read16(smem, L::OFF_KMASK + slot * 16);
+            uint32_t present = 0;
+#pragma unroll
+            for (int u = 0; u < KS; u++) {
+                const int sg = KS * kh + u;
+                present |= (((uint32_t)mw[sg >> 1] >> (16 * (sg & 1) + 4 * grp)) & 0xFu) << (4 * u);
+            }
+            // ---- mask, this half's block maxima (in-lane, then across the 4 k-groups), to LDS.
+            // The row scale is positive, so max(s * scale) = scale * max(s) exactly. ----
+#pragma unroll
+            for (int j = 0; j < TW; j++) {
+                const int64_t lr = lim[j] - kbase;    // keys of the block before the tile's bound
+                const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
+                vis[j] = present;
+#pragma unroll
+                for (int u = 0; u < KS; u++) {
+                    const int keep = lim_rel - (16 * (KS * kh + u) + 4 * grp);   // of the 4 in bound
+                    const uint32_t nib = keep >= 4 ? 0xFu : (keep <= 0 ? 0u : ((1u << keep) - 1u));
+                    vis[j] &= ~(0xFu << (4 * u)) | (nib << (4 * u));
+                }
+                if (!__all(vis[j] == 0xFFFFu)) {
+#pragma unroll
+                    for (int u = 0; u < KS; u++)
+#pragma unroll
+                        for (int jj = 0; jj < 4; jj++)
+                            acc[j][u][jj] = ((vis[j] >> (4 * u + jj)) & 1u) ? acc[j][u][jj] : neg_inf;
+                }
+                float bm = neg_inf;
+#pragma unroll
+                for (int u = 0; u < KS; u++)
+                    bm = fmaxf(bm, fmaxf(fmaxf(acc[j][u][0], acc[j][u][1]), fmaxf(acc[j][u][2], acc[j][u][3])));
+                bmax[j] = wave_max16(bm);
+                if (grp == 0)
+                    xmax[kh * (T * 16) + (qt0 + j) * 16 + n16] = bmax[j];
             }
         }
-        lds_sync();   // B2: the PV waves start on block i - 1
-        uint32_t pk[NSUB];   // E4M3 P of this lane's 4 keys of each subtile
-        float alpha = 1.f;
+        lds_sync();   // B2: the PV waves start on block i - 1; the halves' maxima are published
+        uint32_t pk[TW][KS];   // E4M3 P of this lane's 4 keys of each subtile
+        float alpha[TW];
         if (work) {
-            // ---- visibility of this lane's 32 keys: bit 4u + j <-> key 16u + 4 grp + j ----
-            const int64_t kbase = w.first + (int64_t)i * BLK;
-            const int64_t lr = lim - kbase;      // keys of the block before the tile's bound
-            const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
-            const v4i mw = lds_read16(smem, L::OFF_KMASK + slot * 16);
-            uint32_t vis = 0;
 #pragma unroll
-            for (int u = 0; u < NSUB; u++) {
-                uint32_t nib = ((uint32_t)mw[u >> 1] >> (16 * (u & 1) + 4 * grp)) & 0xFu;
-                const int keep = lim_rel - (16 * u + 4 * grp);   // how many of the 4 are in bound
-                nib &= keep >= 4 ? 0xFu : (keep <= 0 ? 0u : ((1u << keep) - 1u));
-                vis |= nib << (4 * u);
+            for (int j = 0; j < TW; j++) {
+                // both halves combine the same two maxima (fmaxf is exact and symmetric)
+                const float other = xmax[(kh ^ 1) * (T * 16) + (qt0 + j) * 16 + n16];
+                const float bm = fmaxf(bmax[j], other) * row_scale[j];
+                const float m_new = fmaxf(m_run[j], bm);
+                alpha[j] = (m_run[j] == neg_inf) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
+                const float m_use = (m_new == neg_inf) ? 0.f : m_new;   // exp2(-inf - m_use) = 0
+                // ---- P = 448 exp2(s * scale - m) -> E4M3 (P <= 448: no clamp); this half's row
+                // sum of the unrounded P in a fixed order ----
+                float bsum = 0.f;
+#pragma unroll
+                for (int u = 0; u < KS; u++) {
+                    float pr[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; jj++)
+                        pr[jj] = ANCHOR * __builtin_amdgcn_exp2f(fmaf(acc[j][u][jj], row_scale[j], -m_use));
+                    int wp = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+                    pk[j][u] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], wp, true);
+                    bsum = bsum + (((pr[0] + pr[1]) + pr[2]) + pr[3]);
+                }
+                bsum = wave_sum16(bsum);
+                l_run[j] = l_run[j] * alpha[j] + bsum;
+                m_run[j] = m_new;
             }
-            // ---- mask, row max over the block (in-lane, then across the 4 k-groups). The row
-            // scale is positive, so max(s * scale) = scale * max(s) exactly. ----
-            float bmax = neg_inf;
-            if (!__all(vis == 0xFFFFFFFFu)) {
-#pragma unroll
-                for (int u = 0; u < NSUB; u++)
-#pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        acc[u][j] = ((vis >> (4 * u + j)) & 1u) ? acc[u][j] : neg_inf;
-            }
-#pragma unroll
-            for (int u = 0; u < NSUB; u++)
-                bmax = fmaxf(bmax, fmaxf(fmaxf(acc[u][0], acc[u][1]), fmaxf(acc[u][2], acc[u][3])));
-            bmax = wave_max16(bmax) * row_scale;
-            const float m_new = fmaxf(m_run, bmax);
-            alpha = (m_run == neg_inf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            const float m_use = (m_new == neg_inf) ? 0.f : m_new;   // exp2(-inf - m_use) = 0
-            // ---- P = 448 exp2(s * scale - m) -> E4M3 (P <= 448: no clamp); row sum of the
-            // unrounded P in a fixed order ----
-            float bsum = 0.f;
-#pragma unroll
-            for (int u = 0; u < NSUB; u++) {
-                float pr[4];
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    pr[j] = ANCHOR * __builtin_amdgcn_exp2f(fmaf(acc[u][j], row_scale, -m_use));
-                int wp = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
-                pk[u] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], wp, true);
-                bsum = bsum + (((pr[0] + pr[1]) + pr[2]) + pr[3]);
-            }
-            bsum = wave_sum16(bsum);
-            l_run = l_run * alpha + bsum;
-            m_run = m_new;
         }
         lds_sync();   // B3: the PV waves have taken P of block i - 1 into registers
         if (work) {
 #pragma unroll
-            for (int u = 0; u < NSUB; u++)
-                *reinterpret_cast<uint32_t*>(smem + L::OFF_P + qt * PTILE + n16 * PPITCH + 16 * u +
-                                             4 * grp) = pk[u];
-            if (grp == 0)
-                xalpha[qt * 16 + n16] = alpha;
+            for (int j = 0; j < TW; j++) {
+#pragma unroll
+                for (int u = 0; u < KS; u++)
+                    *reinterpret_cast<uint32_t*>(smem + L::OFF_P + (qt0 + j) * PTILE + n16 * PPITCH +
+                                                 16 * (KS * kh + u) + 4 * grp) = pk[j][u];
+                if (grp == 0 && kh == 0)
+                    xalpha[(qt0 + j) * 16 + n16] = alpha[j];
+            }
         }
     }
 
-    // ---- epilogue: (m, l) to the column owners, LSE ----
+    // ---- epilogue: m and the halves' sums to LDS; the row sum is half 0 + half 1 ----
     float* fm = reinterpret_cast<float*>(smem + L::OFF_FM);
-    float* fl = reinterpret_cast<float*>(smem + L::OFF_FL);
+    float* fl = reinterpret_cast<float*>(smem + L::OFF_FL);   // [2][T * 16]
     if (active && grp == 0) {
-        fm[qt * 16 + n16] = m_run;
-        fl[qt * 16 + n16] = l_run;
+#pragma unroll
+        for (int j = 0; j < TW; j++) {
+            if (kh == 0)
+                fm[(qt0 + j) * 16 + n16] = m_run[j];
+            fl[kh * (T * 16) + (qt0 + j) * 16 + n16] = l_run[j];
+        }
     }
     __syncthreads();   // E1
-    const int64_t orow = w.row_base + 16 * tile + n16;
-    if (p.S == 1) {
-        if (active && grp == 0)
-            p.lse[orow] = (l_run > 0.f) ? (m_run - LOG2_ANCHOR + log2f(l_run)) * LN2 : neg_inf;
+    if (!(active && grp == 0 && kh == 0))
         return;
-    }
-    if (active && grp == 0) {
-        p.ws_ml[(orow * p.S + w.s) * 2 + 0] = m_run;
-        p.ws_ml[(orow * p.S + w.s) * 2 + 1] = l_run;
+#pragma unroll
+    for (int j = 0; j < TW; j++) {
+        const int r = (qt0 + j) * 16 + n16;
+        const float l = fl[r] + fl[T * 16 + r];
+        const int64_t orow = w.row_base + 16 * (w.ts * T + qt0 + j) + n16;
+        if (w.count == 1) {
+            p.lse[orow] = (l > 0.f) ? (m_run[j] - LOG2_ANCHOR + log2f(l)) * LN2 : neg_inf;
+        } else {
+            const int64_t prow = (int64_t)w.slot * (T * 16) + r;
+            p.ws_ml[prow * 2 + 0] = m_run[j];
+            p.ws_ml[prow * 2 + 1] = l;
+        }
     }
 }
 
@@ -551,10 +806,12 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     };
     auto issue_block = [&](int blk) {   // this wave's 18 row DMAs of block blk
 #pragma unroll
-        for (int i = 0; i < 18; i++) {
-            const int sub = 2 * pw + i / 9;
-            const uint8_t* src = dma_src(rpt + (blk & 1) * BLK + 16 * sub, i % 9, lane);
-            dma16(src, lds_addr(smem + (blk & 1) * SLOT + sub * SUBB + 1024 * (i % 9)));
+        for (int h = 0; h < 2; h++) {
+            const int sub = 2 * pw + h;
+            const uint8_t* src[9];
+#pragma unroll
+            for (int i = 0; i < 9; i++) src[i] = dma_src(rpt + (blk & 1) * BLK + 16 * sub, i, lane);
+            dma_subtile(src, lds_addr(smem + (blk & 1) * SLOT + sub * SUBB));
         }
     };
     if (w.nblk > 0) {
@@ -625,11 +882,11 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     // ---- epilogue ----
     __syncthreads();   // E1: (m, l) of every row in LDS
     const float* fl = reinterpret_cast<const float*>(smem + L::OFF_FL);
-    if (p.S == 1) {
+    if (w.count == 1) {
         // o = BF16(O / l * k_scale); the single-split merge (weight exp2(0) = 1) is this exactly
 #pragma unroll
         for (int t = 0; t < T; t++) {
-            const float lt = fl[t * 16 + n16];
+            const float lt = fl[t * 16 + n16] + fl[T * 16 + t * 16 + n16];
             const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
 #pragma unroll
             for (int c = 0; c < 8; c++) {
@@ -648,89 +905,117 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         return;
     }
 #pragma unroll
-    for (int t = 0; t < T; t++) {
-        const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
+    for (int t = 0; t < T; t++)
 #pragma unroll
-        for (int c = 0; c < 8; c++) {
-            const int col = 128 * pw + 16 * c + 4 * grp;
-            *reinterpret_cast<v4f*>(p.ws_o + (orow * p.S + w.s) * LATENT + col) = O[t][c];
-        }
-    }
+        for (int c = 0; c < 8; c++)
+            *reinterpret_cast<v4f*>(p.ws_o + partial_o_offset<T>(w.slot, pw, t, c, lane)) = O[t][c];
 }
 
-// The last arriving split of a (group, tile set) merges the FP32 partials in split order.
+// The last arriving item of a (group, tile set) merges the group's FP32 partials in split order.
+// Thread (wave c, lane) owns column block c of every column quarter and tile for rows
+// 16 t + lane % 16: per contributor it weighs T rows and issues 4 T contiguous loads at once.
 template <int T>
 __device__ void merge_splits(const Params& p, const Work& w, int tid)
 {
     const float neg_inf = -INFINITY;
-    for (int item = tid; item < T * 16 * 32; item += THREADS) {
-        const int r = item >> 5;
-        const int c0 = (item & 31) * 16;
-        const int64_t orow = w.row_base + 16 * w.ts * T + r;
-        const float* ml = p.ws_ml + orow * p.S * 2;
-        float top = neg_inf;
-        for (int q = 0; q < p.S; q++) top = fmaxf(top, ml[2 * q]);
-        float total = 0.f;
-        float acc[16];
+    const int lane = tid & 63, c = tid >> 6;
+    const int n16 = lane & 15, grp = lane >> 4;
+    float top[T], total[T];
 #pragma unroll
-        for (int e = 0; e < 16; e++) acc[e] = 0.f;
-        if (top != neg_inf) {
-            for (int q = 0; q < p.S; q++) {
-                const float mq = ml[2 * q];
-                if (mq == neg_inf)
-                    continue;
-                const float wq = exp2f(mq - top);
-                total = total + wq * ml[2 * q + 1];
-                const v4f* src = reinterpret_cast<const v4f*>(p.ws_o + (orow * p.S + q) * LATENT + c0);
+    for (int t = 0; t < T; t++) {
+        top[t] = neg_inf;
+        total[t] = 0.f;
+    }
+    // the rows' top maxima (loads of four contributors in flight at a time)
+    for (int q0 = 0; q0 < w.count; q0 += 4) {
+        float mq[4][T];
 #pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    const v4f x4 = src[v];
+        for (int u = 0; u < 4; u++) {
+            const int64_t prow = (int64_t)contributor_slot(p, w, q0 + u < w.count ? q0 + u : q0) * (T * 16);
 #pragma unroll
-                    for (int e = 0; e < 4; e++) acc[4 * v + e] = acc[4 * v + e] + wq * x4[e];
-                }
-            }
+            for (int t = 0; t < T; t++)
+                mq[u][t] = q0 + u < w.count ? p.ws_ml[(prow + 16 * t + n16) * 2] : neg_inf;
         }
-        uint32_t bits[16];
 #pragma unroll
-        for (int e = 0; e < 16; e++) bits[e] = total > 0.f ? f32_to_bf16_rne(acc[e] / total * p.k_scale) : 0u;
-        v4i w0 = v4i{(int)(bits[0] | (bits[1] << 16)), (int)(bits[2] | (bits[3] << 16)),
-                     (int)(bits[4] | (bits[5] << 16)), (int)(bits[6] | (bits[7] << 16))};
-        v4i w1 = v4i{(int)(bits[8] | (bits[9] << 16)), (int)(bits[10] | (bits[11] << 16)),
-                     (int)(bits[12] | (bits[13] << 16)), (int)(bits[14] | (bits[15] << 16))};
-        *reinterpret_cast<v4i*>(p.o + orow * LATENT + c0) = w0;
-        *reinterpret_cast<v4i*>(p.o + orow * LATENT + c0 + 8) = w1;
-        if ((item & 31) == 0)
-            p.lse[orow] = total > 0.f ? (top - LOG2_ANCHOR + log2f(total)) * LN2 : neg_inf;
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int t = 0; t < T; t++) top[t] = fmaxf(top[t], mq[u][t]);
+    }
+    v4f acc[4][T];
+#pragma unroll
+    for (int pw = 0; pw < 4; pw++)
+#pragma unroll
+        for (int t = 0; t < T; t++) acc[pw][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // per contributor: its (m, l) for the T rows and its 4 T partial loads all issue before any
+    // use (one wait per contributor); two contributors are in flight at a time
+    struct Part {
+        v2f ml[T];
+        v4f x[4][T];
+    };
+    auto load_part = [&](int q, Part& pt) {
+        const int slot = contributor_slot(p, w, q);
+#pragma unroll
+        for (int t = 0; t < T; t++)
+            pt.ml[t] = *reinterpret_cast<const v2f*>(p.ws_ml + ((int64_t)slot * (T * 16) + 16 * t + n16) * 2);
+#pragma unroll
+        for (int pw = 0; pw < 4; pw++)
+#pragma unroll
+            for (int t = 0; t < T; t++)
+                pt.x[pw][t] = *reinterpret_cast<const v4f*>(p.ws_o + partial_o_offset<T>(slot, pw, t, c, lane));
+    };
+    auto add_part = [&](const Part& pt) {
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+            if (pt.ml[t][0] == neg_inf)
+                continue;   // an empty split (and a row with no key at all)
+            const float wq = exp2f(pt.ml[t][0] - top[t]);
+            total[t] = total[t] + wq * pt.ml[t][1];
+#pragma unroll
+            for (int pw = 0; pw < 4; pw++) acc[pw][t] = acc[pw][t] + wq * pt.x[pw][t];
+        }
+    };
+    int q = 0;
+    for (; q + 1 < w.count; q += 2) {
+        Part a, b;
+        load_part(q, a);
+        load_part(q + 1, b);
+        add_part(a);
+        add_part(b);
+    }
+    if (q < w.count) {
+        Part a;
+        load_part(q, a);
+        add_part(a);
+    }
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
+#pragma unroll
+        for (int pw = 0; pw < 4; pw++) {
+            uint32_t b[4] = {0u, 0u, 0u, 0u};
+            if (total[t] > 0.f) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) b[e] = f32_to_bf16_rne(acc[pw][t][e] / total[t] * p.k_scale);
+            }
+            const int col = 128 * pw + 16 * c + 4 * grp;
+            *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) =
+                v2i{(int)(b[0] | (b[1] << 16)), (int)(b[2] | (b[3] << 16))};
+        }
+        if (c == 0 && grp == 0)
+            p.lse[orow] = total[t] > 0.f ? (top[t] - LOG2_ANCHOR + log2f(total[t])) * LN2 : neg_inf;
     }
 }
 
-template <int T, bool DENSE>
-__global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
+// After a work item (all threads): for a split item, the arrival count and, by the last of the
+// group's items to arrive, the merge.
+template <int T>
+__device__ __forceinline__ void finish_item(const Params& p, uint8_t* smem, const Work& w, int tid)
 {
     using L = Smem<T>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
-    Work w;
-    if (!decode_work<DENSE>(p, w))
+    if (w.count == 1)
         return;
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    // waves 0..3: QK (tile = wave); waves 4..7: gather + PV (columns 128 (wave - 4) ..); wave i runs
-    // on SIMD i % 4, so each SIMD pairs one QK wave with one PV wave
-    if (wave < 4) {
-        qk_role<T, DENSE>(p, smem, w, wave, lane);
-    } else {
-        v4f O[T][8];
-#pragma unroll
-        for (int t = 0; t < T; t++)
-#pragma unroll
-            for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
-        pv_role<T, DENSE>(p, smem, w, wave - 4, lane, O);
-    }
-    if (p.S == 1)
-        return;
-    // S > 1: every thread's partial stores completed (vmcnt(0)) before the barrier; one thread then
-    // releases them at agent scope and counts this split in; the last arriver merges.
+    // a split item: every thread's partial stores completed (vmcnt(0)) before the barrier; one
+    // thread then releases them at agent scope and counts this item in; the last arriver merges.
     __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();   // E2
     int* misc = reinterpret_cast<int*>(smem + L::OFF_MISC);
@@ -739,7 +1024,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        misc[0] = (old == (uint32_t)(p.S - 1)) ? 1 : 0;
+        misc[0] = (old == (uint32_t)(w.count - 1)) ? 1 : 0;
     }
     __syncthreads();   // E3
     if (misc[0] == 0)
@@ -747,6 +1032,81 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
     merge_splits<T>(p, w, tid);
     if (tid == 0)
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+typedef const __attribute__((address_space(4))) Params kernarg_params;
+
+// The kernel's parameters read anew: the pointer to them (the first kernel argument) passes
+// through an empty asm, so the compiler cannot prove loads through it invariant across work items
+// and does not keep every value derived from them live across the item loop (it would run out
+// of scalar registers and spill).
+__device__ inline const Params& fresh_params()
+{
+    kernarg_params* k = (kernarg_params*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(k));
+    return *(const Params*)k;   // loads through it stay scalar (address-space inference)
+}
+
+template <int T, bool DENSE>
+__global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
+{
+    using L = Smem<T>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    // a unit's tile sets share one XCD (blockIdx % 8)
+    const int bid = blockIdx.x;
+    const int slotid = bid >> 3;
+    const int ts = slotid % p.tilesets;
+    const int unit = (slotid / p.tilesets) * 8 + (bid & 7);
+    if (unit >= p.units)
+        return;
+    // uniform plan: the one item (group unit % groups); balanced plan: the piece's groups in order
+    Span sp{unit % p.groups, unit % p.groups, 0, 0};
+    if (p.balanced)
+        sp = piece_span<DENSE>(p, smem, unit, tid, lane);
+    auto item = [&](const Params& pi, int g, int64_t pre, Work& w) {
+        if (pi.balanced)
+            balanced_item<DENSE>(pi, unit, ts, g, pre, sp, w);
+        else
+            decode_uniform<DENSE>(pi, unit, ts, w);
+    };
+    // waves 0..3: QK (tile = wave); waves 4..7: gather + PV (columns 128 (wave - 4) ..); wave i runs
+    // on SIMD i % 4, so each SIMD pairs one QK wave with one PV wave. Each role walks the items
+    // itself (same items, same barriers), so neither keeps the other's values live.
+    if (wave < 4) {
+        int64_t pre = sp.pre_lo;
+        for (int g = sp.g_lo; g <= sp.g_hi; g++) {
+            const Params& pi = fresh_params();
+            int li = lane;   // lane-derived offsets are recomputed per item, not kept live
+            asm volatile("" : "+v"(li));
+            Work w;
+            item(pi, g, pre, w);
+            pre += nblocks(w.n_grp);
+            qk_role<T, DENSE>(pi, smem, w, wave, li);
+            finish_item<T>(pi, smem, w, tid);
+            __syncthreads();   // the next item reuses every LDS area
+        }
+    } else {
+        int64_t pre = sp.pre_lo;
+        for (int g = sp.g_lo; g <= sp.g_hi; g++) {
+            const Params& pi = fresh_params();
+            Work w;
+            item(pi, g, pre, w);
+            pre += nblocks(w.n_grp);
+            v4f O[T][8];
+#pragma unroll
+            for (int t = 0; t < T; t++)
+#pragma unroll
+                for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+            int li = lane;
+            asm volatile("" : "+v"(li));
+            pv_role<T, DENSE>(pi, smem, w, wave - 4, li, O);
+            finish_item<T>(pi, smem, w, tid);
+            __syncthreads();
+        }
+    }
 }
 
 // ---- host side ------------------------------------------------------------------------------
@@ -762,18 +1122,27 @@ struct WsLayout {
     size_t cnt_bytes, ml_bytes, o_bytes, total;
 };
 
-WsLayout ws_layout(int B, int Q, int H, int S)
+// Partial rows: a uniform plan with S > 1 leaves every row once per split; a balanced plan with
+// more than one piece leaves at most two partials (of a tile set's rows) per piece and tile set.
+WsLayout ws_layout(int dense, int B, int Q, int H, const mla_plan_t& pl)
 {
     WsLayout w{};
-    if (S <= 1)
+    if (pl.splits <= 1)
         return w;
     const size_t rows = (size_t)B * Q * H;
+    const size_t rows_per_group = dense ? (size_t)Q * H : (size_t)H;
+    const size_t prows = pl.mode == MLA_SPLIT_BALANCED ? 2 * (size_t)pl.splits * rows_per_group
+                                                       : rows * (size_t)pl.splits;
     w.cnt_bytes = round_up(rows / 16 * sizeof(uint32_t), ALIGN_WS);
-    w.ml_bytes = round_up(rows * S * 2 * sizeof(float), ALIGN_WS);
-    w.o_bytes = round_up(rows * S * LATENT * sizeof(float), ALIGN_WS);
+    w.ml_bytes = round_up(prows * 2 * sizeof(float), ALIGN_WS);
+    w.o_bytes = round_up(prows * LATENT * sizeof(float), ALIGN_WS);
     w.total = w.cnt_bytes + w.ml_bytes + w.o_bytes;
     return w;
 }
+
+// Group count a balanced plan supports: the prefix sums of the groups' block counts (G + 1 int32)
+// are staged in the two LDS slots.
+constexpr int MAX_BALANCED_GROUPS = 2 * SLOT / 4 - 1;
 
 int choose_tiles(int tiles_per_group)
 {
@@ -784,21 +1153,31 @@ int choose_tiles(int tiles_per_group)
     return 1;
 }
 
-// Splits from shapes only: enough workgroups to cover the 256 CUs once (one workgroup fills a CU's
-// LDS), each with at least two 128-key blocks of its group's key capacity; every extra split adds
-// a partial per row and a merge.
-int choose_splits(int groups, int tilesets, int64_t max_keys)
+// A plan from shapes only. One workgroup fills a CU's LDS, so 256 workgroups cover the chip once.
+// Groups of at most two 128-key blocks: one workgroup per group and tile set (uniform, S = 1).
+// Longer groups: a balanced plan of 256 / tilesets pieces, which evens out ragged key counts; for
+// more groups than a balanced plan stages, uniform splits up to one workgroup per CU.
+mla_plan_t choose_plan(int groups, int tiles_per_group, int64_t max_keys)
 {
-    const int64_t wgs = (int64_t)groups * tilesets;
-    int64_t s = 256 / wgs;
+    mla_plan_t pl{};
+    pl.tiles = choose_tiles(tiles_per_group);
+    const int tilesets = tiles_per_group / pl.tiles;
+    if (max_keys <= 2 * BLK) {
+        pl.splits = 1;
+        pl.mode = MLA_SPLIT_UNIFORM;
+        return pl;
+    }
+    if (groups <= MAX_BALANCED_GROUPS && (int64_t)groups * ((max_keys + BLK - 1) / BLK) < INT32_MAX) {
+        pl.splits = 256 / tilesets > 1 ? 256 / tilesets : 1;
+        pl.mode = MLA_SPLIT_BALANCED;
+        return pl;
+    }
+    int64_t s = 256 / ((int64_t)groups * tilesets);
     const int64_t cap = max_keys / (2 * BLK);
-    if (s > cap)
-        s = cap;
-    if (s < 1)
-        s = 1;
-    if (s > 64)
-        s = 64;
-    return (int)s;
+    s = s > cap ? cap : s;
+    pl.splits = (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
+    pl.mode = MLA_SPLIT_UNIFORM;
+    return pl;
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -806,7 +1185,7 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 template <int T, bool DENSE>
 hipError_t launch_t(const Params& p, hipStream_t stream)
 {
-    const int64_t gs_pad = ((int64_t)p.gs_count + 7) / 8 * 8;
+    const int64_t gs_pad = ((int64_t)p.units + 7) / 8 * 8;
     const int64_t grid = gs_pad * p.tilesets;
     hipLaunchKernelGGL((mla_decode_kernel<T, DENSE>), dim3((unsigned)grid), dim3(THREADS), 0, stream,
                        p);
@@ -841,16 +1220,22 @@ mla_status_t common_checks(const void* q, const mla_kv_t* kv, int B, int Q, int 
     return MLA_OK;
 }
 
-mla_status_t finish_plan(const mla_plan_t* in, mla_plan_t chosen, int tiles_per_group, int B, int Q,
-                         int H, void* ws, size_t ws_bytes, mla_plan_t* out)
+mla_status_t finish_plan(const mla_plan_t* in, mla_plan_t chosen, int dense, int groups,
+                         int tiles_per_group, int64_t max_keys, int B, int Q, int H, void* ws,
+                         size_t ws_bytes, mla_plan_t* out)
 {
     mla_plan_t pl = in ? *in : chosen;
     if (pl.splits < 1 || pl.splits > 4096)
         return MLA_ERR_UNSUPPORTED;
     if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || tiles_per_group % pl.tiles != 0)
         return MLA_ERR_UNSUPPORTED;
+    if (pl.mode != MLA_SPLIT_UNIFORM && pl.mode != MLA_SPLIT_BALANCED)
+        return MLA_ERR_UNSUPPORTED;
+    if (pl.mode == MLA_SPLIT_BALANCED &&
+        (groups > MAX_BALANCED_GROUPS || (int64_t)groups * ((max_keys + BLK - 1) / BLK) >= INT32_MAX))
+        return MLA_ERR_UNSUPPORTED;
     if (pl.splits > 1) {
-        const WsLayout w = ws_layout(B, Q, H, pl.splits);
+        const WsLayout w = ws_layout(dense, B, Q, H, pl);
         if (!ws || ws_bytes < w.total)
             return MLA_ERR_WORKSPACE;
         if (!aligned(ws, ALIGN_WS))
@@ -860,9 +1245,9 @@ mla_status_t finish_plan(const mla_plan_t* in, mla_plan_t chosen, int tiles_per_
     return MLA_OK;
 }
 
-void fill_workspace(Params& p, int B, int Q, int H, void* ws)
+void fill_workspace(Params& p, int dense, int B, int Q, int H, const mla_plan_t& pl, void* ws)
 {
-    const WsLayout w = ws_layout(B, Q, H, p.S);
+    const WsLayout w = ws_layout(dense, B, Q, H, pl);
     uint8_t* base = (uint8_t*)ws;
     p.ws_cnt = p.S > 1 ? (uint32_t*)base : nullptr;
     p.ws_ml = p.S > 1 ? (float*)(base + w.cnt_bytes) : nullptr;
@@ -887,18 +1272,18 @@ const char* mla_status_string(mla_status_t status)
     return "unknown status";
 }
 
-size_t mla_workspace_bytes(int B, int Q, int H, int splits)
+size_t mla_workspace_bytes(int dense, int B, int Q, int H, const mla_plan_t* plan)
 {
-    if (B <= 0 || Q <= 0 || H <= 0)
+    if (B <= 0 || Q <= 0 || H <= 0 || !plan)
         return 0;
-    return ws_layout(B, Q, H, splits).total;
+    return ws_layout(dense, B, Q, H, *plan).total;
 }
 
-size_t mla_workspace_zero_bytes(int B, int Q, int H, int splits)
+size_t mla_workspace_zero_bytes(int dense, int B, int Q, int H, const mla_plan_t* plan)
 {
-    if (B <= 0 || Q <= 0 || H <= 0)
+    if (B <= 0 || Q <= 0 || H <= 0 || !plan)
         return 0;
-    return ws_layout(B, Q, H, splits).cnt_bytes;
+    return ws_layout(dense, B, Q, H, *plan).cnt_bytes;
 }
 
 mla_status_t mla_plan_dense(int B, int Q, int H, int max_pages, int page_size, mla_plan_t* plan)
@@ -907,9 +1292,7 @@ mla_status_t mla_plan_dense(int B, int Q, int H, int max_pages, int page_size, m
         return MLA_ERR_NULL;
     if (B < 0 || Q < 1 || H < 16 || H % 16 != 0 || max_pages < 1 || page_size < 1)
         return MLA_ERR_SHAPE;
-    const int tpg = Q * H / 16;
-    plan->tiles = choose_tiles(tpg);
-    plan->splits = choose_splits(B > 0 ? B : 1, tpg / plan->tiles, (int64_t)max_pages * page_size);
+    *plan = choose_plan(B > 0 ? B : 1, Q * H / 16, (int64_t)max_pages * page_size);
     return MLA_OK;
 }
 
@@ -919,9 +1302,7 @@ mla_status_t mla_plan_sparse(int B, int Q, int H, int K, mla_plan_t* plan)
         return MLA_ERR_NULL;
     if (B < 0 || Q < 1 || H < 16 || H % 16 != 0 || K < 1)
         return MLA_ERR_SHAPE;
-    const int tpg = H / 16;
-    plan->tiles = choose_tiles(tpg);
-    plan->splits = choose_splits(B > 0 ? B * Q : 1, tpg / plan->tiles, K);
+    *plan = choose_plan(B > 0 ? B * Q : 1, H / 16, K);
     return MLA_OK;
 }
 
@@ -942,7 +1323,8 @@ mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* 
     mla_plan_t chosen;
     mla_plan_dense(B, Q, H, max_pages, kv->page_size, &chosen);
     mla_plan_t pl;
-    st = finish_plan(plan, chosen, Q * H / 16, B, Q, H, workspace, workspace_bytes, &pl);
+    st = finish_plan(plan, chosen, 1, B, Q * H / 16, (int64_t)max_pages * kv->page_size, B, Q, H,
+                     workspace, workspace_bytes, &pl);
     if (st != MLA_OK)
         return st;
     Params p{};
@@ -958,13 +1340,14 @@ mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* 
     p.Q = Q;
     p.H = H;
     p.S = pl.splits;
+    p.balanced = pl.mode == MLA_SPLIT_BALANCED;
     p.groups = B;
     p.rows_per_group = Q * H;
     p.tilesets = Q * H / 16 / pl.tiles;
-    p.gs_count = B * pl.splits;
+    p.units = p.balanced ? pl.splits : B * pl.splits;
     p.o = (uint16_t*)o;
     p.lse = lse;
-    fill_workspace(p, B, Q, H, workspace);
+    fill_workspace(p, 1, B, Q, H, pl, workspace);
     if (launch<true>(pl.tiles, p, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_LAUNCH;
     return MLA_OK;
@@ -987,7 +1370,7 @@ mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t*
     mla_plan_t chosen;
     mla_plan_sparse(B, Q, H, K, &chosen);
     mla_plan_t pl;
-    st = finish_plan(plan, chosen, H / 16, B, Q, H, workspace, workspace_bytes, &pl);
+    st = finish_plan(plan, chosen, 0, B * Q, H / 16, K, B, Q, H, workspace, workspace_bytes, &pl);
     if (st != MLA_OK)
         return st;
     Params p{};
@@ -1003,13 +1386,14 @@ mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t*
     p.Q = Q;
     p.H = H;
     p.S = pl.splits;
+    p.balanced = pl.mode == MLA_SPLIT_BALANCED;
     p.groups = B * Q;
     p.rows_per_group = H;
     p.tilesets = H / 16 / pl.tiles;
-    p.gs_count = B * Q * pl.splits;
+    p.units = p.balanced ? pl.splits : B * Q * pl.splits;
     p.o = (uint16_t*)o;
     p.lse = lse;
-    fill_workspace(p, B, Q, H, workspace);
+    fill_workspace(p, 0, B, Q, H, pl, workspace);
     if (launch<false>(pl.tiles, p, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_LAUNCH;
     return MLA_OK;

@@ -13,6 +13,7 @@ import paged_mla_decode_fp8_amd as mla
 CHUNK = 128  # keys per block of the kernels: the oracle's chunk for METHOD mode
 O_RTOL = 2e-2
 LSE_ATOL = 1e-3
+UNIFORM, BALANCED = 0, 1   # plan modes of the C ABI
 
 
 def say(*args):
@@ -52,17 +53,49 @@ def as_f64(o: torch.Tensor) -> np.ndarray:
     return o.float().cpu().numpy().astype(np.float64)
 
 
-def run_oracle(x, splits, sel=None, mode=oracle.METHOD):
+def group_keys(x) -> np.ndarray:
+    """Key count of each key group: request b (dense, clamped to the table's capacity) or list
+    (b, i) in order b*Q+i (sparse, clamped to [0, K])."""
+    if x.kind == "dense":
+        cap = x.block_table.shape[1] * x.page_size
+        return np.clip(x.seq_lens.astype(np.int64), 0, cap)
+    return np.clip(x.valid.reshape(-1).astype(np.int64), 0, x.rows.shape[2])
+
+
+def balanced_cuts(x, pieces: int):
+    """Split starts per key group under the balanced plan, from its definition in the C header:
+    the groups' 128-key blocks in group order (U of them) are cut at global blocks
+    floor(p U / pieces), p = 1 .. pieces - 1; a group is split at every cut strictly inside it."""
+    nb = -(-group_keys(x) // CHUNK)
+    U = int(nb.sum())
+    cuts_global = sorted({p * U // pieces for p in range(1, pieces)})
+    out, pre = [], 0
+    for n in nb.tolist():
+        out.append([0] + [CHUNK * (b - pre) for b in cuts_global if pre < b < pre + n])
+        pre += n
+    return out
+
+
+def run_oracle(x, plan, sel=None, mode=oracle.METHOD):
+    """The oracle on the same inputs under the same split plan ((splits, tiles[, mode])): o, LSE
+    and the per-element rounding allowance (o may move by that much where a P lies within FP32
+    accuracy of an E4M3 rounding midpoint, so either rounding is correct)."""
+    plan = tuple(plan)
+    kw = {"splits": plan[0], "allowance": True}
+    if len(plan) > 2 and plan[2] == BALANCED:
+        kw = {"cuts": balanced_cuts(x, plan[0]), "allowance": True}
     if x.kind == "dense":
         return oracle.dense(x.q_bits, x.kv, x.page_size, x.k_scale, x.block_table, x.seq_lens,
-                            x.scale, mode=mode, splits=splits, chunk=CHUNK, sel=sel)
+                            x.scale, mode=mode, chunk=CHUNK, sel=sel, **kw)
     return oracle.sparse(x.q_bits, x.kv, x.k_scale, x.rows, x.valid, x.scale, mode=mode,
-                         splits=splits, chunk=CHUNK, sel=sel)
+                         chunk=CHUNK, sel=sel, **kw)
 
 
-def assert_parity(o_gpu: torch.Tensor, lse_gpu: torch.Tensor, o_ref, lse_ref, sel=None, what=""):
-    """max|do| <= 2e-2 max(1, |o|) per element, |dLSE| <= 1e-3, and rows with no key bit-exact
-    (o = +0.0, LSE = -inf)."""
+def assert_parity(o_gpu: torch.Tensor, lse_gpu: torch.Tensor, o_ref, lse_ref, amb=None, sel=None,
+                  what=""):
+    """max|do| <= 2e-2 max(1, |o|) per element (plus the oracle's rounding allowance, which may be
+    needed by few elements only), |dLSE| <= 1e-3, and rows with no key bit-exact (o = +0.0,
+    LSE = -inf)."""
     og = as_f64(o_gpu).reshape(-1, 512)
     lg = lse_gpu.cpu().numpy().astype(np.float64).reshape(-1)
     ob = bits(o_gpu).reshape(-1, 512)
@@ -75,9 +108,14 @@ def assert_parity(o_gpu: torch.Tensor, lse_gpu: torch.Tensor, o_ref, lse_ref, se
     assert np.all(ob[empty] == 0), f"{what}: empty rows must be +0.0"
     err = np.abs(og - o_ref)
     tol = O_RTOL * np.maximum(1.0, np.abs(o_ref))
-    bad = err > tol
+    allow = 0.0 if amb is None else np.asarray(amb).reshape(-1, 512)
+    bad = err > tol + allow
     assert not bad.any(), (f"{what}: {bad.sum()} o elements out of tolerance, max err "
                            f"{err.max():.4g} at {np.unravel_index(err.argmax(), err.shape)}")
+    used = int((err > tol).sum())
+    if used:
+        say(f"{what}: {used} elements within the rounding allowance only")
+    assert used <= max(8, err.size // 200), f"{what}: {used} elements need the rounding allowance"
     fin = ~empty
     if fin.any():
         lerr = np.abs(lg[fin] - lse_ref[fin])

@@ -58,7 +58,7 @@ def _sparse(q=0x1000, kv=None, rows=0x2000, K=8, valid=0x3000, B=2, Q=1, H=16, p
 
 
 def test_bad_arguments_return_status_without_launching():
-    P = lambda s, t: ctypes.byref(mla._Plan(s, t))  # noqa: E731
+    P = lambda s, t, m=0: ctypes.byref(mla._Plan(s, t, m))  # noqa: E731
     assert _dense(q=None) == NULL
     assert _dense(table=None) == NULL
     assert _dense(kv=_kv(ptr=0)) == NULL
@@ -74,9 +74,16 @@ def test_bad_arguments_return_status_without_launching():
     assert _dense(plan=P(1, 3)) == UNSUPPORTED
     assert _dense(plan=P(1, 2)) == UNSUPPORTED       # 1 row tile per group: tiles must divide it
     assert _dense(plan=P(2, 1)) == WORKSPACE         # splits > 1 need a workspace
-    need = mla.workspace_bytes(2, 1, 16, 2)
+    need = mla.workspace_bytes(True, 2, 1, 16, (2, 1))
     assert _dense(plan=P(2, 1), ws=0x10000, ws_bytes=need - 1) == WORKSPACE
     assert _dense(plan=P(2, 1), ws=0x10010, ws_bytes=need) == ALIGN
+    assert _dense(plan=P(1, 1, 2)) == UNSUPPORTED    # unknown mode
+    assert _dense(plan=P(3, 1, 1)) == WORKSPACE      # balanced with pieces > 1 needs one too
+    need = mla.workspace_bytes(True, 2, 1, 16, (3, 1, 1))
+    assert _dense(plan=P(3, 1, 1), ws=0x10000, ws_bytes=need - 1) == WORKSPACE
+    assert _sparse(B=36864, plan=P(2, 1, 1), ws=0x10000, ws_bytes=1 << 40) == UNSUPPORTED
+    assert _sparse(B=20000, K=1 << 24, plan=P(2, 1, 1), ws=0x10000, ws_bytes=1 << 40) == UNSUPPORTED
+    assert _dense(plan=P(4097, 1, 1)) == UNSUPPORTED
     assert _sparse(K=0) == SHAPE
     assert _sparse(valid=None) == NULL
     assert _sparse(rows=0x2002) == ALIGN
@@ -84,13 +91,20 @@ def test_bad_arguments_return_status_without_launching():
 
 
 def test_workspace_sizes_and_plans():
-    assert mla.workspace_bytes(4, 5, 16, 1) == 0
-    assert mla.workspace_zero_bytes(4, 5, 16, 1) == 0
-    n = mla.workspace_bytes(4, 5, 16, 3)
-    z = mla.workspace_zero_bytes(4, 5, 16, 3)
-    rows = 4 * 5 * 16
-    assert 0 < z < n and z % 256 == 0 and n % 256 == 0
-    assert n >= rows * 3 * (512 + 2) * 4 + rows // 16 * 4
+    for dense in (True, False):
+        assert mla.workspace_bytes(dense, 4, 5, 16, (1, 1)) == 0
+        assert mla.workspace_zero_bytes(dense, 4, 5, 16, (1, 1)) == 0
+        assert mla.workspace_bytes(dense, 4, 5, 16, (1, 1, 1)) == 0
+        n = mla.workspace_bytes(dense, 4, 5, 16, (3, 1))
+        z = mla.workspace_zero_bytes(dense, 4, 5, 16, (3, 1))
+        rows = 4 * 5 * 16
+        assert 0 < z < n and z % 256 == 0 and n % 256 == 0
+        assert n >= rows * 3 * (512 + 2) * 4 + rows // 16 * 4
+        # balanced: at most two partials per piece, each of a key group's rows
+        nb = mla.workspace_bytes(dense, 4, 5, 16, (7, 1, 1))
+        rows_per_group = 5 * 16 if dense else 16
+        assert nb >= 2 * 7 * rows_per_group * (512 + 2) * 4 + rows // 16 * 4
+        assert mla.workspace_zero_bytes(dense, 4, 5, 16, (7, 1, 1)) == z
     for B, Q, H, K in ((2, 1, 16, 64), (4, 5, 16, 256), (32, 5, 64, 2048)):
         p = mla.plan_sparse(B, Q, H, K)
         assert p.splits >= 1 and p.tiles in (1, 2, 4) and (H // 16) % p.tiles == 0
@@ -114,4 +128,4 @@ def test_chooser_picks_the_benchmark_plans():
     for name, (kind, B, Q, H, n) in shapes.items():
         p = mla.plan_dense(B, Q, H, n, 64) if kind == "dense" else mla.plan_sparse(B, Q, H, n)
         w = wl.WORKLOADS[name]
-        assert (p.splits, p.tiles) == (w.splits, w.tiles), name
+        assert (p.splits, p.tiles, p.mode) == w.plan, name

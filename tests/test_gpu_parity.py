@@ -6,29 +6,29 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import (assert_parity, bits, run_gpu, run_oracle, say, upload)
+from gpu_util import (BALANCED, assert_parity, bits, run_gpu, run_oracle, say, upload)
 
 pytestmark = pytest.mark.gpu
 
 
-def _parity(x, splits, tiles, what, sel=None):
-    say(what, x.kind, "B,Q,H =", x.B, x.Q, x.H, "plan", (splits, tiles))
+def _parity(x, plan, what, sel=None):
+    say(what, x.kind, "B,Q,H =", x.B, x.Q, x.H, "plan", plan)
     dev = upload(x)
-    o, lse = run_gpu(x, dev, (splits, tiles))
-    o_ref, lse_ref = run_oracle(x, splits, sel=sel)
-    return assert_parity(o, lse, o_ref, lse_ref, sel=sel, what=what), o, lse
+    o, lse = run_gpu(x, dev, plan)
+    o_ref, lse_ref, amb = run_oracle(x, plan, sel=sel)
+    return assert_parity(o, lse, o_ref, lse_ref, amb, sel=sel, what=what), o, lse
 
 
 # ---- the small named workloads, whole ----------------------------------------------------------
 
 @pytest.mark.parametrize("splits", [1, 2, 3])
 def test_tiny_sparse(splits):
-    _parity(wl.tiny_sparse(), splits, 1, f"tiny_sparse S={splits}")
+    _parity(wl.tiny_sparse(), (splits, 1), f"tiny_sparse S={splits}")
 
 
 @pytest.mark.parametrize("splits", [1, 2, 4])
 def test_latency_sparse(splits):
-    _parity(wl.latency_sparse(), splits, 1, f"latency_sparse S={splits}")
+    _parity(wl.latency_sparse(), (splits, 1), f"latency_sparse S={splits}")
 
 
 # ---- shape fuzz: ragged counts around the 16-key subtile and 128-key block ---------------------
@@ -50,7 +50,7 @@ def test_sparse_fuzz(case):
     B, Q, H, K, valid, N, plan = SPARSE_CASES[case]
     valid = np.array(valid, np.int32).reshape(-1)[: B * Q].reshape(B, Q)
     x = wl.sparse_case(B, Q, H, K, valid, N, seed=500 + case)
-    _parity(x, plan[0], plan[1], f"sparse fuzz {case}")
+    _parity(x, plan, f"sparse fuzz {case}")
 
 
 DENSE_CASES = [
@@ -69,7 +69,7 @@ DENSE_CASES = [
 def test_dense_fuzz(case):
     B, Q, H, seq, ps, plan = DENSE_CASES[case]
     x = wl.dense_case(B, Q, H, seq, page_size=ps, seed=600 + case, extra_pages=3)
-    _parity(x, plan[0], plan[1], f"dense fuzz {case}")
+    _parity(x, plan, f"dense fuzz {case}")
 
 
 # ---- exact properties ----------------------------------------------------------------------
@@ -184,7 +184,72 @@ def test_absent_keys_and_clamped_counts_match_oracle():
     x = wl.sparse_case(2, 2, 16, 200, [[10**6, -3], [150, 200]], 1000, seed=1200)
     x.rows[1, 0, [0, 5, 149]] = [-1, 1000, 2**31 - 1]
     x.rows[1, 1, 100:120] = -7
-    _parity(x, 2, 1, "absent keys")
+    _parity(x, (2, 1), "absent keys")
+    _parity(x, (3, 1, BALANCED), "absent keys, balanced")
+
+
+# ---- balanced plans: pieces over the call's concatenated blocks ---------------------------------
+
+BALANCED_SPARSE = [
+    # B, Q, H, K, valid pattern, cache rows, plan (pieces, tiles)
+    # more pieces than blocks: empty pieces, every group cut into several items
+    (1, 3, 16, 300, [[300, 129, 1]], 2000, (16, 1)),
+    # many short groups per piece, empty groups at the start, middle and end
+    (4, 5, 32, 200, [[0, 5, 17, 128, 129], [0, 0, 200, 1, 64], [3, 0, 0, 77, 150],
+                     [200, 199, 2, 0, 0]], 3000, (3, 2)),
+    # a few long groups over many pieces, tile sets of 4
+    (2, 2, 64, 1500, [[1500, 700], [1, 1200]], 9000, (9, 4)),
+    # every group empty
+    (2, 2, 16, 50, [[0, 0], [0, 0]], 100, (4, 1)),
+    # one piece: the whole call in one workgroup per tile set, no partials
+    (3, 1, 16, 400, [[400], [129], [0]], 2000, (1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BALANCED_SPARSE)))
+def test_balanced_sparse(case):
+    B, Q, H, K, valid, N, plan = BALANCED_SPARSE[case]
+    valid = np.array(valid, np.int32).reshape(B, Q)
+    x = wl.sparse_case(B, Q, H, K, valid, N, seed=1300 + case)
+    _parity(x, (plan[0], plan[1], BALANCED), f"balanced sparse {case}")
+
+
+BALANCED_DENSE = [
+    # B, Q, H, seq_lens, page_size, plan (pieces, tiles)
+    (5, 1, 16, [700, 3, 129, 0, 1300], 64, (7, 1)),
+    (3, 4, 32, [2000, 5, 900], 16, (11, 4)),
+    (6, 2, 16, [128, 256, 1, 0, 513, 384], 32, (4, 2)),
+    (1, 2, 128, [3000], 64, (6, 4)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BALANCED_DENSE)))
+def test_balanced_dense(case):
+    B, Q, H, seq, ps, plan = BALANCED_DENSE[case]
+    x = wl.dense_case(B, Q, H, seq, page_size=ps, seed=1400 + case, extra_pages=2)
+    _parity(x, (plan[0], plan[1], BALANCED), f"balanced dense {case}")
+
+
+def test_balanced_determinism_and_tiles_invariance():
+    x = wl.sparse_case(3, 2, 64, 900, [[900, 13], [0, 640], [257, 899]], 5000, seed=1500)
+    dev = upload(x)
+    ref = run_gpu(x, dev, (5, 1, BALANCED))
+    for plan in ((5, 1, BALANCED), (5, 2, BALANCED), (5, 4, BALANCED)):
+        o, lse = run_gpu(x, dev, plan)
+        assert np.array_equal(bits(o), bits(ref[0])), plan
+        assert np.array_equal(lse.cpu().numpy().view(np.uint32),
+                              ref[1].cpu().numpy().view(np.uint32)), plan
+
+
+def test_balanced_one_piece_per_group_equals_uniform_single_split():
+    """Groups of equal block counts and as many pieces as groups: every piece is one whole group,
+    the same work as the uniform plan with one split (bit-equal)."""
+    x = wl.sparse_case(2, 3, 32, 256, [[256, 200, 129], [250, 160, 255]], 4000, seed=1600)
+    dev = upload(x)
+    u = run_gpu(x, dev, (1, 2))
+    b = run_gpu(x, dev, (6, 2, BALANCED))
+    assert np.array_equal(bits(u[0]), bits(b[0]))
+    assert np.array_equal(u[1].cpu().numpy(), b[1].cpu().numpy())
 
 
 # ---- full-size named workloads, sampled rows ---------------------------------------------------
@@ -199,7 +264,7 @@ def test_full_size_workloads_sampled(name):
     if name == "topk_sparse":
         empty = np.flatnonzero(x.valid.reshape(-1) == 0)[:2]
         sel = np.unique(np.concatenate([sel, empty * x.H, empty * x.H + x.H - 1]))
-    _parity(x, w.splits, w.tiles, f"{name} sampled", sel=sel)
+    _parity(x, w.plan, f"{name} sampled", sel=sel)
 
 
 def test_workspace_reused_across_shapes_with_zero_prefix_contract():
@@ -208,16 +273,18 @@ def test_workspace_reused_across_shapes_with_zero_prefix_contract():
     import paged_mla_decode_fp8_amd as mla
     a = wl.latency_sparse()
     b = wl.sparse_case(2, 2, 32, 129, [[127, 128], [129, 31]], 500, seed=502)
-    need = max(mla.workspace_bytes(4, 5, 16, 4), mla.workspace_bytes(2, 2, 32, 3))
+    plans = ((a, (4, 1)), (b, (3, 2)), (a, (4, 1)), (b, (5, 1, BALANCED)), (a, (7, 1, BALANCED)))
+    need = max(mla.workspace_bytes(False, x.B, x.Q, x.H, plan) for x, plan in plans)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
-    for x, plan in ((a, (4, 1)), (b, (3, 2)), (a, (4, 1))):
+    for x, plan in plans:
         say("workspace reuse", x.B, x.Q, x.H, plan)
-        ws[: mla.workspace_zero_bytes(x.B, x.Q, x.H, plan[0])].zero_()
+        zero = mla.workspace_zero_bytes(False, x.B, x.Q, x.H, plan)
+        ws[:zero].zero_()
         dev = upload(x)
         o, lse = mla.sparse(dev["q"], dev["kv"], dev["rows"], dev["valid"], x.scale, x.k_scale,
                             plan=plan, workspace=ws)
         torch.cuda.synchronize()
-        o_ref, lse_ref = run_oracle(x, plan[0])
-        assert_parity(o, lse, o_ref, lse_ref, what="workspace reuse")
+        o_ref, lse_ref, amb = run_oracle(x, plan)
+        assert_parity(o, lse, o_ref, lse_ref, amb, what="workspace reuse")
         # the call left its counter prefix zero
-        assert int(ws[: mla.workspace_zero_bytes(x.B, x.Q, x.H, plan[0])].count_nonzero()) == 0
+        assert int(ws[:zero].count_nonzero()) == 0

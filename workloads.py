@@ -203,20 +203,25 @@ def long_dense(seed=1004) -> Inputs:
 class Workload:
     name: str
     make: object
-    splits: int      # the split plan the benchmark launches
+    splits: int      # the plan the benchmark launches: splits (uniform) or pieces (balanced)
     tiles: int       # 16-row tiles per workgroup
+    mode: int        # 0: uniform splits per key group, 1: balanced pieces over the call's blocks
     description: str
+
+    @property
+    def plan(self):
+        return (self.splits, self.tiles, self.mode)
 
 
 WORKLOADS = {
-    "tiny_sparse": Workload("tiny_sparse", tiny_sparse, 1, 1,
+    "tiny_sparse": Workload("tiny_sparse", tiny_sparse, 1, 1, 0,
                             "sparse B=2 Q=1 H=16, 64 of 128 rows, one row empty"),
-    "dense_paged": Workload("dense_paged", dense_paged, 2, 4,
+    "dense_paged": Workload("dense_paged", dense_paged, 128, 4, 1,
                             "dense B=64 Q=1 H=128 page 64 seq_len U[1024,8192]"),
-    "latency_sparse": Workload("latency_sparse", latency_sparse, 1, 1,
+    "latency_sparse": Workload("latency_sparse", latency_sparse, 1, 1, 0,
                                "sparse B=4 Q=5 H=16 valid U[200,256] of a 65536-row cache"),
-    "topk_sparse": Workload("topk_sparse", topk_sparse, 1, 4,
+    "topk_sparse": Workload("topk_sparse", topk_sparse, 256, 4, 1,
                             "sparse B=32 Q=5 H=64 top-k 2048 over 32768 positions, 5% empty"),
-    "long_dense": Workload("long_dense", long_dense, 4, 4,
+    "long_dense": Workload("long_dense", long_dense, 32, 4, 1,
                            "dense causal B=8 Q=4 H=128 seq_len 131072 page 64"),
 }
