@@ -111,8 +111,7 @@ struct Smem {
     static constexpr int OFF_XMAX = OFF_FL + 2 * T * 16 * 4;   // float [2][T*16] block maxima
     static constexpr int OFF_KMASK = OFF_XMAX + 2 * T * 16 * 4; // uint32 [2][4] key presence bits
     static constexpr int OFF_IDX = OFF_KMASK + 2 * 16;         // int32 [2][BLK] raw key indices
-    static constexpr int OFF_RP = OFF_IDX + 2 * BLK * 4;       // uint64 [2][BLK] key row pointers
-    static constexpr int OFF_MISC = OFF_RP + 2 * BLK * 8;      // int [4]
+    static constexpr int OFF_MISC = OFF_IDX + 2 * BLK * 4;     // int [4]
     static constexpr int BYTES = OFF_MISC + 16;
 };
 static_assert(Smem<4>::BYTES <= 163840, "LDS budget");
@@ -204,48 +203,6 @@ __device__ inline void dma16(const uint8_t* gsrc, uint32_t lds_base)
         : "memory");
 }
 
-// The nine row DMAs of one 16-key subtile: instruction i moves 16 bytes at this lane's src[i] to
-// LDS byte lds_base + 1024 i + 16 lane. One asm block steps M0 itself, so the destinations cost one
-// scalar register instead of nine (the compiler would keep all of them live).
-__device__ inline void dma_subtile(const uint8_t* const (&src)[9], uint32_t lds_base)
-{
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %4, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %5, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %6, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %7, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %8, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %9, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %10, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_base), "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3]), "v"(src[4]),
-          "v"(src[5]), "v"(src[6]), "v"(src[7]), "v"(src[8])
-        : "memory", "scc");
-}
-
 // One global_load_lds_dword: 4 bytes at this lane's gsrc -> LDS byte lds_base + 4 * lane (asm
 // for the same reasons as dma16).
 __device__ inline void dma4(const void* gsrc, uint32_t lds_base)
@@ -284,18 +241,6 @@ __device__ inline int64_t key_row(const Params& p, int64_t jabs, bool inrange, i
         }
     }
     return (row >= 0 && row < p.num_rows) ? row : -1;
-}
-
-// Source address of DMA instruction i (0..8) of a subtile for this lane, from the row pointers of
-// the subtile's 16 keys (rp: 16 x u64 in LDS). Latent instruction i: key 2i + lane / 32, chunk
-// (lane % 32) ^ key; rope instruction 8: key lane % 16, chunk 32 + lane / 16.
-__device__ inline const uint8_t* dma_src(const uint64_t* rp, int i, int lane)
-{
-    if (i < 8) {
-        const int k = 2 * i + (lane >> 5);
-        return reinterpret_cast<const uint8_t*>(rp[k]) + 16 * ((lane & 31) ^ k);
-    }
-    return reinterpret_cast<const uint8_t*>(rp[lane & 15]) + 512 + 16 * (lane >> 4);
 }
 
 // One work item of a workgroup: tile set ts of key group g, the group's keys
@@ -490,6 +435,24 @@ __device__ inline int64_t partial_o_offset(int slot, int pw, int t, int c, int l
     return ((((int64_t)slot * 4 + pw) * T + t) * 8 + c) * 256 + 4 * lane;
 }
 
+// Q staging: the tile set's T * 16 query rows (bf16, 1152 B each) are DMA'd by the QK waves into
+// KV slot 1, which stays free until iteration 0 issues the DMA of block 1. LDS unit (16 bytes)
+// 72 r + c of row r holds the row's unit c ^ s(r) for the latent units c < 64, s(r) = (r / 2) % 4
+// (so that the 16 rows read at one unit offset spread over the banks), and unit c for the rope
+// units 64..71.
+template <int T>
+__device__ inline void stage_q(const Params& p, uint8_t* smem, const Work& w, int qw, int lane)
+{
+    const uint8_t* qbase =
+        reinterpret_cast<const uint8_t*>(p.q + (w.row_base + 16 * w.ts * T) * ROW);
+    for (int i = qw; i < T * 18; i += 4) {   // 64 units per instruction, T * 16 * 72 units
+        const int u = 64 * i + lane;
+        const int r = u / 72, c = u - 72 * r;
+        const int src = c < 64 ? (c ^ ((r >> 1) & 3)) : c;
+        dma16(qbase + (int64_t)r * (2 * ROW) + 16 * src, lds_addr(smem + SLOT + 1024 * i));
+    }
+}
+
 // ---- QK waves: Q stage, S^T = K (hi + lo)^T, softmax; P and the rescale factors to LDS ----
 // QK wave qw owns key half kh = qw % 2 (subtiles 4 kh .. 4 kh + 3 of every block) of the tile pair
 // qw / 2: each K fragment read from LDS feeds the MFMAs of both tiles. The two halves of a tile's
@@ -508,46 +471,52 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     const int kh = qw & 1;
     const bool active = (qw >> 1) * TW < T;
     const int qt0 = active ? (qw >> 1) * TW : 0;   // first tile of the pair within the tile set
-    int64_t lim[TW];   // keys [0, lim) of the group are visible to tile j
+    int lim[TW];   // keys [first, first + lim) of the item are visible to tile j (lim may be < 0)
 #pragma unroll
     for (int j = 0; j < TW; j++) {
+        int64_t c = w.n_grp;
         if (DENSE) {
             const int pos = (16 * (w.ts * T + qt0 + j)) / p.H;
-            const int64_t c = w.n_grp - p.Q + pos + 1;
-            lim[j] = c < 0 ? 0 : (c > w.n_grp ? w.n_grp : c);
-        } else {
-            lim[j] = w.n_grp;
+            c = w.n_grp - p.Q + pos + 1;
+            c = c < 0 ? 0 : (c > w.n_grp ? w.n_grp : c);
         }
+        lim[j] = (int)(c - w.first);   // |c - first| <= n_grp < 2^31
     }
 
-    // ---- Q of the tiles -> exact E4M3 hi + lo of q * 2^k (B operands) ----
+    if (w.nblk > 0)
+        stage_q<T>(p, smem, w, qw, lane);
+    __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's Q rows landed
+    lds_sync();                          // Q0: every staged row landed
+
+    // ---- Q of the tiles -> exact E4M3 hi + lo of q * 2^k (B operands), from the staged copy in
+    // KV slot 1 (stage_q). Two passes over LDS (the row maximum, then the split), so no more than
+    // one operand step of raw values is live at a time. ----
     v8i qhi[TW][4], qlo[TW][4], qrope[TW];
     float row_scale[TW];  // scale_log2 * 2^-k for row n16
 #pragma unroll
     for (int j = 0; j < TW; j++) {
         row_scale[j] = 0.f;
         if (w.nblk > 0 && active) {
-            const uint16_t* qrow = p.q + (w.row_base + 16 * (w.ts * T + qt0 + j) + n16) * ROW;
-            // 32 bf16 per operand step st: values q[128 st + 32 grp + 0..31] (rope: 512 + 32 (grp & 1))
-            v4i raw[10], rawb[10];
-#pragma unroll
-            for (int st = 0; st < 5; st++) {
-                const uint16_t* src = st < 4 ? qrow + 128 * st + 32 * grp : qrow + 512 + 32 * (grp & 1);
-                raw[2 * st] = *reinterpret_cast<const v4i*>(src);
-                raw[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 8);
-                rawb[2 * st] = *reinterpret_cast<const v4i*>(src + 16);
-                rawb[2 * st + 1] = *reinterpret_cast<const v4i*>(src + 24);
-            }
+            const int r = 16 * (qt0 + j) + n16;   // row within the tile set
+            const uint8_t* qrow = smem + SLOT + r * (2 * ROW);
+            const int sw = (r >> 1) & 3;
+            // operand step st: values q[128 st + 32 grp + 0..31] (rope: 512 + 32 (grp & 1) + 0..31),
+            // 16-byte units 16 st + 4 grp + e (rope: 64 + 4 (grp & 1) + e), e = 0..3
+            auto unit = [&](int st, int e) {
+                const int c = st < 4 ? ((16 * st + 4 * grp + e) ^ sw) : (64 + 4 * (grp & 1) + e);
+                return *reinterpret_cast<const v4i*>(qrow + 16 * c);
+            };
             float amax = 0.f;
 #pragma unroll
-            for (int i = 0; i < 10; i++) {
+            for (int st = 0; st < 5; st++) {
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const uint32_t wa = (uint32_t)raw[i][e], wb = (uint32_t)rawb[i][e];
-                    amax = fmaxf(amax, fabsf(bf16_to_f32(wa & 0xFFFF)));
-                    amax = fmaxf(amax, fabsf(bf16_to_f32(wa >> 16)));
-                    amax = fmaxf(amax, fabsf(bf16_to_f32(wb & 0xFFFF)));
-                    amax = fmaxf(amax, fabsf(bf16_to_f32(wb >> 16)));
+                    const v4i u = unit(st, e);
+#pragma unroll
+                    for (int d = 0; d < 4; d++) {
+                        amax = fmaxf(amax, fabsf(bf16_to_f32((uint32_t)u[d] & 0xFFFF)));
+                        amax = fmaxf(amax, fabsf(bf16_to_f32((uint32_t)u[d] >> 16)));
+                    }
                 }
             }
             amax = wave_max16(amax);
@@ -573,21 +542,18 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
             };
 #pragma unroll
             for (int st = 0; st < 5; st++) {
-                // dword e of the operand holds values 4e..4e+3
-                const uint32_t wd[16] = {
-                    (uint32_t)raw[2 * st][0], (uint32_t)raw[2 * st][1], (uint32_t)raw[2 * st][2],
-                    (uint32_t)raw[2 * st][3], (uint32_t)raw[2 * st + 1][0], (uint32_t)raw[2 * st + 1][1],
-                    (uint32_t)raw[2 * st + 1][2], (uint32_t)raw[2 * st + 1][3], (uint32_t)rawb[2 * st][0],
-                    (uint32_t)rawb[2 * st][1], (uint32_t)rawb[2 * st][2], (uint32_t)rawb[2 * st][3],
-                    (uint32_t)rawb[2 * st + 1][0], (uint32_t)rawb[2 * st + 1][1],
-                    (uint32_t)rawb[2 * st + 1][2], (uint32_t)rawb[2 * st + 1][3]};
+                // dword e of the operand holds values 4e..4e+3: unit e / 2, dwords 2 (e % 2), + 1
                 v8i vh, vl;
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
+                for (int e2 = 0; e2 < 4; e2++) {
+                    const v4i u = unit(st, e2);
                     uint32_t h, l;
-                    split4(wd[2 * e], wd[2 * e + 1], h, l);
-                    vh[e] = (int)h;
-                    vl[e] = (int)l;
+                    split4((uint32_t)u[0], (uint32_t)u[1], h, l);
+                    vh[2 * e2] = (int)h;
+                    vl[2 * e2] = (int)l;
+                    split4((uint32_t)u[2], (uint32_t)u[3], h, l);
+                    vh[2 * e2 + 1] = (int)h;
+                    vl[2 * e2 + 1] = (int)l;
                 }
                 if (st < 4) {
                     qhi[j][st] = vh;
@@ -599,11 +565,14 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         }
     }
 
-    // this lane's LDS byte offset within a subtile of its operand read (step st, half h)
-    auto koff = [&](int st, int h) {
-        return st < 4 ? 16 * (32 * n16 + ((8 * st + 2 * grp + h) ^ n16))
-                      : 16 * (512 + 16 * (2 * (grp & 1) + h) + n16);
-    };
+    // This lane's LDS byte offset within a key half of a slot for its operand read of step st,
+    // half h, subtile u: u * SUBB + koff. For the latent steps koff = 16 (32 n16 + ((8 st + 2 grp
+    // + h) ^ n16)) = ka_h ^ (128 st), with ka_h = 512 n16 + 128 (n16 >> 3) + 16 ((2 grp + h) ^
+    // (n16 & 7)) (the bits of 128 st meet only the 128 (n16 >> 3) term). Rope: 8192 + 256 (2 (grp
+    // & 1) + h) + 16 n16.
+    const int ka0 = 512 * n16 + 128 * (n16 >> 3) + 16 * ((2 * grp) ^ (n16 & 7));
+    const int ka1 = 512 * n16 + 128 * (n16 >> 3) + 16 * ((2 * grp + 1) ^ (n16 & 7));
+    const int kr0 = 8192 + 256 * (2 * (grp & 1)) + 16 * n16;
     const float neg_inf = -INFINITY;
     float m_run[TW], l_run[TW];   // running max (log2 units) and this half's running sum, row n16
 #pragma unroll
@@ -623,7 +592,18 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         float bmax[TW];
         uint32_t vis[TW];
         if (work) {
-            const uint8_t* kslot = smem + slot * SLOT + (KS * kh) * SUBB;
+            // presence bits of the block's keys, read before the MFMAs so that the LDS latency
+            // hides behind them; this lane's 16 keys: bit 4u + jj <-> key 16 (4 kh + u) + 4 grp + jj
+            const v2i mw = *reinterpret_cast<const v2i*>(smem + L::OFF_KMASK + slot * 16 + 8 * kh);
+            const uint8_t* kslot = smem;
+            // the lane's bases for this slot and key half (kept out of the loop-invariant set so
+            // that they are recomputed here rather than held in registers across the loop)
+            int kb0 = ka0, kb1 = ka1, kbr = kr0;
+            asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(kbr));
+            const int soff = slot * SLOT + (KS * kh) * SUBB;
+            kb0 += soff;
+            kb1 += soff;
+            kbr += soff;
 #pragma unroll
             for (int j = 0; j < TW; j++)
 #pragma unroll
@@ -636,8 +616,10 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
             v8i kf[RING];
             auto load_frag = [&](int f) {
                 const int st = f / KS, sub = f % KS;
-                return cat(lds_read16(kslot, sub * SUBB + koff(st, 0)),
-                           lds_read16(kslot, sub * SUBB + koff(st, 1)));
+                if (st < 4)
+                    return cat(lds_read16(kslot, (kb0 ^ (128 * st)) + sub * SUBB),
+                               lds_read16(kslot, (kb1 ^ (128 * st)) + sub * SUBB));
+                return cat(lds_read16(kslot, kbr + sub * SUBB), lds_read16(kslot, kbr + 256 + sub * SUBB));
             };
 #pragma unroll
             for (int f = 0; f < AHEAD; f++) kf[f % RING] = load_frag(f);
@@ -658,20 +640,17 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                         acc[j][sub] = mfma(kf[(f - 1) % RING], qlo[j][st], acc[j][sub]);
                 }
             }
-            // ---- visibility of this lane's 16 keys: bit 4u + jj <-> key 16 (4 kh + u) + 4 grp + jj
-            const int64_t kbase = w.first + (int64_t)i * BLK;
-            const v4i mw = lds_read16(smem, L::OFF_KMASK + slot * 16);
             uint32_t present = 0;
 #pragma unroll
             for (int u = 0; u < KS; u++) {
-                const int sg = KS * kh + u;
-                present |= (((uint32_t)mw[sg >> 1] >> (16 * (sg & 1) + 4 * grp)) & 0xFu) << (4 * u);
+                // subtile 4 kh + u: word 2 kh + u / 2 of the block, half u % 2
+                present |= (((uint32_t)mw[u >> 1] >> (16 * (u & 1) + 4 * grp)) & 0xFu) << (4 * u);
             }
             // ---- mask, this half's block maxima (in-lane, then across the 4 k-groups), to LDS.
             // The row scale is positive, so max(s * scale) = scale * max(s) exactly. ----
 #pragma unroll
             for (int j = 0; j < TW; j++) {
-                const int64_t lr = lim[j] - kbase;    // keys of the block before the tile's bound
+                const int lr = lim[j] - i * BLK;      // keys of the block before the tile's bound
                 const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
                 vis[j] = present;
 #pragma unroll
@@ -781,9 +760,9 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     // Gather: this wave moves keys 32 pw .. 32 pw + 31 (subtiles 2 pw, 2 pw + 1) of every block.
     // Per block: the raw indices (page ids or row ids) arrive in an LDS slot by DMA one block
     // earlier; lanes 0..31 turn them into row pointers (the zero row when absent) and a presence
-    // word; the wave then issues its 18 row DMAs.
+    // word; the wave then issues its 18 row DMAs, each lane's source built from the key pointers
+    // held by lanes 0..31 (no LDS round trip).
     int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
-    uint64_t* rpt = reinterpret_cast<uint64_t*>(smem + L::OFF_RP);
     auto dma_indices = [&](int blk) {  // raw indices of block blk -> idx slot blk % 2
         const int kk = 32 * pw + lane;
         const int64_t left = w.mine - (int64_t)blk * BLK;
@@ -791,50 +770,65 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
             dma4(index_ptr<DENSE>(p, w.g, w.first + (int64_t)blk * BLK + kk),
                  lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * pw * 4));
     };
-    auto prepare_rows = [&](int blk, int32_t idx) {  // idx: raw index of key 32 pw + lane
+    // lane k < 32: pointer of key 32 pw + k of block blk (idx: its raw index); the presence word
+    // of the wave's 32 keys goes to LDS for the QK waves
+    auto key_ptrs = [&](int blk, int32_t idx) -> uint64_t {
         const int kk = 32 * pw + lane;
         const int64_t left = w.mine - (int64_t)blk * BLK;
         const bool in = lane < 32 && kk < left;
         const int64_t row = key_row<DENSE>(p, w.first + (int64_t)blk * BLK + kk, in, idx);
-        const uint64_t ptr = row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW)
-                                      : (uint64_t)(uintptr_t)g_zero_row;
-        if (lane < 32)
-            rpt[(blk & 1) * BLK + kk] = ptr;
         const uint32_t word = (uint32_t)__ballot(row >= 0);   // lanes 0..31: keys 32 pw + lane
         if (lane == 0)
             *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 1) * 16 + 4 * pw) = word;
+        return row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW) : (uint64_t)(uintptr_t)g_zero_row;
     };
-    auto issue_block = [&](int blk) {   // this wave's 18 row DMAs of block blk
+    // The wave's 18 row DMAs of block blk. Latent instruction i of subtile h moves keys 16 h + 2 i
+    // (lanes 0..31) and 16 h + 2 i + 1 (lanes 32..63) of the wave, chunk (lane % 32) ^ key; the
+    // two key pointers are broadcast from their lanes. Rope instruction: key 16 h + lane % 16,
+    // chunk 32 + lane / 16, its pointer fetched from that key's lane.
+    auto issue_block = [&](int blk, uint64_t kp) {
+        const int lo = (int)(uint32_t)kp, hi = (int)(uint32_t)(kp >> 32);
+        const int hb = lane >> 5;
+        const uint32_t boff = 16u * (uint32_t)((lane & 31) ^ hb);   // 16 ((lane % 32) ^ key) ^ 32 i
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            const int sub = 2 * pw + h;
-            const uint8_t* src[9];
+            const uint32_t lds0 = lds_addr(smem + (blk & 1) * SLOT + (2 * pw + h) * SUBB);
 #pragma unroll
-            for (int i = 0; i < 9; i++) src[i] = dma_src(rpt + (blk & 1) * BLK + 16 * sub, i, lane);
-            dma_subtile(src, lds_addr(smem + (blk & 1) * SLOT + sub * SUBB));
+            for (int i = 0; i < 8; i++) {
+                const int ka = 16 * h + 2 * i;
+                const uint64_t pa = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, ka) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane(lo, ka);
+                const uint64_t pb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, ka + 1) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane(lo, ka + 1);
+                const uint64_t base = hb ? pb : pa;
+                dma16(reinterpret_cast<const uint8_t*>(base + (boff ^ (32u * i))), lds0 + 1024 * i);
+            }
+            const int src = 16 * h + (lane & 15);
+            const uint64_t rp = ((uint64_t)(uint32_t)__shfl(hi, src) << 32) | (uint32_t)__shfl(lo, src);
+            dma16(reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (lane >> 4)), lds0 + 8192);
         }
     };
     if (w.nblk > 0) {
         int32_t idx0 = -1;
         if (lane < 32 && 32 * pw + lane < w.mine)
             idx0 = *index_ptr<DENSE>(p, w.g, w.first + 32 * pw + lane);
-        prepare_rows(0, idx0);
-        issue_block(0);
+        issue_block(0, key_ptrs(0, idx0));
         if (w.nblk > 1)
             dma_indices(1);
     }
+    lds_sync();   // Q0: the QK waves' staged query rows landed (they read them before B1)
 
-    // this lane's LDS byte offset within a subtile of its transposed V read (column chunk
-    // 8 pw + c, key half rb)
-    auto voff = [&](int c, int rb) {
-        const int kk = 8 * rb + (n16 >> 1), cc = 8 * pw + c;
-        return 2 * grp * SUBB + 16 * (32 * kk + (cc ^ kk)) + 8 * (n16 & 1);
-    };
-    auto load_vt = [&](int slot, int c) {
+    // This lane's transposed V read of column chunk 8 pw + c, key half rb of subtile 2 grp + sp:
+    // LDS unit 32 kk + (cc ^ kk) of the subtile, kk = 8 rb + m, cc = 8 pw + c, m = n16 / 2, plus
+    // 8 bytes for odd n16. Its byte offset in the slot is (vb + 128 (pw ^ rb)) ^ 16 c plus
+    // sp SUBB + 4096 rb, with vb = 2 grp SUBB + 528 m + 8 (n16 % 2): 16 (c ^ m) = 16 c ^ 16 m, and
+    // no other term has bits 4..8 set.
+    const int vb = 2 * grp * SUBB + 528 * (n16 >> 1) + 8 * (n16 & 1);
+    auto load_vt = [&](int slot, int c, int vb0, int vb1) {
         v2i tr[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int off = slot * SLOT + (r >> 1) * SUBB + voff(c, r & 1);
+            const int off = ((r & 1 ? vb1 : vb0) ^ (16 * c)) + (r >> 1) * SUBB + 4096 * (r & 1);
             tr[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(smem + off));
         }
         return v8i{tr[0].x, tr[0].y, tr[1].x, tr[1].y, tr[2].x, tr[2].y, tr[3].x, tr[3].y};
@@ -846,16 +840,18 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     for (int i = 0; i <= w.nblk; i++) {
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's DMAs of block i (and indices)
         lds_sync();   // B1: block i landed; P of block i - 1 published
+        float alpha[T];   // rescale factors of block i - 1, read before the gather (LDS latency)
+#pragma unroll
+        for (int t = 0; t < T; t++) alpha[t] = xalpha[t * 16 + n16];
         if (i + 1 < w.nblk) {
-            prepare_rows(i + 1, lane < 32 ? idx_lds[((i + 1) & 1) * BLK + 32 * pw + lane] : -1);
-            issue_block(i + 1);
+            issue_block(i + 1, key_ptrs(i + 1, lane < 32 ? idx_lds[((i + 1) & 1) * BLK + 32 * pw + lane] : -1));
         }
         if (i + 2 < w.nblk)
             dma_indices(i + 2);
         if (i >= 1) {   // rescale O for block i - 1 while the QK waves issue their MFMAs
 #pragma unroll
             for (int t = 0; t < T; t++) {
-                const float a = xalpha[t * 16 + n16];
+                const float a = alpha[t];
                 if (!__all(a == 1.f)) {
 #pragma unroll
                     for (int c = 0; c < 8; c++) O[t][c] *= a;
@@ -874,7 +870,13 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         }
         if (i < w.nblk) {
 #pragma unroll
-            for (int c = 0; c < 8; c++) vt[c] = load_vt(i & 1, c);
+            for (int c = 0; c < 8; c++) {
+                // the lane's bases for this slot (recomputed here, not held across the loop)
+                int b = vb;
+                asm volatile("" : "+v"(b));
+                b += (i & 1) * SLOT;
+                vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
+            }
         }
         lds_sync();   // B3: P of block i - 1 and V^T of block i are in registers
     }
