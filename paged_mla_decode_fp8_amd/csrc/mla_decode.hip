@@ -203,6 +203,48 @@ __device__ inline void dma16(const uint8_t* gsrc, uint32_t lds_base)
         : "memory");
 }
 
+// Nine row DMAs into consecutive 1 KB LDS pieces: instruction i moves 16 bytes at this lane's
+// src[i] to LDS byte lds_base + 1024 i + 16 lane. One asm block steps M0 itself, so all nine
+// sources are computed before the first DMA issues and the DMAs go out back to back.
+__device__ inline void dma9(const uint8_t* const (&src)[9], uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %8, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %9, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %10, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3]), "v"(src[4]),
+          "v"(src[5]), "v"(src[6]), "v"(src[7]), "v"(src[8])
+        : "memory", "scc");
+}
+
 // One global_load_lds_dword: 4 bytes at this lane's gsrc -> LDS byte lds_base + 4 * lane (asm
 // for the same reasons as dma16).
 __device__ inline void dma4(const void* gsrc, uint32_t lds_base)
@@ -792,7 +834,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         const uint32_t boff = 16u * (uint32_t)((lane & 31) ^ hb);   // 16 ((lane % 32) ^ key) ^ 32 i
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            const uint32_t lds0 = lds_addr(smem + (blk & 1) * SLOT + (2 * pw + h) * SUBB);
+            const uint8_t* src[9];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int ka = 16 * h + 2 * i;
@@ -801,11 +843,12 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                 const uint64_t pb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, ka + 1) << 32) |
                                     (uint32_t)__builtin_amdgcn_readlane(lo, ka + 1);
                 const uint64_t base = hb ? pb : pa;
-                dma16(reinterpret_cast<const uint8_t*>(base + (boff ^ (32u * i))), lds0 + 1024 * i);
+                src[i] = reinterpret_cast<const uint8_t*>(base + (boff ^ (32u * i)));
             }
-            const int src = 16 * h + (lane & 15);
-            const uint64_t rp = ((uint64_t)(uint32_t)__shfl(hi, src) << 32) | (uint32_t)__shfl(lo, src);
-            dma16(reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (lane >> 4)), lds0 + 8192);
+            const int sl = 16 * h + (lane & 15);
+            const uint64_t rp = ((uint64_t)(uint32_t)__shfl(hi, sl) << 32) | (uint32_t)__shfl(lo, sl);
+            src[8] = reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (lane >> 4));
+            dma9(src, lds_addr(smem + (blk & 1) * SLOT + (2 * pw + h) * SUBB));
         }
     };
     if (w.nblk > 0) {
@@ -1157,28 +1200,37 @@ int choose_tiles(int tiles_per_group)
 
 // A plan from shapes only. One workgroup fills a CU's LDS, so 256 workgroups cover the chip once.
 // Groups of at most two 128-key blocks: one workgroup per group and tile set (uniform, S = 1).
-// Longer groups: a balanced plan of 256 / tilesets pieces, which evens out ragged key counts; for
-// more groups than a balanced plan stages, uniform splits up to one workgroup per CU.
+// Longer groups: either one workgroup per group and tile set (S = 1, no partials to merge) or a
+// balanced plan of 256 / tilesets pieces, which evens out ragged key counts but pays for every
+// extra work item and merge (measured on MI355X at about ITEM_COST blocks per piece). The cost is
+// estimated in 128-key blocks per CU with every group at its maximum key count. For more groups
+// than a balanced plan stages, uniform splits up to one workgroup per CU.
+constexpr int64_t ITEM_COST = 10;
+
 mla_plan_t choose_plan(int groups, int tiles_per_group, int64_t max_keys)
 {
     mla_plan_t pl{};
     pl.tiles = choose_tiles(tiles_per_group);
     const int tilesets = tiles_per_group / pl.tiles;
-    if (max_keys <= 2 * BLK) {
-        pl.splits = 1;
-        pl.mode = MLA_SPLIT_UNIFORM;
+    const int64_t mb = (max_keys + BLK - 1) / BLK;
+    pl.splits = 1;
+    pl.mode = MLA_SPLIT_UNIFORM;
+    if (max_keys <= 2 * BLK)
         return pl;
-    }
-    if (groups <= MAX_BALANCED_GROUPS && (int64_t)groups * ((max_keys + BLK - 1) / BLK) < INT32_MAX) {
-        pl.splits = 256 / tilesets > 1 ? 256 / tilesets : 1;
-        pl.mode = MLA_SPLIT_BALANCED;
+    if (groups <= MAX_BALANCED_GROUPS && (int64_t)groups * mb < INT32_MAX) {
+        const int64_t wgs = (int64_t)groups * tilesets;
+        const int64_t whole = (wgs + 255) / 256 * mb;           // S = 1: rounds of workgroups
+        const int64_t balanced = (wgs * mb + 255) / 256 + ITEM_COST;
+        if (balanced < whole) {
+            pl.splits = 256 / tilesets > 1 ? 256 / tilesets : 1;
+            pl.mode = MLA_SPLIT_BALANCED;
+        }
         return pl;
     }
     int64_t s = 256 / ((int64_t)groups * tilesets);
     const int64_t cap = max_keys / (2 * BLK);
     s = s > cap ? cap : s;
     pl.splits = (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
-    pl.mode = MLA_SPLIT_UNIFORM;
     return pl;
 }
 

@@ -42,6 +42,8 @@ SPARSE_CASES = [
     (1, 5, 16, 256, [[200, 256, 231, 255, 129]], 65536, (5, 1)),
     (2, 1, 128, 1000, [[1000], [999]], 8000, (4, 4)),
     (1, 1, 48, 77, [[77]], 100, (2, 1)),
+    (2, 2, 16, 130, [[63, 64], [65, 130]], 400, (1, 1)),
+    (1, 3, 32, 200, [[191, 193, 200]], 1000, (3, 2)),
 ]
 
 
@@ -62,6 +64,8 @@ DENSE_CASES = [
     (1, 5, 16, [1031], 1, (4, 1)),
     (2, 3, 64, [0, 700], 32, (2, 4)),
     (1, 2, 128, [2100], 64, (5, 4)),
+    (2, 1, 16, [63, 65], 16, (2, 1)),
+    (1, 2, 16, [200], 48, (3, 1)),
 ]
 
 

@@ -220,7 +220,7 @@ WORKLOADS = {
                             "dense B=64 Q=1 H=128 page 64 seq_len U[1024,8192]"),
     "latency_sparse": Workload("latency_sparse", latency_sparse, 1, 1, 0,
                                "sparse B=4 Q=5 H=16 valid U[200,256] of a 65536-row cache"),
-    "topk_sparse": Workload("topk_sparse", topk_sparse, 256, 4, 1,
+    "topk_sparse": Workload("topk_sparse", topk_sparse, 1, 4, 0,
                             "sparse B=32 Q=5 H=64 top-k 2048 over 32768 positions, 5% empty"),
     "long_dense": Workload("long_dense", long_dense, 32, 4, 1,
                            "dense causal B=8 Q=4 H=128 seq_len 131072 page 64"),
