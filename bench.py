@@ -7,7 +7,10 @@ the other four workloads are timed the same way and reported under "workloads".
 
 Timing is cold with respect to the 256 MB Infinity Cache: the timed calls rotate over several
 copies of the KV cache (together well above 256 MB), all resident in HBM before timing starts.
-HIP events on the stream the kernel runs on bracket the K timed calls.
+HIP events on the stream the kernel runs on bracket the timed calls. The reported time per call is
+measured on a HIP graph that holds one call per KV copy, replayed back to back (the GPU time per
+call, with no host launch work in between); the time of K eager launches from Python is reported
+beside it (us_per_call_eager), and for the large workloads the two agree.
 
 Prints ONE JSON line.
 """
@@ -109,12 +112,33 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20):
     stream = torch.cuda.current_stream(dev)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    # eager: one stream launch per call from Python
     start.record(stream)
     for k in range(steps):
         call(warmup + k)
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms_eager = start.elapsed_time(end) / steps
+    o_eager = o.clone()
+    # graph replay: the calls over all KV copies captured once (no host work between launches)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(copies):
+            call(k)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(o.view(torch.int16), o_eager.view(torch.int16)):
+        raise RuntimeError(f"{name}: graph replay output differs from the eager call")
+    reps = max(1, steps // copies)
+    stream = torch.cuda.current_stream(dev)
+    start.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (reps * copies)
+    del graph
     sec = ms * 1e-3
     res = {
         "workload": name,
@@ -122,6 +146,7 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20):
         "plan": {"splits": plan[0], "tiles": plan[1],
                  "mode": "balanced" if plan[2] == mla.BALANCED else "uniform"},
         "us_per_call": round(ms * 1e3, 3),
+        "us_per_call_eager": round(ms_eager * 1e3, 3),
         "kv_bytes": alg["kv_bytes"],
         "alg_bytes": alg["bytes"],
         "alg_flops": alg["flops"],

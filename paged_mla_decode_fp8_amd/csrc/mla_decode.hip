@@ -137,6 +137,23 @@ __device__ inline uint32_t pack_e4m3(float a, float b, float c, float d)
     return (uint32_t)w;
 }
 
+// x unchanged, but opaque to the optimizer: values derived from it at a use site are computed
+// there instead of being hoisted out of loops and kept live (or spilled) across them.
+__device__ inline int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// x / y from r = 1 / y (rounded): the product x r, then one correction with its exactly computed
+// residual x - q y (fma). Exact whenever x / y is representable (a single key's O / l = v), and
+// within an ulp otherwise; three operations instead of a full division per element.
+__device__ inline float div_by(float x, float y, float r)
+{
+    const float q = x * r;
+    return fmaf(fmaf(-q, y, x), r, q);
+}
+
 __device__ inline v8i cat(v4i a, v4i b) { return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}; }
 
 __device__ inline v4i lds_read16(const uint8_t* smem, int off)
@@ -168,6 +185,17 @@ __device__ inline float wave_max16(float v)
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Maximum over all 64 lanes (every lane gets it): within each 16-lane row by DPP (quad swaps, then
+// the half-row and row mirrors), then across the rows by the row-swap permutes.
+__device__ inline float wave_max64(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true)));
+    return wave_max16(v);
 }
 
 __device__ inline float wave_sum16(float v)
@@ -477,22 +505,128 @@ __device__ inline int64_t partial_o_offset(int slot, int pw, int t, int c, int l
     return ((((int64_t)slot * 4 + pw) * T + t) * 8 + c) * 256 + 4 * lane;
 }
 
-// Q staging: the tile set's T * 16 query rows (bf16, 1152 B each) are DMA'd by the QK waves into
-// KV slot 1, which stays free until iteration 0 issues the DMA of block 1. LDS unit (16 bytes)
-// 72 r + c of row r holds the row's unit c ^ s(r) for the latent units c < 64, s(r) = (r / 2) % 4
-// (so that the 16 rows read at one unit offset spread over the banks), and unit c for the rope
-// units 64..71.
+// Q staging: the tile set's T * 16 query rows (bf16, 1152 B each, from row row0 of q) are DMA'd by
+// the QK waves into KV slot 1, which stays free until iteration 0 issues the DMA of block 1. LDS
+// unit (16 bytes) 72 r + c of row r holds the row's unit c ^ s(r) for the latent units c < 64,
+// s(r) = (r / 2) % 4, and unit c for the rope units 64..71.
 template <int T>
-__device__ inline void stage_q(const Params& p, uint8_t* smem, const Work& w, int qw, int lane)
+__device__ inline void stage_q(const Params& p, uint8_t* smem, int64_t row0, int qw, int lane)
 {
-    const uint8_t* qbase =
-        reinterpret_cast<const uint8_t*>(p.q + (w.row_base + 16 * w.ts * T) * ROW);
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(p.q + row0 * ROW);
     for (int i = qw; i < T * 18; i += 4) {   // 64 units per instruction, T * 16 * 72 units
         const int u = 64 * i + lane;
         const int r = u / 72, c = u - 72 * r;
         const int src = c < 64 ? (c ^ ((r >> 1) & 3)) : c;
         dma16(qbase + (int64_t)r * (2 * ROW) + 16 * src, lds_addr(smem + SLOT + 1024 * i));
     }
+}
+
+// The staged query rows -> the QK waves' MFMA B operands, by all 512 threads: per row the power
+// of two 2^k with max |q 2^k| <= 448 (k the largest such integer, 0 for a zero row), then the
+// exact E4M3 split hi = E4M3(q 2^k), lo = E4M3(q 2^k - hi) (|q 2^k| <= 448 and |q 2^k - hi| <= 16,
+// so neither rounding saturates). Thread tid handles the rows' 16-byte units tid + 512 j (8 bf16
+// each). The operands replace the rows in slot 1: [tile][operand][lane][32 B], operands 0..3 the hi
+// steps, 4..7 the lo steps, 8 the rope step (k-groups 0, 1 carry hi, 2, 3 lo); the row maxima
+// stay in the P area (free until the first P) for the row scales. Three workgroup barriers.
+template <int T>
+__device__ void convert_q(uint8_t* smem, int tid)
+{
+    using L = Smem<T>;
+    constexpr int UNITS = T * 16 * 72;   // a multiple of 64: a wave's units are all real or none
+    constexpr int PER = (UNITS + THREADS - 1) / THREADS;
+    uint32_t* amax = reinterpret_cast<uint32_t*>(smem + L::OFF_P);   // [T * 16] float bits
+    const int lane = tid & 63;
+    if (tid < T * 16)
+        amax[tid] = 0u;
+    __syncthreads();
+    v4i raw[PER];
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        const int ubase = tid - lane + THREADS * j;   // the wave's first unit (wave-uniform)
+        if (ubase >= UNITS)
+            continue;
+        const int u = ubase + lane;
+        const int r = u / 72, c = u - 72 * r;
+        raw[j] = *reinterpret_cast<const v4i*>(smem + SLOT + 16 * (72 * r + (c < 64 ? c ^ ((r >> 1) & 3) : c)));
+        float m = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[j][d] & 0xFFFF)));
+            m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[j][d] >> 16)));
+        }
+        // the wave's 64 units lie in at most two rows (72 units per row): reduce each row over the
+        // wave, then one atomic per row (non-negative floats order like their bits)
+        const int r0 = ubase / 72, r1 = (ubase + 63) / 72;
+        const float m0 = wave_max64(r == r0 ? m : 0.f), m1 = wave_max64(r == r1 ? m : 0.f);
+        if (lane == 0)
+            atomicMax(&amax[r0], __float_as_uint(m0));
+        if (lane == 0 && r1 != r0)
+            atomicMax(&amax[r1], __float_as_uint(m1));
+    }
+    __syncthreads();   // every raw unit is in registers; the row maxima are complete
+    uint8_t* qop = smem + SLOT;
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        const int ubase = tid - lane + THREADS * j;
+        if (ubase >= UNITS)
+            continue;
+        const int u = ubase + lane;
+        const int r = u / 72, c = u - 72 * r;
+        const float am = __uint_as_float(amax[r]);
+        int k = 0;
+        if (am > 0.f) {
+            int e;
+            const float mm = frexpf(am, &e);  // am = mm * 2^e, mm in [0.5, 1)
+            k = (2.f * mm <= 1.75f) ? (9 - e) : (8 - e);
+        }
+        float x[8];
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            x[2 * d] = ldexpf(bf16_to_f32((uint32_t)raw[j][d] & 0xFFFF), k);
+            x[2 * d + 1] = ldexpf(bf16_to_f32((uint32_t)raw[j][d] >> 16), k);
+        }
+        uint32_t hi[2], lo[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h], x[4 * h + 1], 0, false);
+            hi[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2], x[4 * h + 3], w0, true);
+            const float d4[4] = {x[4 * h] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 0),
+                                 x[4 * h + 1] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 1),
+                                 x[4 * h + 2] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 2),
+                                 x[4 * h + 3] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 3)};
+            const int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(d4[0], d4[1], 0, false);
+            lo[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d4[2], d4[3], w1, true);
+        }
+        raw[j] = v4i{(int)hi[0], (int)hi[1], (int)lo[0], (int)lo[1]};
+    }
+    __syncthreads();   // every raw read of slot 1 has been made (the operands overwrite the rows)
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        const int ubase = tid - lane + THREADS * j;
+        if (ubase >= UNITS)
+            continue;
+        const int u = ubase + lane;
+        const int r = u / 72, c = u - 72 * r;
+        // values 8 c .. 8 c + 7 of row r: tile t, row n16 of the tile
+        const int t = r >> 4, n16 = r & 15, v0 = 8 * c;
+        int op_hi, op_lo, lane_hi, lane_lo, wi;
+        if (v0 < LATENT) {   // latent step st, k-group g: byte v0 % 32 of that lane's operand
+            const int st = v0 >> 7, g = (v0 >> 5) & 3;
+            op_hi = st;
+            op_lo = 4 + st;
+            lane_hi = lane_lo = n16 + 16 * g;
+            wi = v0 & 31;
+        } else {             // rope half: hi in k-group half, lo in k-group 2 + half
+            const int half = (v0 - LATENT) >> 5;
+            op_hi = op_lo = 8;
+            lane_hi = n16 + 16 * half;
+            lane_lo = n16 + 16 * (2 + half);
+            wi = (v0 - LATENT) & 31;
+        }
+        *reinterpret_cast<v2i*>(qop + ((t * 9 + op_hi) * 64 + lane_hi) * 32 + wi) = v2i{raw[j][0], raw[j][1]};
+        *reinterpret_cast<v2i*>(qop + ((t * 9 + op_lo) * 64 + lane_lo) * 32 + wi) = v2i{raw[j][2], raw[j][3]};
+    }
+    __syncthreads();   // the operands are in LDS
 }
 
 // ---- QK waves: Q stage, S^T = K (hi + lo)^T, softmax; P and the rescale factors to LDS ----
@@ -525,85 +659,37 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         lim[j] = (int)(c - w.first);   // |c - first| <= n_grp < 2^31
     }
 
-    if (w.nblk > 0)
-        stage_q<T>(p, smem, w, qw, lane);
-    __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's Q rows landed
+    __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's staged Q rows landed
     lds_sync();                          // Q0: every staged row landed
+    if (w.nblk > 0)
+        convert_q<T>(smem, qw * 64 + lane);
 
-    // ---- Q of the tiles -> exact E4M3 hi + lo of q * 2^k (B operands), from the staged copy in
-    // KV slot 1 (stage_q). Two passes over LDS (the row maximum, then the split), so no more than
-    // one operand step of raw values is live at a time. ----
+    // ---- the tiles' B operands (exact E4M3 hi + lo of q * 2^k) and row scales from LDS ----
     v8i qhi[TW][4], qlo[TW][4], qrope[TW];
     float row_scale[TW];  // scale_log2 * 2^-k for row n16
 #pragma unroll
     for (int j = 0; j < TW; j++) {
         row_scale[j] = 0.f;
         if (w.nblk > 0 && active) {
-            const int r = 16 * (qt0 + j) + n16;   // row within the tile set
-            const uint8_t* qrow = smem + SLOT + r * (2 * ROW);
-            const int sw = (r >> 1) & 3;
-            // operand step st: values q[128 st + 32 grp + 0..31] (rope: 512 + 32 (grp & 1) + 0..31),
-            // 16-byte units 16 st + 4 grp + e (rope: 64 + 4 (grp & 1) + e), e = 0..3
-            auto unit = [&](int st, int e) {
-                const int c = st < 4 ? ((16 * st + 4 * grp + e) ^ sw) : (64 + 4 * (grp & 1) + e);
-                return *reinterpret_cast<const v4i*>(qrow + 16 * c);
+            const int t = qt0 + j;
+            auto op = [&](int o) {
+                const int off = SLOT + ((t * 9 + o) * 64 + lane) * 32;
+                return cat(lds_read16(smem, off), lds_read16(smem, off + 16));
             };
-            float amax = 0.f;
 #pragma unroll
-            for (int st = 0; st < 5; st++) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const v4i u = unit(st, e);
-#pragma unroll
-                    for (int d = 0; d < 4; d++) {
-                        amax = fmaxf(amax, fabsf(bf16_to_f32((uint32_t)u[d] & 0xFFFF)));
-                        amax = fmaxf(amax, fabsf(bf16_to_f32((uint32_t)u[d] >> 16)));
-                    }
-                }
+            for (int st = 0; st < 4; st++) {
+                qhi[j][st] = op(st);
+                qlo[j][st] = op(4 + st);
             }
-            amax = wave_max16(amax);
-            // k: the largest integer with amax * 2^k <= 448 (0 for a zero row)
+            qrope[j] = op(8);
+            const float am = __uint_as_float(reinterpret_cast<const uint32_t*>(smem + L::OFF_P)[16 * t + n16]);
             int k = 0;
-            if (amax > 0.f) {
+            if (am > 0.f) {
                 int e;
-                const float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
+                const float m = frexpf(am, &e);
                 k = (2.f * m <= 1.75f) ? (9 - e) : (8 - e);
             }
             row_scale[j] = ldexpf(p.scale_log2, -k);
-            auto split4 = [&](uint32_t w0, uint32_t w1, uint32_t& hi, uint32_t& lo) {
-                const float x0 = ldexpf(bf16_to_f32(w0 & 0xFFFF), k);
-                const float x1 = ldexpf(bf16_to_f32(w0 >> 16), k);
-                const float x2 = ldexpf(bf16_to_f32(w1 & 0xFFFF), k);
-                const float x3 = ldexpf(bf16_to_f32(w1 >> 16), k);
-                hi = pack_e4m3(x0, x1, x2, x3);
-                const float h0 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 0);
-                const float h1 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 1);
-                const float h2 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 2);
-                const float h3 = __builtin_amdgcn_cvt_f32_fp8((int)hi, 3);
-                lo = pack_e4m3(x0 - h0, x1 - h1, x2 - h2, x3 - h3);
-            };
-#pragma unroll
-            for (int st = 0; st < 5; st++) {
-                // dword e of the operand holds values 4e..4e+3: unit e / 2, dwords 2 (e % 2), + 1
-                v8i vh, vl;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; e2++) {
-                    const v4i u = unit(st, e2);
-                    uint32_t h, l;
-                    split4((uint32_t)u[0], (uint32_t)u[1], h, l);
-                    vh[2 * e2] = (int)h;
-                    vl[2 * e2] = (int)l;
-                    split4((uint32_t)u[2], (uint32_t)u[3], h, l);
-                    vh[2 * e2 + 1] = (int)h;
-                    vl[2 * e2 + 1] = (int)l;
-                }
-                if (st < 4) {
-                    qhi[j][st] = vh;
-                    qlo[j][st] = vl;
-                } else {
-                    qrope[j] = grp < 2 ? vh : vl;  // rope step: k-groups 0,1 carry hi, 2,3 carry lo
-                }
-            }
         }
     }
 
@@ -654,7 +740,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
             // fragment f (or its packed rope MFMAs) and the lo MFMAs of fragment f - 1, so no MFMA
             // waits on the one just issued; a fragment stays in the ring until its lo MFMAs.
             constexpr int NFRAG = 5 * KS;
-            constexpr int AHEAD = 2, RING = AHEAD + 2;
+            constexpr int AHEAD = 1, RING = AHEAD + 2;
             v8i kf[RING];
             auto load_frag = [&](int f) {
                 const int st = f / KS, sub = f % KS;
@@ -714,7 +800,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                     bm = fmaxf(bm, fmaxf(fmaxf(acc[j][u][0], acc[j][u][1]), fmaxf(acc[j][u][2], acc[j][u][3])));
                 bmax[j] = wave_max16(bm);
                 if (grp == 0)
-                    xmax[kh * (T * 16) + (qt0 + j) * 16 + n16] = bmax[j];
+                    xmax[kh * (T * 16) + (qt0 + j) * 16 + (opaque(lane) & 15)] = bmax[j];
             }
         }
         lds_sync();   // B2: the PV waves start on block i - 1; the halves' maxima are published
@@ -724,7 +810,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
 #pragma unroll
             for (int j = 0; j < TW; j++) {
                 // both halves combine the same two maxima (fmaxf is exact and symmetric)
-                const float other = xmax[(kh ^ 1) * (T * 16) + (qt0 + j) * 16 + n16];
+                const float other = xmax[(kh ^ 1) * (T * 16) + (qt0 + j) * 16 + (opaque(lane) & 15)];
                 const float bm = fmaxf(bmax[j], other) * row_scale[j];
                 const float m_new = fmaxf(m_run[j], bm);
                 alpha[j] = (m_run[j] == neg_inf) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
@@ -749,14 +835,15 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         }
         lds_sync();   // B3: the PV waves have taken P of block i - 1 into registers
         if (work) {
+            const int lo = opaque(lane);
 #pragma unroll
             for (int j = 0; j < TW; j++) {
 #pragma unroll
                 for (int u = 0; u < KS; u++)
-                    *reinterpret_cast<uint32_t*>(smem + L::OFF_P + (qt0 + j) * PTILE + n16 * PPITCH +
-                                                 16 * (KS * kh + u) + 4 * grp) = pk[j][u];
+                    *reinterpret_cast<uint32_t*>(smem + L::OFF_P + (qt0 + j) * PTILE + (lo & 15) * PPITCH +
+                                                 16 * (KS * kh + u) + 4 * (lo >> 4)) = pk[j][u];
                 if (grp == 0 && kh == 0)
-                    xalpha[(qt0 + j) * 16 + n16] = alpha[j];
+                    xalpha[(qt0 + j) * 16 + (lo & 15)] = alpha[j];
             }
         }
     }
@@ -859,7 +946,9 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         if (w.nblk > 1)
             dma_indices(1);
     }
-    lds_sync();   // Q0: the QK waves' staged query rows landed (they read them before B1)
+    lds_sync();   // Q0: the QK waves' staged query rows landed
+    if (w.nblk > 0)
+        convert_q<T>(smem, 256 + pw * 64 + lane);
 
     // This lane's transposed V read of column chunk 8 pw + c, key half rb of subtile 2 grp + sp:
     // LDS unit 32 kk + (cc ^ kk) of the subtile, kk = 8 rb + m, cc = 8 pw + c, m = n16 / 2, plus
@@ -905,7 +994,8 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         if (i >= 1) {
 #pragma unroll
             for (int t = 0; t < T; t++) {
-                const int off = L::OFF_P + t * PTILE + n16 * PPITCH + 32 * grp;
+                const int lo = opaque(lane);
+                const int off = L::OFF_P + t * PTILE + (lo & 15) * PPITCH + 32 * (lo >> 4);
                 const v8i pb = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
 #pragma unroll
                 for (int c = 0; c < 8; c++) O[t][c] = mfma(vt[c], pb, O[t][c]);
@@ -932,16 +1022,17 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
 #pragma unroll
         for (int t = 0; t < T; t++) {
             const float lt = fl[t * 16 + n16] + fl[T * 16 + t * 16 + n16];
+            const float rl = 1.f / lt;   // one division per row
             const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
 #pragma unroll
             for (int c = 0; c < 8; c++) {
                 const int col = 128 * pw + 16 * c + 4 * grp;
                 uint32_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
                 if (lt > 0.f) {
-                    b0 = f32_to_bf16_rne(O[t][c][0] / lt * p.k_scale);
-                    b1 = f32_to_bf16_rne(O[t][c][1] / lt * p.k_scale);
-                    b2 = f32_to_bf16_rne(O[t][c][2] / lt * p.k_scale);
-                    b3 = f32_to_bf16_rne(O[t][c][3] / lt * p.k_scale);
+                    b0 = f32_to_bf16_rne(div_by(O[t][c][0], lt, rl) * p.k_scale);
+                    b1 = f32_to_bf16_rne(div_by(O[t][c][1], lt, rl) * p.k_scale);
+                    b2 = f32_to_bf16_rne(div_by(O[t][c][2], lt, rl) * p.k_scale);
+                    b3 = f32_to_bf16_rne(div_by(O[t][c][3], lt, rl) * p.k_scale);
                 }
                 v2i wv = v2i{(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
                 *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) = wv;
@@ -1039,8 +1130,9 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid)
         for (int pw = 0; pw < 4; pw++) {
             uint32_t b[4] = {0u, 0u, 0u, 0u};
             if (total[t] > 0.f) {
+                const float rt = 1.f / total[t];
 #pragma unroll
-                for (int e = 0; e < 4; e++) b[e] = f32_to_bf16_rne(acc[pw][t][e] / total[t] * p.k_scale);
+                for (int e = 0; e < 4; e++) b[e] = f32_to_bf16_rne(div_by(acc[pw][t][e], total[t], rt) * p.k_scale);
             }
             const int col = 128 * pw + 16 * c + 4 * grp;
             *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) =
@@ -1126,6 +1218,8 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             const Params& pi = fresh_params();
             int li = lane;   // lane-derived offsets are recomputed per item, not kept live
             asm volatile("" : "+v"(li));
+            // the query rows go out before the key counts are read (they depend on g and ts only)
+            stage_q<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
             Work w;
             item(pi, g, pre, w);
             pre += nblocks(w.n_grp);
