@@ -40,8 +40,12 @@ KERNEL_SRC = os.path.join(ROOT, "paged_mla_decode_fp8_amd", "csrc", "mla_decode.
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source with its // comments and blank lines removed, so that counter
+    summaries stay valid across comment edits and go stale on any code change."""
+    with open(KERNEL_SRC) as f:
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in f]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def algorithmic(x):

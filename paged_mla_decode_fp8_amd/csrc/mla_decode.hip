@@ -20,11 +20,13 @@
 //
 // Workgroup = (key group, split, set of T 16-row tiles), 512 threads = 8 waves, two per SIMD,
 // specialised as on the AMD page (QK waves and PV waves). Wave i runs on SIMD i % 4:
-//   QK waves 0..3: wave t owns tile t. Per 128-key block: S^T of all 128 keys x 16 rows by 9
-//          16x16x128 MFMAs per 16-key subtile (4 latent steps x {hi, lo} + 1 rope step packing
-//          rope hi | rope lo against rope | rope), K fragments streamed from LDS through a register
-//          ring; then the whole softmax inside the wave: row max, running max, P = 448 exp2(x - max)
-//          -> E4M3 into LDS, row sums of the unrounded P in a fixed order, rescale factor to LDS.
+//   QK waves 0..3: wave w owns key half w % 2 (64 of the block's 128 keys) of tile pair w / 2.
+//          Per 128-key block: S^T of its 64 keys x 16 rows of both tiles by 9 16x16x128 MFMAs per
+//          16-key subtile and tile (4 latent steps x {hi, lo} + 1 rope step packing rope hi | rope lo
+//          against rope | rope), each K fragment streamed from LDS through a register ring and used
+//          for both tiles; then the softmax inside the wave: block maximum (exchanged with the
+//          other key half through LDS), running max, P = 448 exp2(x - max) -> E4M3 into LDS, row
+//          sums of the unrounded P in a fixed order, rescale factor to LDS.
 //   PV waves 4..7: wave 4 + c owns latent columns 128c..128c+127 of every tile. They run one block
 //          behind: O^T += V^T P^T of block i - 1 while the QK waves work on block i, so on each
 //          SIMD one wave's softmax VALU overlaps the other's MFMAs. They also do the gather: raw
