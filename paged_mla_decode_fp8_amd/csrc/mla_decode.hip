@@ -189,17 +189,6 @@ __device__ inline float wave_max16(float v)
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Maximum over all 64 lanes (every lane gets it): within each 16-lane row by DPP (quad swaps, then
-// the half-row and row mirrors), then across the rows by the row-swap permutes.
-__device__ inline float wave_max64(float v)
-{
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true)));
-    return wave_max16(v);
-}
-
 __device__ inline float wave_sum16(float v)
 {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -523,69 +512,71 @@ __device__ inline void stage_q(const Params& p, uint8_t* smem, int64_t row0, int
     }
 }
 
+// Maximum over each aligned group of N lanes (N = 8, 16 or 32; every lane of a group gets it): quad
+// swaps and the half-row mirror (8), the row mirror (16), the 16-lane row swap (32).
+template <int N>
+__device__ inline float group_max(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
+    if (N >= 16)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true)));
+    if (N >= 32) {
+        auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    }
+    return v;
+}
+
 // The staged query rows -> the QK waves' MFMA B operands, by all 512 threads: per row the power
 // of two 2^k with max |q 2^k| <= 448 (k the largest such integer, 0 for a zero row), then the
 // exact E4M3 split hi = E4M3(q 2^k), lo = E4M3(q 2^k - hi) (|q 2^k| <= 448 and |q 2^k - hi| <= 16,
-// so neither rounding saturates). Thread tid handles the rows' 16-byte units tid + 512 j (8 bf16
-// each). The operands replace the rows in slot 1: [tile][operand][lane][32 B], operands 0..3 the hi
-// steps, 4..7 the lo steps, 8 the rope step (k-groups 0, 1 carry hi, 2, 3 lo); the row maxima
-// stay in the P area (free until the first P) for the row scales. Three workgroup barriers.
+// so neither rounding saturates). LPR = 32 / T consecutive lanes (inside one wave) share a row:
+// lane li of the group takes the row's 16-byte units li, li + LPR, .. (8 bf16 each), so the row
+// maximum is a reduction inside the lane group. The operands replace the rows in slot 1:
+// [tile][operand][lane][32 B], operands 0..3 the hi steps, 4..7 the lo steps, 8 the rope step
+// (k-groups 0, 1 carry hi, 2, 3 lo); the row maxima go to the P area (free until the first P) for
+// the row scales. Two workgroup barriers.
 template <int T>
 __device__ void convert_q(uint8_t* smem, int tid)
 {
     using L = Smem<T>;
-    constexpr int UNITS = T * 16 * 72;   // a multiple of 64: a wave's units are all real or none
-    constexpr int PER = (UNITS + THREADS - 1) / THREADS;
-    uint32_t* amax = reinterpret_cast<uint32_t*>(smem + L::OFF_P);   // [T * 16] float bits
-    const int lane = tid & 63;
-    if (tid < T * 16)
-        amax[tid] = 0u;
-    __syncthreads();
-    v4i raw[PER];
+    constexpr int LPR = 32 / T;                  // lanes per row
+    constexpr int UPL = (72 + LPR - 1) / LPR;    // units per lane
+    const int r = tid / LPR, li = tid % LPR;     // row of the tile set, lane in the row's group
+    const int sw = (r >> 1) & 3;                 // the staged row's unit swizzle
+    v4i raw[UPL];
+    float m = 0.f;
 #pragma unroll
-    for (int j = 0; j < PER; j++) {
-        const int ubase = tid - lane + THREADS * j;   // the wave's first unit (wave-uniform)
-        if (ubase >= UNITS)
-            continue;
-        const int u = ubase + lane;
-        const int r = u / 72, c = u - 72 * r;
-        raw[j] = *reinterpret_cast<const v4i*>(smem + SLOT + 16 * (72 * r + (c < 64 ? c ^ ((r >> 1) & 3) : c)));
-        float m = 0.f;
+    for (int k = 0; k < UPL; k++) {
+        const int c = li + LPR * k;
+        raw[k] = v4i{0, 0, 0, 0};
+        if (c < 72) {
+            raw[k] = *reinterpret_cast<const v4i*>(smem + SLOT + 16 * (72 * r + (c < 64 ? c ^ sw : c)));
 #pragma unroll
-        for (int d = 0; d < 4; d++) {
-            m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[j][d] & 0xFFFF)));
-            m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[j][d] >> 16)));
+            for (int d = 0; d < 4; d++) {
+                m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[k][d] & 0xFFFF)));
+                m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[k][d] >> 16)));
+            }
         }
-        // the wave's 64 units lie in at most two rows (72 units per row): reduce each row over the
-        // wave, then one atomic per row (non-negative floats order like their bits)
-        const int r0 = ubase / 72, r1 = (ubase + 63) / 72;
-        const float m0 = wave_max64(r == r0 ? m : 0.f), m1 = wave_max64(r == r1 ? m : 0.f);
-        if (lane == 0)
-            atomicMax(&amax[r0], __float_as_uint(m0));
-        if (lane == 0 && r1 != r0)
-            atomicMax(&amax[r1], __float_as_uint(m1));
     }
-    __syncthreads();   // every raw unit is in registers; the row maxima are complete
-    uint8_t* qop = smem + SLOT;
+    m = group_max<LPR>(m);
+    if (li == 0)
+        reinterpret_cast<float*>(smem + L::OFF_P)[r] = m;
+    int ks = 0;
+    if (m > 0.f) {
+        int e;
+        const float mm = frexpf(m, &e);  // m = mm * 2^e, mm in [0.5, 1)
+        ks = (2.f * mm <= 1.75f) ? (9 - e) : (8 - e);
+    }
 #pragma unroll
-    for (int j = 0; j < PER; j++) {
-        const int ubase = tid - lane + THREADS * j;
-        if (ubase >= UNITS)
-            continue;
-        const int u = ubase + lane;
-        const int r = u / 72, c = u - 72 * r;
-        const float am = __uint_as_float(amax[r]);
-        int k = 0;
-        if (am > 0.f) {
-            int e;
-            const float mm = frexpf(am, &e);  // am = mm * 2^e, mm in [0.5, 1)
-            k = (2.f * mm <= 1.75f) ? (9 - e) : (8 - e);
-        }
+    for (int k = 0; k < UPL; k++) {
         float x[8];
 #pragma unroll
         for (int d = 0; d < 4; d++) {
-            x[2 * d] = ldexpf(bf16_to_f32((uint32_t)raw[j][d] & 0xFFFF), k);
-            x[2 * d + 1] = ldexpf(bf16_to_f32((uint32_t)raw[j][d] >> 16), k);
+            x[2 * d] = ldexpf(bf16_to_f32((uint32_t)raw[k][d] & 0xFFFF), ks);
+            x[2 * d + 1] = ldexpf(bf16_to_f32((uint32_t)raw[k][d] >> 16), ks);
         }
         uint32_t hi[2], lo[2];
 #pragma unroll
@@ -599,18 +590,18 @@ __device__ void convert_q(uint8_t* smem, int tid)
             const int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(d4[0], d4[1], 0, false);
             lo[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d4[2], d4[3], w1, true);
         }
-        raw[j] = v4i{(int)hi[0], (int)hi[1], (int)lo[0], (int)lo[1]};
+        raw[k] = v4i{(int)hi[0], (int)hi[1], (int)lo[0], (int)lo[1]};
     }
     __syncthreads();   // every raw read of slot 1 has been made (the operands overwrite the rows)
+    uint8_t* qop = smem + SLOT;
+    const int t = r >> 4, n16 = r & 15;
 #pragma unroll
-    for (int j = 0; j < PER; j++) {
-        const int ubase = tid - lane + THREADS * j;
-        if (ubase >= UNITS)
+    for (int k = 0; k < UPL; k++) {
+        const int c = li + LPR * k;
+        if (c >= 72)
             continue;
-        const int u = ubase + lane;
-        const int r = u / 72, c = u - 72 * r;
         // values 8 c .. 8 c + 7 of row r: tile t, row n16 of the tile
-        const int t = r >> 4, n16 = r & 15, v0 = 8 * c;
+        const int v0 = 8 * c;
         int op_hi, op_lo, lane_hi, lane_lo, wi;
         if (v0 < LATENT) {   // latent step st, k-group g: byte v0 % 32 of that lane's operand
             const int st = v0 >> 7, g = (v0 >> 5) & 3;
@@ -625,10 +616,10 @@ __device__ void convert_q(uint8_t* smem, int tid)
             lane_lo = n16 + 16 * (2 + half);
             wi = (v0 - LATENT) & 31;
         }
-        *reinterpret_cast<v2i*>(qop + ((t * 9 + op_hi) * 64 + lane_hi) * 32 + wi) = v2i{raw[j][0], raw[j][1]};
-        *reinterpret_cast<v2i*>(qop + ((t * 9 + op_lo) * 64 + lane_lo) * 32 + wi) = v2i{raw[j][2], raw[j][3]};
+        *reinterpret_cast<v2i*>(qop + ((t * 9 + op_hi) * 64 + lane_hi) * 32 + wi) = v2i{raw[k][0], raw[k][1]};
+        *reinterpret_cast<v2i*>(qop + ((t * 9 + op_lo) * 64 + lane_lo) * 32 + wi) = v2i{raw[k][2], raw[k][3]};
     }
-    __syncthreads();   // the operands are in LDS
+    __syncthreads();   // the operands and the row maxima are in LDS
 }
 
 // ---- QK waves: Q stage, S^T = K (hi + lo)^T, softmax; P and the rescale factors to LDS ----
