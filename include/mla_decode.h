@@ -34,7 +34,8 @@ extern "C" {
 typedef enum {
     MLA_OK = 0,
     MLA_ERR_NULL = 1,        /* a required pointer is NULL */
-    MLA_ERR_SHAPE = 2,       /* B, Q, H, K, max_pages or page_size out of range (H % 16 != 0 ...) */
+    MLA_ERR_SHAPE = 2,       /* B, Q, H, K, max_pages or page_size out of range (H % 16 != 0,
+                                max_pages * page_size above 2^31 - 1 ...) */
     MLA_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
     MLA_ERR_WORKSPACE = 4,   /* the workspace is missing or smaller than mla_workspace_bytes() */
     MLA_ERR_UNSUPPORTED = 5, /* a plan the kernels do not implement (tiles not 1/2/4 or not

@@ -77,6 +77,8 @@ struct Params {
     const uint8_t* kv;
     int64_t num_rows;
     int page_size;
+    uint32_t pg_magic;   // n / page_size = (t + ((n - t) >> pg_s1)) >> pg_s2, t = umulhi(n, pg_magic)
+    int pg_s1, pg_s2;
     const int32_t* table;
     int max_pages;
     const int32_t* seq_lens;
@@ -111,9 +113,10 @@ struct Smem {
     static constexpr int OFF_FM = OFF_ALPHA + T * 16 * 4;      // float [T*16]
     static constexpr int OFF_FL = OFF_FM + T * 16 * 4;         // float [2][T*16] (key halves)
     static constexpr int OFF_XMAX = OFF_FL + 2 * T * 16 * 4;   // float [2][T*16] block maxima
-    static constexpr int OFF_KMASK = OFF_XMAX + 2 * T * 16 * 4; // uint32 [2][4] key presence bits
-    static constexpr int OFF_IDX = OFF_KMASK + 2 * 16;         // int32 [2][BLK] raw key indices
-    static constexpr int OFF_MISC = OFF_IDX + 2 * BLK * 4;     // int [4]
+    static constexpr int OFF_KMASK = OFF_XMAX + 2 * T * 16 * 4; // uint32 [4][4] key presence bits
+    static constexpr int OFF_IDX = OFF_KMASK + 4 * 16;         // int32 [2][BLK] raw key indices
+    static constexpr int OFF_PTAB = OFF_IDX + 2 * BLK * 4;     // uint64 [4 waves][32] key pointers
+    static constexpr int OFF_MISC = OFF_PTAB + 4 * 32 * 8;     // int [4]
     static constexpr int BYTES = OFF_MISC + 16;
 };
 static_assert(Smem<4>::BYTES <= 163840, "LDS budget");
@@ -280,11 +283,20 @@ __device__ inline void dma4(const void* gsrc, uint32_t lds_base)
         : "memory");
 }
 
+// n / page_size for n < 2^32 by a multiply with the divisor's precomputed magic number
+// (Granlund and Montgomery, "Division by invariant integers using multiplication", 1994, the
+// unsigned N-bit form of their Figure 4.1).
+__device__ inline uint32_t page_div(const Params& p, uint32_t n)
+{
+    const uint32_t t = __umulhi(n, p.pg_magic);
+    return (t + ((n - t) >> p.pg_s1)) >> p.pg_s2;
+}
+
 template <bool DENSE>
 __device__ inline const int32_t* index_ptr(const Params& p, int g, int64_t jabs)
 {
     if (DENSE)
-        return p.table + (int64_t)g * p.max_pages + (uint32_t)jabs / (uint32_t)p.page_size;
+        return p.table + (int64_t)g * p.max_pages + page_div(p, (uint32_t)jabs);
     return p.rows + (int64_t)g * p.K + jabs;
 }
 
@@ -296,7 +308,8 @@ __device__ inline int64_t key_row(const Params& p, int64_t jabs, bool inrange, i
     if (inrange) {
         if (DENSE) {
             if (idx >= 0)
-                row = (int64_t)idx * p.page_size + (int64_t)((uint32_t)jabs % (uint32_t)p.page_size);
+                row = (int64_t)idx * p.page_size +
+                      (int64_t)((uint32_t)jabs - page_div(p, (uint32_t)jabs) * (uint32_t)p.page_size);
         } else {
             row = idx;
         }
@@ -715,7 +728,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         if (work) {
             // presence bits of the block's keys, read before the MFMAs so that the LDS latency
             // hides behind them; this lane's 16 keys: bit 4u + jj <-> key 16 (4 kh + u) + 4 grp + jj
-            const v2i mw = *reinterpret_cast<const v2i*>(smem + L::OFF_KMASK + slot * 16 + 8 * kh);
+            const v2i mw = *reinterpret_cast<const v2i*>(smem + L::OFF_KMASK + (i & 3) * 16 + 8 * kh);
             const uint8_t* kslot = smem;
             // the lane's bases for this slot and key half (kept out of the loop-invariant set so
             // that they are recomputed here rather than held in registers across the loop)
@@ -880,11 +893,12 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     const int grp = lane >> 4;
 
     // Gather: this wave moves keys 32 pw .. 32 pw + 31 (subtiles 2 pw, 2 pw + 1) of every block.
-    // Per block: the raw indices (page ids or row ids) arrive in an LDS slot by DMA one block
-    // earlier; lanes 0..31 turn them into row pointers (the zero row when absent) and a presence
-    // word; the wave then issues its 18 row DMAs, each lane's source built from the key pointers
-    // held by lanes 0..31 (no LDS round trip).
+    // The raw indices (page ids or row ids) of block b arrive in LDS slot b % 2 by DMA three blocks
+    // ahead; one block ahead, lanes 0..31 turn them into row pointers (the zero row when absent),
+    // which go to the wave's pointer table, and a presence word; the wave then issues the block's
+    // 18 row DMAs with each lane's source read from the table.
     int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
+    uint64_t* ptab = reinterpret_cast<uint64_t*>(smem + L::OFF_PTAB) + 32 * pw;
     auto dma_indices = [&](int blk) {  // raw indices of block blk -> idx slot blk % 2
         const int kk = 32 * pw + lane;
         const int64_t left = w.mine - (int64_t)blk * BLK;
@@ -892,52 +906,61 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
             dma4(index_ptr<DENSE>(p, w.g, w.first + (int64_t)blk * BLK + kk),
                  lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * pw * 4));
     };
-    // lane k < 32: pointer of key 32 pw + k of block blk (idx: its raw index); the presence word
-    // of the wave's 32 keys goes to LDS for the QK waves
-    auto key_ptrs = [&](int blk, int32_t idx) -> uint64_t {
+    // Lane k < 32: the pointer of key 32 pw + k of block blk (idx: its raw index) into table entry
+    // 16 (k % 2) + 8 (k / 16) + (k % 16) / 2, i.e. the keys of latent DMA i of subtile h (keys
+    // 16 h + 2 i and 16 h + 2 i + 1 of the wave) sit at entries 8 h + i and 16 + 8 h + i. The
+    // presence word of the wave's 32 keys goes to LDS for the QK waves.
+    auto key_ptrs = [&](int blk, int32_t idx) {
         const int kk = 32 * pw + lane;
         const int64_t left = w.mine - (int64_t)blk * BLK;
         const bool in = lane < 32 && kk < left;
         const int64_t row = key_row<DENSE>(p, w.first + (int64_t)blk * BLK + kk, in, idx);
         const uint32_t word = (uint32_t)__ballot(row >= 0);   // lanes 0..31: keys 32 pw + lane
         if (lane == 0)
-            *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 1) * 16 + 4 * pw) = word;
-        return row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW) : (uint64_t)(uintptr_t)g_zero_row;
+            *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 3) * 16 + 4 * pw) = word;
+        const uint64_t ptr = row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW) : (uint64_t)(uintptr_t)g_zero_row;
+        if (lane < 32)
+            ptab[16 * (lane & 1) + 8 * (lane >> 4) + ((lane & 15) >> 1)] = ptr;
     };
-    // The wave's 18 row DMAs of block blk. Latent instruction i of subtile h moves keys 16 h + 2 i
-    // (lanes 0..31) and 16 h + 2 i + 1 (lanes 32..63) of the wave, chunk (lane % 32) ^ key; the
-    // two key pointers are broadcast from their lanes. Rope instruction: key 16 h + lane % 16,
-    // chunk 32 + lane / 16, its pointer fetched from that key's lane.
-    auto issue_block = [&](int blk, uint64_t kp) {
-        const int lo = (int)(uint32_t)kp, hi = (int)(uint32_t)(kp >> 32);
+    // The wave's 18 row DMAs of the block whose pointers are in the table. Latent instruction i of
+    // subtile h moves keys 16 h + 2 i (lanes 0..31) and 16 h + 2 i + 1 (lanes 32..63), chunk
+    // (lane % 32) ^ key; rope instruction: key 16 h + lane % 16, chunk 32 + lane / 16.
+    auto issue_block = [&](int blk) {
         const int hb = lane >> 5;
         const uint32_t boff = 16u * (uint32_t)((lane & 31) ^ hb);   // 16 ((lane % 32) ^ key) ^ 32 i
 #pragma unroll
         for (int h = 0; h < 2; h++) {
+            const uint64_t* row8 = ptab + 16 * hb + 8 * h;   // the 8 keys of this lane's half
+            uint64_t kp[8];
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const v4i two = *reinterpret_cast<const v4i*>(row8 + 2 * m);
+                kp[2 * m] = ((uint64_t)(uint32_t)two.y << 32) | (uint32_t)two.x;
+                kp[2 * m + 1] = ((uint64_t)(uint32_t)two.w << 32) | (uint32_t)two.z;
+            }
+            const int rk = lane & 15;   // rope key 16 h + rk
+            const uint64_t rp = ptab[16 * (rk & 1) + 8 * h + (rk >> 1)];
             const uint8_t* src[9];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int ka = 16 * h + 2 * i;
-                const uint64_t pa = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, ka) << 32) |
-                                    (uint32_t)__builtin_amdgcn_readlane(lo, ka);
-                const uint64_t pb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, ka + 1) << 32) |
-                                    (uint32_t)__builtin_amdgcn_readlane(lo, ka + 1);
-                const uint64_t base = hb ? pb : pa;
-                src[i] = reinterpret_cast<const uint8_t*>(base + (boff ^ (32u * i)));
-            }
-            const int sl = 16 * h + (lane & 15);
-            const uint64_t rp = ((uint64_t)(uint32_t)__shfl(hi, sl) << 32) | (uint32_t)__shfl(lo, sl);
+            for (int i = 0; i < 8; i++)
+                src[i] = reinterpret_cast<const uint8_t*>(kp[i] + (boff ^ (32u * i)));
             src[8] = reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (lane >> 4));
             dma9(src, lds_addr(smem + (blk & 1) * SLOT + (2 * pw + h) * SUBB));
         }
     };
     if (w.nblk > 0) {
-        int32_t idx0 = -1;
-        if (lane < 32 && 32 * pw + lane < w.mine)
-            idx0 = *index_ptr<DENSE>(p, w.g, w.first + 32 * pw + lane);
-        issue_block(0, key_ptrs(0, idx0));
+        const int kk = 32 * pw + lane;
+        int32_t idx0 = -1, idx1 = -1;
+        if (lane < 32 && kk < w.mine)
+            idx0 = *index_ptr<DENSE>(p, w.g, w.first + kk);
+        if (lane < 32 && BLK + kk < w.mine)
+            idx1 = *index_ptr<DENSE>(p, w.g, w.first + BLK + kk);
+        if (w.nblk > 2)
+            dma_indices(2);
+        key_ptrs(0, idx0);
+        issue_block(0);
         if (w.nblk > 1)
-            dma_indices(1);
+            key_ptrs(1, idx1);   // the table's reads for block 0 precede these writes (one wave)
     }
     lds_sync();   // Q0: the QK waves' staged query rows landed
     if (w.nblk > 0)
@@ -968,11 +991,15 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         float alpha[T];   // rescale factors of block i - 1, read before the gather (LDS latency)
 #pragma unroll
         for (int t = 0; t < T; t++) alpha[t] = xalpha[t * 16 + n16];
-        if (i + 1 < w.nblk) {
-            issue_block(i + 1, key_ptrs(i + 1, lane < 32 ? idx_lds[((i + 1) & 1) * BLK + 32 * pw + lane] : -1));
-        }
+        if (i + 1 < w.nblk)
+            issue_block(i + 1);
+        if (i + 3 < w.nblk)
+            dma_indices(i + 3);
+        // pointers of block i + 2 (its indices landed with this iteration's vmcnt wait; the table's
+        // reads for block i + 1 precede these writes; presence words of block b sit in slot b % 4,
+        // away from the QK waves' reads of block i)
         if (i + 2 < w.nblk)
-            dma_indices(i + 2);
+            key_ptrs(i + 2, lane < 32 ? idx_lds[(i & 1) * BLK + 32 * pw + lane] : -1);
         if (i >= 1) {   // rescale O for block i - 1 while the QK waves issue their MFMAs
 #pragma unroll
             for (int t = 0; t < T; t++) {
@@ -1323,6 +1350,19 @@ mla_plan_t choose_plan(int groups, int tiles_per_group, int64_t max_keys)
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+// The magic number and shifts of division by d (1 <= d < 2^31) for 32-bit dividends: with
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, s1 = min(l, 1), s2 = max(l - 1, 0)
+// (Granlund and Montgomery 1994, Figure 4.1).
+void set_page_division(Params& p, int d)
+{
+    int l = 0;
+    while ((1ll << l) < d)
+        l++;
+    p.pg_magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - (uint64_t)d)) / (uint64_t)d + 1);
+    p.pg_s1 = l < 1 ? l : 1;
+    p.pg_s2 = l - 1 > 0 ? l - 1 : 0;
+}
+
 template <int T, bool DENSE>
 hipError_t launch_t(const Params& p, hipStream_t stream)
 {
@@ -1431,7 +1471,8 @@ mla_status_t mla_plan_dense(int B, int Q, int H, int max_pages, int page_size, m
 {
     if (!plan)
         return MLA_ERR_NULL;
-    if (B < 0 || Q < 1 || H < 16 || H % 16 != 0 || max_pages < 1 || page_size < 1)
+    if (B < 0 || Q < 1 || H < 16 || H % 16 != 0 || max_pages < 1 || page_size < 1 ||
+        (int64_t)max_pages * page_size > INT32_MAX)
         return MLA_ERR_SHAPE;
     *plan = choose_plan(B > 0 ? B : 1, Q * H / 16, (int64_t)max_pages * page_size);
     return MLA_OK;
@@ -1455,7 +1496,7 @@ mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* 
     mla_status_t st = common_checks(q, kv, B, Q, H, o, lse);
     if (st != MLA_OK || B == 0)
         return st;
-    if (max_pages < 1 || kv->page_size < 1)
+    if (max_pages < 1 || kv->page_size < 1 || (int64_t)max_pages * kv->page_size > INT32_MAX)
         return MLA_ERR_SHAPE;
     if (!block_table || !seq_lens)
         return MLA_ERR_NULL;
@@ -1473,6 +1514,7 @@ mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* 
     p.kv = (const uint8_t*)kv->data;
     p.num_rows = kv->num_rows;
     p.page_size = kv->page_size;
+    set_page_division(p, kv->page_size);
     p.table = block_table;
     p.max_pages = max_pages;
     p.seq_lens = seq_lens;
@@ -1519,6 +1561,7 @@ mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t*
     p.kv = (const uint8_t*)kv->data;
     p.num_rows = kv->num_rows;
     p.page_size = 1;
+    set_page_division(p, 1);
     p.rows = rows;
     p.K = K;
     p.valid = valid;

@@ -66,6 +66,8 @@ DENSE_CASES = [
     (1, 2, 128, [2100], 64, (5, 4)),
     (2, 1, 16, [63, 65], 16, (2, 1)),
     (1, 2, 16, [200], 48, (3, 1)),
+    (2, 1, 16, [300, 517], 7, (2, 1)),
+    (1, 1, 32, [1000], 256, (1, 2)),
 ]
 
 
