@@ -40,7 +40,8 @@ typedef enum {
     MLA_ERR_WORKSPACE = 4,   /* the workspace is missing or smaller than mla_workspace_bytes() */
     MLA_ERR_UNSUPPORTED = 5, /* a plan the kernels do not implement (tiles not 1/2/4 or not
                                 dividing the row tiles, splits outside [1, 4096], an unknown mode,
-                                a balanced plan over more than 36863 groups or 2^31 blocks) */
+                                a balanced plan over more than 36863 groups or 2^31 virtual
+                                blocks) */
     MLA_ERR_LAUNCH = 6       /* the kernel launch failed (HIP error) */
 } mla_status_t;
 
@@ -59,14 +60,17 @@ typedef struct {
  * ceil(n / 128) blocks of 128.
  *   MLA_SPLIT_UNIFORM   the pages' rule: every group in `splits` = S parts, part s holding keys
  *                       [s*per, min(n, (s+1)*per)), per = ceil(n / S).
- *   MLA_SPLIT_BALANCED  the blocks of all groups, concatenated in group order (U blocks), are cut
- *                       into `splits` = P pieces of equal size: piece p holds global blocks
- *                       [floor(p*U/P), floor((p+1)*U/P)). A group is split where a piece boundary
- *                       falls inside it (so split boundaries are multiples of 128 keys) and each
- *                       piece goes to one workgroup per tile set, which evens out ragged key counts.
- *                       A group's result then depends on the key counts of the whole call (still
+ *   MLA_SPLIT_BALANCED  every group counts as a run of 4 + (its blocks) virtual blocks, the 4
+ *                       standing for the fixed cost of one work item; the runs, concatenated in
+ *                       group order (V virtual blocks), are cut into `splits` = P pieces of equal
+ *                       size: piece p holds virtual blocks [floor(p*V/P), floor((p+1)*V/P)), and
+ *                       block j of a group whose run starts at virtual block r sits at r + 4 + j.
+ *                       A group is split where a piece boundary falls among its blocks (so split
+ *                       boundaries are multiples of 128 keys) and each piece goes to one
+ *                       workgroup per tile set, which evens out ragged key counts. A group's
+ *                       result then depends on the key counts of the whole call (still
  *                       bit-identical for identical inputs). At most 36863 groups, and fewer than
- *                       2^31 blocks in total (counted at each group's maximum key count). */
+ *                       2^31 virtual blocks in total (counted at each group's maximum key count). */
 enum { MLA_SPLIT_UNIFORM = 0, MLA_SPLIT_BALANCED = 1 };
 
 /* A launch plan. splits: S >= 1 (see mode); tiles: 16-row query tiles per workgroup (1, 2 or 4),

@@ -150,6 +150,14 @@ __device__ inline int opaque(int x)
     return x;
 }
 
+// This lane's index in the wave, computed afresh (mbcnt) where it is used. In the gather loop any
+// scratch reload would wait (vmcnt is in order) for the row DMAs issued before it, so lane-derived
+// values there are recomputed rather than held live where the compiler might spill them.
+__device__ inline int lane_now()
+{
+    return opaque((int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+}
+
 // x / y from r = 1 / y (rounded): the product x r, then one correction with its exactly computed
 // residual x - q y (fma). Exact whenever x / y is representable (a single key's O / l = v), and
 // within an ulp otherwise; three operations instead of a full division per element.
@@ -362,29 +370,33 @@ __device__ inline void decode_uniform(const Params& p, int unit, int ts, Work& w
     w.row_base = (int64_t)w.g * p.rows_per_group;
 }
 
-// Balanced plan: the groups' 128-key blocks, concatenated in group order (U of them), are cut into
-// S pieces of equal size (piece q = blocks [floor(q U / S), floor((q + 1) U / S))), one per
-// workgroup (and tile set). A group is split where piece boundaries fall inside it; a piece walks
-// the groups it overlaps in order. An empty group belongs to the piece holding the block where it
-// would start (the last piece at the end; with no block at all, piece floor(g S / groups)).
+// Balanced plan: every group is a run of ITEM_BLOCKS + (its 128-key blocks) virtual blocks, the
+// leading ITEM_BLOCKS standing for the fixed cost of a work item (query staging and conversion,
+// pipeline fill, output); the runs, concatenated in group order (V virtual blocks), are cut into
+// S pieces of equal size (piece q = [floor(q V / S), floor((q + 1) V / S))), one per workgroup
+// (and tile set). A group's real blocks go to the pieces their virtual positions fall in, so a
+// group is split where piece boundaries fall among its blocks; a piece walks the groups it
+// overlaps in order. An empty group belongs to the piece holding the start of its run.
+constexpr int ITEM_BLOCKS = 4;
+
 struct Span {
     int g_lo, g_hi;   // the piece's groups
-    int64_t pre_lo;   // blocks before group g_lo
-    int64_t U;        // blocks of all groups
+    int64_t pre_lo;   // virtual blocks before group g_lo
+    int64_t V;        // virtual blocks of all groups
 };
 
-__device__ inline int piece_of(int64_t b, int64_t U, int np) { return (int)(((b + 1) * np - 1) / U); }
+__device__ inline int piece_of(int64_t v, int64_t V, int np) { return (int)(((v + 1) * np - 1) / V); }
 
-__device__ inline int first_piece(int64_t pre, int g, int64_t U, int np, int groups)
+// The pieces holding the first and the last real block of a group whose run starts at virtual
+// block pre (nb real blocks); an empty group: the piece holding the start of its run.
+__device__ inline int first_piece(int64_t pre, int64_t nb, int64_t V, int np)
 {
-    if (U == 0)
-        return (int)((int64_t)g * np / groups);
-    return pre < U ? piece_of(pre, U, np) : np - 1;
+    return piece_of(nb > 0 ? pre + ITEM_BLOCKS : pre, V, np);
 }
 
-__device__ inline int last_piece(int64_t pre, int64_t nb, int g, int64_t U, int np, int groups)
+__device__ inline int last_piece(int64_t pre, int64_t nb, int64_t V, int np)
 {
-    return nb > 0 ? piece_of(pre + nb - 1, U, np) : first_piece(pre, g, U, np, groups);
+    return piece_of(nb > 0 ? pre + ITEM_BLOCKS + nb - 1 : pre, V, np);
 }
 
 __device__ inline int wave_sum_i32(int v)
@@ -394,9 +406,9 @@ __device__ inline int wave_sum_i32(int v)
     return v;
 }
 
-// The piece's groups, by the whole workgroup: a block-wide prefix sum of the groups' block counts
+// The piece's groups, by the whole workgroup: a block-wide prefix sum of the groups' run lengths
 // into the (still unused) KV slots, then counts of the groups wholly before the piece and of the
-// groups starting at or before it. The host bounds U below 2^31 and the groups by the slots' size.
+// groups starting at or before it. The host bounds V below 2^31 and the groups by the slots' size.
 // Contains workgroup barriers; every thread returns the same span.
 template <bool DENSE>
 __device__ Span piece_span(const Params& p, uint8_t* smem, int piece, int tid, int lane)
@@ -409,8 +421,8 @@ __device__ Span piece_span(const Params& p, uint8_t* smem, int piece, int tid, i
     int carry = 0;
     for (int base = 0; base < G; base += THREADS) {
         const int g = base + tid;
-        const int nb = g < G ? (int)nblocks(group_keys<DENSE>(p, g)) : 0;
-        int incl = nb;   // inclusive prefix within the wave
+        const int len = g < G ? ITEM_BLOCKS + (int)nblocks(group_keys<DENSE>(p, g)) : 0;
+        int incl = len;   // inclusive prefix within the wave
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int t = __shfl_up(incl, d);
@@ -428,13 +440,13 @@ __device__ Span piece_span(const Params& p, uint8_t* smem, int piece, int tid, i
             chunk += v;
         }
         if (g < G)
-            pre[g] = before + incl - nb;
+            pre[g] = before + incl - len;
         carry += chunk;
         __syncthreads();   // the wave sums are reused by the next chunk
     }
-    const int U = carry;
+    const int V = carry;
     if (tid == 0) {
-        pre[G] = U;
+        pre[G] = V;
         red[8] = 0;
         red[9] = 0;
     }
@@ -442,9 +454,9 @@ __device__ Span piece_span(const Params& p, uint8_t* smem, int piece, int tid, i
     int lo = 0, hi = 0;
     for (int g = tid; g < G; g += THREADS) {
         const int pg = pre[g];
-        const int nb = pre[g + 1] - pg;
-        lo += last_piece(pg, nb, g, U, np, G) < piece ? 1 : 0;
-        hi += first_piece(pg, g, U, np, G) <= piece ? 1 : 0;
+        const int nb = pre[g + 1] - pg - ITEM_BLOCKS;
+        lo += last_piece(pg, nb, V, np) < piece ? 1 : 0;
+        hi += first_piece(pg, nb, V, np) <= piece ? 1 : 0;
     }
     lo = wave_sum_i32(lo);
     hi = wave_sum_i32(hi);
@@ -457,12 +469,12 @@ __device__ Span piece_span(const Params& p, uint8_t* smem, int piece, int tid, i
     sp.g_lo = __builtin_amdgcn_readfirstlane(red[8]);
     sp.g_hi = __builtin_amdgcn_readfirstlane(red[9]) - 1;
     sp.pre_lo = __builtin_amdgcn_readfirstlane(pre[sp.g_lo]);
-    sp.U = U;
+    sp.V = V;
     __syncthreads();   // every wave has read the span before the slots fill
     return sp;
 }
 
-// Item of group g (whose blocks start at global block pre) in piece `piece`.
+// Item of group g (whose run starts at virtual block pre) in piece `piece`.
 template <bool DENSE>
 __device__ inline void balanced_item(const Params& p, int piece, int ts, int g, int64_t pre,
                                      const Span& sp, Work& w)
@@ -472,13 +484,16 @@ __device__ inline void balanced_item(const Params& p, int piece, int ts, int g, 
     w.ts = ts;
     w.n_grp = group_keys<DENSE>(p, g);
     const int64_t nb = nblocks(w.n_grp);
-    const int fp = first_piece(pre, g, sp.U, np, p.groups);
-    const int lp = last_piece(pre, nb, g, sp.U, np, p.groups);
+    const int fp = first_piece(pre, nb, sp.V, np);
+    const int lp = last_piece(pre, nb, sp.V, np);
     int64_t lo = 0, hi = 0;
     if (nb > 0) {
-        const int64_t a0 = (int64_t)piece * sp.U / np, a1 = (int64_t)(piece + 1) * sp.U / np;
-        lo = (a0 > pre ? a0 : pre) - pre;
-        hi = (a1 < pre + nb ? a1 : pre + nb) - pre;
+        const int64_t b0 = pre + ITEM_BLOCKS;   // virtual position of the group's first block
+        const int64_t a0 = (int64_t)piece * sp.V / np, a1 = (int64_t)(piece + 1) * sp.V / np;
+        lo = (a0 > b0 ? a0 : b0) - b0;
+        hi = (a1 < b0 + nb ? a1 : b0 + nb) - b0;
+        if (lo > nb)
+            lo = nb;
         if (hi < lo)
             hi = lo;
     }
@@ -724,7 +739,6 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         const bool work = active && i < w.nblk;
         v4f acc[TW][KS];
         float bmax[TW];
-        uint32_t vis[TW];
         if (work) {
             // presence bits of the block's keys, read before the MFMAs so that the LDS latency
             // hides behind them; this lane's 16 keys: bit 4u + jj <-> key 16 (4 kh + u) + 4 grp + jj
@@ -774,31 +788,34 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                         acc[j][sub] = mfma(kf[(f - 1) % RING], qlo[j][st], acc[j][sub]);
                 }
             }
-            uint32_t present = 0;
-#pragma unroll
-            for (int u = 0; u < KS; u++) {
-                // subtile 4 kh + u: word 2 kh + u / 2 of the block, half u % 2
-                present |= (((uint32_t)mw[u >> 1] >> (16 * (u & 1) + 4 * grp)) & 0xFu) << (4 * u);
-            }
+            // all 64 keys of the half present (the words are the same in every lane) and the
+            // block wholly before both tiles' bounds: nothing to mask
+            const uint32_t all_in = (uint32_t)__builtin_amdgcn_readfirstlane(mw.x) &
+                                    (uint32_t)__builtin_amdgcn_readfirstlane(mw.y);
             // ---- mask, this half's block maxima (in-lane, then across the 4 k-groups), to LDS.
             // The row scale is positive, so max(s * scale) = scale * max(s) exactly. ----
 #pragma unroll
             for (int j = 0; j < TW; j++) {
                 const int lr = lim[j] - i * BLK;      // keys of the block before the tile's bound
-                const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
-                vis[j] = present;
+                if (!(all_in == 0xFFFFFFFFu && lr >= BLK)) {
+                    uint32_t vis = 0;
 #pragma unroll
-                for (int u = 0; u < KS; u++) {
-                    const int keep = lim_rel - (16 * (KS * kh + u) + 4 * grp);   // of the 4 in bound
-                    const uint32_t nib = keep >= 4 ? 0xFu : (keep <= 0 ? 0u : ((1u << keep) - 1u));
-                    vis[j] &= ~(0xFu << (4 * u)) | (nib << (4 * u));
-                }
-                if (!__all(vis[j] == 0xFFFFu)) {
+                    for (int u = 0; u < KS; u++) {
+                        // subtile 4 kh + u: word 2 kh + u / 2 of the block, half u % 2
+                        vis |= (((uint32_t)mw[u >> 1] >> (16 * (u & 1) + 4 * grp)) & 0xFu) << (4 * u);
+                    }
+                    const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
+#pragma unroll
+                    for (int u = 0; u < KS; u++) {
+                        const int keep = lim_rel - (16 * (KS * kh + u) + 4 * grp);   // of the 4 in bound
+                        const uint32_t nib = keep >= 4 ? 0xFu : (keep <= 0 ? 0u : ((1u << keep) - 1u));
+                        vis &= ~(0xFu << (4 * u)) | (nib << (4 * u));
+                    }
 #pragma unroll
                     for (int u = 0; u < KS; u++)
 #pragma unroll
                         for (int jj = 0; jj < 4; jj++)
-                            acc[j][u][jj] = ((vis[j] >> (4 * u + jj)) & 1u) ? acc[j][u][jj] : neg_inf;
+                            acc[j][u][jj] = ((vis >> (4 * u + jj)) & 1u) ? acc[j][u][jj] : neg_inf;
                 }
                 float bm = neg_inf;
 #pragma unroll
@@ -900,9 +917,10 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
     uint64_t* ptab = reinterpret_cast<uint64_t*>(smem + L::OFF_PTAB) + 32 * pw;
     auto dma_indices = [&](int blk) {  // raw indices of block blk -> idx slot blk % 2
-        const int kk = 32 * pw + lane;
+        const int ln = lane_now();
+        const int kk = 32 * pw + ln;
         const int64_t left = w.mine - (int64_t)blk * BLK;
-        if (lane < 32 && kk < left)
+        if (ln < 32 && kk < left)
             dma4(index_ptr<DENSE>(p, w.g, w.first + (int64_t)blk * BLK + kk),
                  lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * pw * 4));
     };
@@ -911,23 +929,25 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     // 16 h + 2 i and 16 h + 2 i + 1 of the wave) sit at entries 8 h + i and 16 + 8 h + i. The
     // presence word of the wave's 32 keys goes to LDS for the QK waves.
     auto key_ptrs = [&](int blk, int32_t idx) {
-        const int kk = 32 * pw + lane;
+        const int ln = lane_now();
+        const int kk = 32 * pw + ln;
         const int64_t left = w.mine - (int64_t)blk * BLK;
-        const bool in = lane < 32 && kk < left;
+        const bool in = ln < 32 && kk < left;
         const int64_t row = key_row<DENSE>(p, w.first + (int64_t)blk * BLK + kk, in, idx);
         const uint32_t word = (uint32_t)__ballot(row >= 0);   // lanes 0..31: keys 32 pw + lane
-        if (lane == 0)
+        if (ln == 0)
             *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 3) * 16 + 4 * pw) = word;
         const uint64_t ptr = row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW) : (uint64_t)(uintptr_t)g_zero_row;
-        if (lane < 32)
-            ptab[16 * (lane & 1) + 8 * (lane >> 4) + ((lane & 15) >> 1)] = ptr;
+        if (ln < 32)
+            ptab[16 * (ln & 1) + 8 * (ln >> 4) + ((ln & 15) >> 1)] = ptr;
     };
     // The wave's 18 row DMAs of the block whose pointers are in the table. Latent instruction i of
     // subtile h moves keys 16 h + 2 i (lanes 0..31) and 16 h + 2 i + 1 (lanes 32..63), chunk
     // (lane % 32) ^ key; rope instruction: key 16 h + lane % 16, chunk 32 + lane / 16.
     auto issue_block = [&](int blk) {
-        const int hb = lane >> 5;
-        const uint32_t boff = 16u * (uint32_t)((lane & 31) ^ hb);   // 16 ((lane % 32) ^ key) ^ 32 i
+        const int ln = lane_now();
+        const int hb = ln >> 5;
+        const uint32_t boff = 16u * (uint32_t)((ln & 31) ^ hb);   // 16 ((lane % 32) ^ key) ^ 32 i
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             const uint64_t* row8 = ptab + 16 * hb + 8 * h;   // the 8 keys of this lane's half
@@ -938,13 +958,13 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                 kp[2 * m] = ((uint64_t)(uint32_t)two.y << 32) | (uint32_t)two.x;
                 kp[2 * m + 1] = ((uint64_t)(uint32_t)two.w << 32) | (uint32_t)two.z;
             }
-            const int rk = lane & 15;   // rope key 16 h + rk
+            const int rk = ln & 15;   // rope key 16 h + rk
             const uint64_t rp = ptab[16 * (rk & 1) + 8 * h + (rk >> 1)];
             const uint8_t* src[9];
 #pragma unroll
             for (int i = 0; i < 8; i++)
                 src[i] = reinterpret_cast<const uint8_t*>(kp[i] + (boff ^ (32u * i)));
-            src[8] = reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (lane >> 4));
+            src[8] = reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (ln >> 4));
             dma9(src, lds_addr(smem + (blk & 1) * SLOT + (2 * pw + h) * SUBB));
         }
     };
@@ -971,7 +991,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     // 8 bytes for odd n16. Its byte offset in the slot is (vb + 128 (pw ^ rb)) ^ 16 c plus
     // sp SUBB + 4096 rb, with vb = 2 grp SUBB + 528 m + 8 (n16 % 2): 16 (c ^ m) = 16 c ^ 16 m, and
     // no other term has bits 4..8 set.
-    const int vb = 2 * grp * SUBB + 528 * (n16 >> 1) + 8 * (n16 & 1);
+    auto vbase = [](int ln) { return 2 * (ln >> 4) * SUBB + 528 * ((ln & 15) >> 1) + 8 * (ln & 1); };
     auto load_vt = [&](int slot, int c, int vb0, int vb1) {
         v2i tr[4];
 #pragma unroll
@@ -990,7 +1010,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         lds_sync();   // B1: block i landed; P of block i - 1 published
         float alpha[T];   // rescale factors of block i - 1, read before the gather (LDS latency)
 #pragma unroll
-        for (int t = 0; t < T; t++) alpha[t] = xalpha[t * 16 + n16];
+        for (int t = 0; t < T; t++) alpha[t] = xalpha[t * 16 + (lane_now() & 15)];
         if (i + 1 < w.nblk)
             issue_block(i + 1);
         if (i + 3 < w.nblk)
@@ -999,7 +1019,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         // reads for block i + 1 precede these writes; presence words of block b sit in slot b % 4,
         // away from the QK waves' reads of block i)
         if (i + 2 < w.nblk)
-            key_ptrs(i + 2, lane < 32 ? idx_lds[(i & 1) * BLK + 32 * pw + lane] : -1);
+            key_ptrs(i + 2, lane_now() < 32 ? idx_lds[(i & 1) * BLK + 32 * pw + lane_now()] : -1);
         if (i >= 1) {   // rescale O for block i - 1 while the QK waves issue their MFMAs
 #pragma unroll
             for (int t = 0; t < T; t++) {
@@ -1011,25 +1031,28 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
             }
         }
         lds_sync();   // B2: the QK waves have issued their MFMAs of block i
+        // the lane's V^T base for block i's slot (recomputed here, not held across the loop)
+        const int b = (i & 1) * SLOT + vbase(lane_now());
         if (i >= 1) {
+            // chunk by chunk over all tiles, so that each V^T fragment is reloaded with block i as
+            // soon as its MFMAs have issued
+            v8i pb[T];
 #pragma unroll
             for (int t = 0; t < T; t++) {
-                const int lo = opaque(lane);
+                const int lo = lane_now();
                 const int off = L::OFF_P + t * PTILE + (lo & 15) * PPITCH + 32 * (lo >> 4);
-                const v8i pb = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
-#pragma unroll
-                for (int c = 0; c < 8; c++) O[t][c] = mfma(vt[c], pb, O[t][c]);
+                pb[t] = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
             }
-        }
-        if (i < w.nblk) {
 #pragma unroll
             for (int c = 0; c < 8; c++) {
-                // the lane's bases for this slot (recomputed here, not held across the loop)
-                int b = vb;
-                asm volatile("" : "+v"(b));
-                b += (i & 1) * SLOT;
-                vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
+#pragma unroll
+                for (int t = 0; t < T; t++) O[t][c] = mfma(vt[c], pb[t], O[t][c]);
+                if (i < w.nblk)
+                    vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
             }
+        } else if (i < w.nblk) {
+#pragma unroll
+            for (int c = 0; c < 8; c++) vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
         }
         lds_sync();   // B3: P of block i - 1 and V^T of block i are in registers
     }
@@ -1242,7 +1265,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             stage_q<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
             Work w;
             item(pi, g, pre, w);
-            pre += nblocks(w.n_grp);
+            pre += ITEM_BLOCKS + nblocks(w.n_grp);
             qk_role<T, DENSE>(pi, smem, w, wave, li);
             finish_item<T>(pi, smem, w, tid);
             __syncthreads();   // the next item reuses every LDS area
@@ -1253,7 +1276,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             const Params& pi = fresh_params();
             Work w;
             item(pi, g, pre, w);
-            pre += nblocks(w.n_grp);
+            pre += ITEM_BLOCKS + nblocks(w.n_grp);
             v4f O[T][8];
 #pragma unroll
             for (int t = 0; t < T; t++)
@@ -1315,12 +1338,12 @@ int choose_tiles(int tiles_per_group)
 // A plan from shapes only. One workgroup fills a CU's LDS, so 256 workgroups cover the chip once.
 // Groups of at most two 128-key blocks: one workgroup per group and tile set (uniform, S = 1).
 // Longer groups: either one workgroup per group and tile set (S = 1, no partials to merge) or a
-// balanced plan of 256 / tilesets pieces, which evens out ragged key counts but pays for every
-// extra work item and merge (measured on MI355X at about ITEM_COST blocks per piece). The cost is
-// estimated in 128-key blocks per CU with every group at its maximum key count. For more groups
-// than a balanced plan stages, uniform splits up to one workgroup per CU.
-constexpr int64_t ITEM_COST = 10;
-
+// balanced plan of 256 / tilesets pieces, which evens out ragged key counts but adds work items
+// and merges. The cost of each is estimated in 128-key blocks per CU, every group at its maximum
+// key count and every work item costing ITEM_BLOCKS more; a balanced piece also pays for the
+// group it continues and for the FP32 partials and their merge, about two items (measured on
+// MI355X). For more groups than a balanced plan stages, uniform splits up to one workgroup per
+// CU.
 mla_plan_t choose_plan(int groups, int tiles_per_group, int64_t max_keys)
 {
     mla_plan_t pl{};
@@ -1331,10 +1354,10 @@ mla_plan_t choose_plan(int groups, int tiles_per_group, int64_t max_keys)
     pl.mode = MLA_SPLIT_UNIFORM;
     if (max_keys <= 2 * BLK)
         return pl;
-    if (groups <= MAX_BALANCED_GROUPS && (int64_t)groups * mb < INT32_MAX) {
+    if (groups <= MAX_BALANCED_GROUPS && (int64_t)groups * (mb + ITEM_BLOCKS) < INT32_MAX) {
         const int64_t wgs = (int64_t)groups * tilesets;
-        const int64_t whole = (wgs + 255) / 256 * mb;           // S = 1: rounds of workgroups
-        const int64_t balanced = (wgs * mb + 255) / 256 + ITEM_COST;
+        const int64_t whole = (wgs + 255) / 256 * (mb + ITEM_BLOCKS);   // S = 1: rounds of workgroups
+        const int64_t balanced = (wgs * (mb + ITEM_BLOCKS) + 255) / 256 + 2 * ITEM_BLOCKS;
         if (balanced < whole) {
             pl.splits = 256 / tilesets > 1 ? 256 / tilesets : 1;
             pl.mode = MLA_SPLIT_BALANCED;
@@ -1413,7 +1436,8 @@ mla_status_t finish_plan(const mla_plan_t* in, mla_plan_t chosen, int dense, int
     if (pl.mode != MLA_SPLIT_UNIFORM && pl.mode != MLA_SPLIT_BALANCED)
         return MLA_ERR_UNSUPPORTED;
     if (pl.mode == MLA_SPLIT_BALANCED &&
-        (groups > MAX_BALANCED_GROUPS || (int64_t)groups * ((max_keys + BLK - 1) / BLK) >= INT32_MAX))
+        (groups > MAX_BALANCED_GROUPS ||
+         (int64_t)groups * ((max_keys + BLK - 1) / BLK + ITEM_BLOCKS) >= INT32_MAX))
         return MLA_ERR_UNSUPPORTED;
     if (pl.splits > 1) {
         const WsLayout w = ws_layout(dense, B, Q, H, pl);

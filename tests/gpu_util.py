@@ -62,17 +62,23 @@ def group_keys(x) -> np.ndarray:
     return np.clip(x.valid.reshape(-1).astype(np.int64), 0, x.rows.shape[2])
 
 
+ITEM_BLOCKS = 4   # virtual blocks a key group's run starts with under the balanced plan
+
+
 def balanced_cuts(x, pieces: int):
     """Split starts per key group under the balanced plan, from its definition in the C header:
-    the groups' 128-key blocks in group order (U of them) are cut at global blocks
-    floor(p U / pieces), p = 1 .. pieces - 1; a group is split at every cut strictly inside it."""
+    each group is a run of ITEM_BLOCKS + (its 128-key blocks) virtual blocks, the runs in group
+    order (V of them) are cut at virtual blocks floor(p V / pieces), p = 1 .. pieces - 1, and
+    block j of a group whose run starts at r sits at r + ITEM_BLOCKS + j; a group is split at
+    every cut that falls strictly inside its blocks."""
     nb = -(-group_keys(x) // CHUNK)
-    U = int(nb.sum())
-    cuts_global = sorted({p * U // pieces for p in range(1, pieces)})
+    V = int((nb + ITEM_BLOCKS).sum())
+    cuts_global = sorted({p * V // pieces for p in range(1, pieces)})
     out, pre = [], 0
     for n in nb.tolist():
-        out.append([0] + [CHUNK * (b - pre) for b in cuts_global if pre < b < pre + n])
-        pre += n
+        b0 = pre + ITEM_BLOCKS
+        out.append([0] + [CHUNK * (c - b0) for c in cuts_global if b0 < c < b0 + n])
+        pre += ITEM_BLOCKS + n
     return out
 
 
