@@ -1099,34 +1099,7 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid)
     const float neg_inf = -INFINITY;
     const int lane = tid & 63, c = tid >> 6;
     const int n16 = lane & 15, grp = lane >> 4;
-    float top[T], total[T];
-#pragma unroll
-    for (int t = 0; t < T; t++) {
-        top[t] = neg_inf;
-        total[t] = 0.f;
-    }
-    // the rows' top maxima (loads of four contributors in flight at a time)
-    for (int q0 = 0; q0 < w.count; q0 += 4) {
-        float mq[4][T];
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int64_t prow = (int64_t)contributor_slot(p, w, q0 + u < w.count ? q0 + u : q0) * (T * 16);
-#pragma unroll
-            for (int t = 0; t < T; t++)
-                mq[u][t] = q0 + u < w.count ? p.ws_ml[(prow + 16 * t + n16) * 2] : neg_inf;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-#pragma unroll
-            for (int t = 0; t < T; t++) top[t] = fmaxf(top[t], mq[u][t]);
-    }
-    v4f acc[4][T];
-#pragma unroll
-    for (int pw = 0; pw < 4; pw++)
-#pragma unroll
-        for (int t = 0; t < T; t++) acc[pw][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    // per contributor: its (m, l) for the T rows and its 4 T partial loads all issue before any
-    // use (one wait per contributor); two contributors are in flight at a time
+    // per contributor: its (m, l) for the T rows and its 4 T partial loads
     struct Part {
         v2f ml[T];
         v4f x[4][T];
@@ -1142,6 +1115,32 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid)
             for (int t = 0; t < T; t++)
                 pt.x[pw][t] = *reinterpret_cast<const v4f*>(p.ws_o + partial_o_offset<T>(slot, pw, t, c, lane));
     };
+    // One round trip for the common case: the first two contributors' partials and every
+    // contributor's maximum are requested before any of them is used.
+    Part a, b;
+    load_part(0, a);
+    if (w.count > 1)
+        load_part(1, b);
+    float top[T], total[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        top[t] = a.ml[t][0];
+        total[t] = 0.f;
+    }
+    for (int q = 2; q < w.count; q++) {
+        const int64_t prow = (int64_t)contributor_slot(p, w, q) * (T * 16);
+#pragma unroll
+        for (int t = 0; t < T; t++) top[t] = fmaxf(top[t], p.ws_ml[(prow + 16 * t + n16) * 2]);
+    }
+    if (w.count > 1) {
+#pragma unroll
+        for (int t = 0; t < T; t++) top[t] = fmaxf(top[t], b.ml[t][0]);
+    }
+    v4f acc[4][T];
+#pragma unroll
+    for (int pw = 0; pw < 4; pw++)
+#pragma unroll
+        for (int t = 0; t < T; t++) acc[pw][t] = v4f{0.f, 0.f, 0.f, 0.f};
     auto add_part = [&](const Part& pt) {
 #pragma unroll
         for (int t = 0; t < T; t++) {
@@ -1153,16 +1152,18 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid)
             for (int pw = 0; pw < 4; pw++) acc[pw][t] = acc[pw][t] + wq * pt.x[pw][t];
         }
     };
-    int q = 0;
+    // in split order; two contributors in flight at a time
+    add_part(a);
+    if (w.count > 1)
+        add_part(b);
+    int q = 2;
     for (; q + 1 < w.count; q += 2) {
-        Part a, b;
         load_part(q, a);
         load_part(q + 1, b);
         add_part(a);
         add_part(b);
     }
     if (q < w.count) {
-        Part a;
         load_part(q, a);
         add_part(a);
     }
