@@ -370,6 +370,32 @@ __device__ inline void decode_uniform(const Params& p, int unit, int ts, Work& w
     w.row_base = (int64_t)w.g * p.rows_per_group;
 }
 
+// Raw indices of the first two blocks, requested before the key count is known: for split 0 of
+// a uniform plan the keys start at 0, so lanes 0..31 of PV wave pw load those of keys 32 pw + lane
+// and 128 + 32 pw + lane that lie within the list's capacity (their count mask comes later).
+struct FirstIdx {
+    int32_t i0, i1;
+    bool ok;
+};
+
+template <bool DENSE>
+__device__ inline FirstIdx first_indices(const Params& p, int unit, int pw)
+{
+    FirstIdx f{-1, -1, false};
+    if (p.balanced || unit >= p.groups)
+        return f;
+    f.ok = true;
+    const int ln = lane_now();
+    const int kk = 32 * pw + ln;
+    const int g = unit;
+    const int64_t cap = DENSE ? (int64_t)p.max_pages * p.page_size : (int64_t)p.K;
+    if (ln < 32 && kk < cap)
+        f.i0 = *index_ptr<DENSE>(p, g, kk);
+    if (ln < 32 && BLK + kk < cap)
+        f.i1 = *index_ptr<DENSE>(p, g, BLK + kk);
+    return f;
+}
+
 // Balanced plan: every group is a run of ITEM_BLOCKS + (its 128-key blocks) virtual blocks, the
 // leading ITEM_BLOCKS standing for the fixed cost of a work item (query staging and conversion,
 // pipeline fill, output); the runs, concatenated in group order (V virtual blocks), are cut into
@@ -903,7 +929,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
 // ---- PV waves: the gather, and O^T += V^T P^T for 128 latent columns of every tile ----
 template <int T, bool DENSE>
 __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Work& w, int pw,
-                                        int lane, v4f (&O)[T][8])
+                                        int lane, const FirstIdx& fi, v4f (&O)[T][8])
 {
     using L = Smem<T>;
     const int n16 = lane & 15;
@@ -970,11 +996,13 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     };
     if (w.nblk > 0) {
         const int kk = 32 * pw + lane;
-        int32_t idx0 = -1, idx1 = -1;
-        if (lane < 32 && kk < w.mine)
-            idx0 = *index_ptr<DENSE>(p, w.g, w.first + kk);
-        if (lane < 32 && BLK + kk < w.mine)
-            idx1 = *index_ptr<DENSE>(p, w.g, w.first + BLK + kk);
+        int32_t idx0 = fi.i0, idx1 = fi.i1;
+        if (!fi.ok) {
+            if (lane < 32 && kk < w.mine)
+                idx0 = *index_ptr<DENSE>(p, w.g, w.first + kk);
+            if (lane < 32 && BLK + kk < w.mine)
+                idx1 = *index_ptr<DENSE>(p, w.g, w.first + BLK + kk);
+        }
         if (w.nblk > 2)
             dma_indices(2);
         key_ptrs(0, idx0);
@@ -1275,6 +1303,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
         int64_t pre = sp.pre_lo;
         for (int g = sp.g_lo; g <= sp.g_hi; g++) {
             const Params& pi = fresh_params();
+            const FirstIdx fi = first_indices<DENSE>(pi, unit, wave - 4);
             Work w;
             item(pi, g, pre, w);
             pre += ITEM_BLOCKS + nblocks(w.n_grp);
@@ -1285,7 +1314,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
                 for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
             int li = lane;
             asm volatile("" : "+v"(li));
-            pv_role<T, DENSE>(pi, smem, w, wave - 4, li, O);
+            pv_role<T, DENSE>(pi, smem, w, wave - 4, li, fi, O);
             finish_item<T>(pi, smem, w, tid);
             __syncthreads();
         }
