@@ -67,6 +67,8 @@ constexpr float LN2 = 0.6931471805599453f;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -566,6 +568,18 @@ __device__ inline void stage_q(const Params& p, uint8_t* smem, int64_t row0, int
     }
 }
 
+// The power of two of a query row: the largest k with max|q| 2^k <= 448 (0 for a zero row), at most
+// 126 so that 2^-k stays a normal float (a row whose entries are all below 2^-117 keeps fewer bits).
+__device__ inline int row_shift(float amax)
+{
+    if (!(amax > 0.f))
+        return 0;
+    int e;
+    const float mm = frexpf(amax, &e);   // amax = mm * 2^e, mm in [0.5, 1)
+    const int k = (2.f * mm <= 1.75f) ? (9 - e) : (8 - e);
+    return k < 126 ? k : 126;
+}
+
 // Maximum over each aligned group of N lanes (N = 8, 16 or 32; every lane of a group gets it): quad
 // swaps and the half-row mirror (8), the row mirror (16), the 16-lane row swap (32).
 template <int N>
@@ -618,31 +632,27 @@ __device__ void convert_q(uint8_t* smem, int tid)
     m = group_max<LPR>(m);
     if (li == 0)
         reinterpret_cast<float*>(smem + L::OFF_P)[r] = m;
-    int ks = 0;
-    if (m > 0.f) {
-        int e;
-        const float mm = frexpf(m, &e);  // m = mm * 2^e, mm in [0.5, 1)
-        ks = (2.f * mm <= 1.75f) ? (9 - e) : (8 - e);
-    }
+    // gfx950's scaled conversions: bf16 / f32 -> E4M3 computes RNE(x / s) and E4M3 -> f32 computes
+    // v * s (both exact for a power of two s; checked bit for bit against the plain conversions of
+    // x / s and v * s on MI355X). With s = 2^-k: hi = E4M3(q 2^k), its value in q units hi 2^-k,
+    // the exact remainder d = q - hi 2^-k and lo = E4M3(d 2^k).
+    const float sinv = ldexpf(1.f, -row_shift(m));
 #pragma unroll
     for (int k = 0; k < UPL; k++) {
-        float x[8];
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-            x[2 * d] = ldexpf(bf16_to_f32((uint32_t)raw[k][d] & 0xFFFF), ks);
-            x[2 * d + 1] = ldexpf(bf16_to_f32((uint32_t)raw[k][d] >> 16), ks);
-        }
         uint32_t hi[2], lo[2];
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            const int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h], x[4 * h + 1], 0, false);
-            hi[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2], x[4 * h + 3], w0, true);
-            const float d4[4] = {x[4 * h] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 0),
-                                 x[4 * h + 1] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 1),
-                                 x[4 * h + 2] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 2),
-                                 x[4 * h + 3] - __builtin_amdgcn_cvt_f32_fp8((int)hi[h], 3)};
-            const int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(d4[0], d4[1], 0, false);
-            lo[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d4[2], d4[3], w1, true);
+            const uint32_t qa = (uint32_t)raw[k][2 * h], qb = (uint32_t)raw[k][2 * h + 1];   // q 4h .. 4h + 3
+            v2s hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2s{0, 0}, __builtin_bit_cast(v2bf, qa), sinv, false);
+            hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw, __builtin_bit_cast(v2bf, qb), sinv, true);
+            hi[h] = __builtin_bit_cast(uint32_t, hw);
+            const v2f b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi[h], sinv, false);
+            const v2f b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi[h], sinv, true);
+            const float d0 = bf16_to_f32(qa & 0xFFFF) - b01.x, d1 = bf16_to_f32(qa >> 16) - b01.y;
+            const float d2 = bf16_to_f32(qb & 0xFFFF) - b23.x, d3 = bf16_to_f32(qb >> 16) - b23.y;
+            v2s lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, d0, d1, sinv, false);
+            lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, d2, d3, sinv, true);
+            lo[h] = __builtin_bit_cast(uint32_t, lw);
         }
         raw[k] = v4i{(int)hi[0], (int)hi[1], (int)lo[0], (int)lo[1]};
     }
@@ -730,13 +740,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
             }
             qrope[j] = op(8);
             const float am = __uint_as_float(reinterpret_cast<const uint32_t*>(smem + L::OFF_P)[16 * t + n16]);
-            int k = 0;
-            if (am > 0.f) {
-                int e;
-                const float m = frexpf(am, &e);
-                k = (2.f * m <= 1.75f) ? (9 - e) : (8 - e);
-            }
-            row_scale[j] = ldexpf(p.scale_log2, -k);
+            row_scale[j] = ldexpf(p.scale_log2, -row_shift(am));
         }
     }
 
