@@ -28,15 +28,14 @@
 //          other key half through LDS), running max, P = 448 exp2(x - max) -> E4M3 into LDS, row
 //          sums of the unrounded P in a fixed order, rescale factor to LDS.
 //   PV waves 4..7: wave 4 + c owns latent columns 128c..128c+127 of every tile. They run one block
-//          behind: O^T += V^T P^T of block i - 1 while the QK waves work on block i, so on each
-//          SIMD one wave's softmax VALU overlaps the other's MFMAs. They also do the gather: raw
-//          indices DMA'd into LDS two blocks ahead, row pointers, 18 row DMAs per wave one block
-//          ahead into the other LDS slot, and they copy each block's V^T (ds_read_b64_tr_b8) into
-//          registers while its slot is valid, so two slots suffice.
-// Three barriers per block: B1 "block i landed, P of block i - 1 published", B2 "the QK waves have
-// issued the MFMAs of block i" (the PV waves' MFMAs of block i - 1 then overlap the QK waves'
-// softmax) and B3 "the PV waves hold P of block i - 1 and V^T of block i in registers" (the QK
-// waves then write P of block i).
+//          behind: after issuing the gather of block i + 1 (raw indices DMA'd into LDS three blocks
+//          ahead, row pointers one block ahead in a per-wave LDS table, 18 row DMAs per wave into
+//          the other LDS slot) they take O^T += V^T P^T of block i - 1, whose MFMAs share each SIMD's
+//          matrix pipe with the QK wave's MFMAs of block i; then they copy block i's V^T
+//          (ds_read_b64_tr_b8) into registers while its slot is valid, so two slots suffice.
+// Two barriers per block: B1 "block i landed; P and the rescale factors of block i - 1 published",
+// B2 "both key halves' maxima of block i published; the PV waves hold P of block i - 1" (the QK
+// waves then run the softmax of block i and write its P, the PV waves copy V^T of block i).
 //
 // LDS slot layout (73728 B = 8 subtiles x 9216 B). Within a 16-key subtile, the 16-byte unit of
 // key k and latent chunk c (c < 32) sits at unit 32 k + (c ^ k), and rope chunk c (32..35) at
@@ -607,7 +606,7 @@ __device__ inline float group_max(float v)
 // (k-groups 0, 1 carry hi, 2, 3 lo); the row maxima go to the P area (free until the first P) for
 // the row scales. Two workgroup barriers.
 template <int T>
-__device__ void convert_q(uint8_t* smem, int tid)
+__device__ __forceinline__ void convert_q(uint8_t* smem, int tid)
 {
     using L = Smem<T>;
     constexpr int LPR = 32 / T;                  // lanes per row
@@ -765,7 +764,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     // iteration i: QK and softmax of block i (the PV waves work on block i - 1)
     for (int i = 0; i <= w.nblk; i++) {
         const int slot = i & 1;
-        lds_sync();   // B1: block i landed; P of block i - 1 published
+        lds_sync();   // B1: block i landed; P and the rescale factors of block i - 1 published
         const bool work = active && i < w.nblk;
         v4f acc[TW][KS];
         float bmax[TW];
@@ -856,7 +855,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                     xmax[kh * (T * 16) + (qt0 + j) * 16 + (opaque(lane) & 15)] = bmax[j];
             }
         }
-        lds_sync();   // B2: the PV waves start on block i - 1; the halves' maxima are published
+        lds_sync();   // B2: the halves' maxima are published; the PV waves hold P of block i - 1
         uint32_t pk[TW][KS];   // E4M3 P of this lane's 4 keys of each subtile
         float alpha[TW];
         if (work) {
@@ -886,7 +885,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                 m_run[j] = m_new;
             }
         }
-        lds_sync();   // B3: the PV waves have taken P of block i - 1 into registers
+        // P of block i may overwrite P of block i - 1: the PV waves took that before B2
         if (work) {
             const int lo = opaque(lane);
 #pragma unroll
@@ -1036,7 +1035,10 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     const float* xalpha = reinterpret_cast<const float*>(smem + L::OFF_ALPHA);
     v8i vt[8];   // V^T of the block the next iteration multiplies (copied while its slot is valid)
 
-    // iteration i: gather of block i + 1; PV of block i - 1; V^T of block i into registers
+    // iteration i, before B2: the gather of block i + 1, then the PV of block i - 1 (its P and
+    // rescale factors were published before B1; its V^T is in registers), whose MFMAs share the
+    // SIMD's matrix pipe with the QK waves' MFMAs of block i while the row DMAs drain; after B2:
+    // V^T of block i into registers (its slot is refilled only after the next B1)
     for (int i = 0; i <= w.nblk; i++) {
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's DMAs of block i (and indices)
         lds_sync();   // B1: block i landed; P of block i - 1 published
@@ -1052,7 +1054,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         // away from the QK waves' reads of block i)
         if (i + 2 < w.nblk)
             key_ptrs(i + 2, lane_now() < 32 ? idx_lds[(i & 1) * BLK + 32 * pw + lane_now()] : -1);
-        if (i >= 1) {   // rescale O for block i - 1 while the QK waves issue their MFMAs
+        if (i >= 1) {
 #pragma unroll
             for (int t = 0; t < T; t++) {
                 const float a = alpha[t];
@@ -1061,13 +1063,6 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                     for (int c = 0; c < 8; c++) O[t][c] *= a;
                 }
             }
-        }
-        lds_sync();   // B2: the QK waves have issued their MFMAs of block i
-        // the lane's V^T base for block i's slot (recomputed here, not held across the loop)
-        const int b = (i & 1) * SLOT + vbase(lane_now());
-        if (i >= 1) {
-            // chunk by chunk over all tiles, so that each V^T fragment is reloaded with block i as
-            // soon as its MFMAs have issued
             v8i pb[T];
 #pragma unroll
             for (int t = 0; t < T; t++) {
@@ -1076,17 +1071,17 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                 pb[t] = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
             }
 #pragma unroll
-            for (int c = 0; c < 8; c++) {
+            for (int c = 0; c < 8; c++)
 #pragma unroll
                 for (int t = 0; t < T; t++) O[t][c] = mfma(vt[c], pb[t], O[t][c]);
-                if (i < w.nblk)
-                    vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
-            }
-        } else if (i < w.nblk) {
+        }
+        lds_sync();   // B2: the PV waves hold P of block i - 1; the QK waves' maxima are published
+        if (i < w.nblk) {
+            // the lane's V^T base for block i's slot (recomputed here, not held across the loop)
+            const int b = (i & 1) * SLOT + vbase(lane_now());
 #pragma unroll
             for (int c = 0; c < 8; c++) vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
         }
-        lds_sync();   // B3: P of block i - 1 and V^T of block i are in registers
     }
 
     // ---- epilogue ----
