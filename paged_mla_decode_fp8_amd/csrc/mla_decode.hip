@@ -112,9 +112,9 @@ struct Smem {
     static constexpr int OFF_P = 2 * SLOT;                     // E4M3 P [T][16][PPITCH]
     static constexpr int OFF_ALPHA = OFF_P + T * PTILE;        // float [T*16]
     static constexpr int OFF_FM = OFF_ALPHA + T * 16 * 4;      // float [T*16]
-    static constexpr int OFF_FL = OFF_FM + T * 16 * 4;         // float [2][T*16] (key halves)
-    static constexpr int OFF_XMAX = OFF_FL + 2 * T * 16 * 4;   // float [2][T*16] block maxima
-    static constexpr int OFF_KMASK = OFF_XMAX + 2 * T * 16 * 4; // uint32 [4][4] key presence bits
+    static constexpr int OFF_FL = OFF_FM + T * 16 * 4;         // float [4][T*16] (32-key parts)
+    static constexpr int OFF_XMAX = OFF_FL + 4 * T * 16 * 4;   // float [4][T*16] block maxima per QK wave
+    static constexpr int OFF_KMASK = OFF_XMAX + 4 * T * 16 * 4; // uint32 [4][4] key presence bits
     static constexpr int OFF_IDX = OFF_KMASK + 4 * 16;         // int32 [2][BLK] raw key indices
     static constexpr int OFF_PTAB = OFF_IDX + 2 * BLK * 4;     // uint64 [4 waves][32] key pointers
     static constexpr int OFF_MISC = OFF_PTAB + 4 * 32 * 8;     // int [4]
@@ -686,23 +686,27 @@ __device__ __forceinline__ void convert_q(uint8_t* smem, int tid)
 }
 
 // ---- QK waves: Q stage, S^T = K (hi + lo)^T, softmax; P and the rescale factors to LDS ----
-// QK wave qw owns key half kh = qw % 2 (subtiles 4 kh .. 4 kh + 3 of every block) of the tile pair
-// qw / 2: each K fragment read from LDS feeds the MFMAs of both tiles. The two halves of a tile's
-// keys exchange their block maxima through LDS (both then hold the same running maximum) and
-// keep separate row sums, added in a fixed order at the end. The same split is used for every T
-// (T <= 2: waves 0 and 1, one tile pair), so results do not depend on T.
+// The QK waves share a tile pair's keys: T <= 2 (one pair of TW = T tiles): wave qw owns subtiles
+// 2 qw, 2 qw + 1 of every block; T = 4 (two pairs): wave qw owns subtiles 4 (qw % 2) .. + 3 of
+// pair qw / 2. Each K fragment read from LDS feeds the MFMAs of the pair's tiles. The waves of a
+// pair exchange their block maxima through LDS (all then hold the same running maximum) and keep
+// a row sum per 32-key part (subtiles 2 p, 2 p + 1), added in part order at the end, so results
+// do not depend on T.
 template <int T, bool DENSE>
 __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Work& w, int qw,
                                         int lane)
 {
     using L = Smem<T>;
     constexpr int TW = T >= 2 ? 2 : 1;   // tiles per QK wave
-    constexpr int KS = NSUB / 2;          // subtiles per key half
+    constexpr int KW = T >= 4 ? 2 : 4;    // QK waves per tile pair
+    constexpr int KS = NSUB / KW;         // subtiles per QK wave
+    constexpr int PPW = KS / 2;           // 32-key parts per QK wave
     const int n16 = lane & 15;   // MFMA row / column within 16
     const int grp = lane >> 4;   // MFMA k-group 0..3
-    const int kh = qw & 1;
-    const bool active = (qw >> 1) * TW < T;
-    const int qt0 = active ? (qw >> 1) * TW : 0;   // first tile of the pair within the tile set
+    const int kq = qw % KW;      // key range: subtiles sub0 .. sub0 + KS - 1 of every block
+    const int sub0 = KS * kq;
+    const int qt0 = (qw / KW) * TW;   // first tile of the pair within the tile set
+    const bool active = true;
     int lim[TW];   // keys [first, first + lim) of the item are visible to tile j (lim may be < 0)
 #pragma unroll
     for (int j = 0; j < TW; j++) {
@@ -752,14 +756,15 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     const int ka1 = 512 * n16 + 128 * (n16 >> 3) + 16 * ((2 * grp + 1) ^ (n16 & 7));
     const int kr0 = 8192 + 256 * (2 * (grp & 1)) + 16 * n16;
     const float neg_inf = -INFINITY;
-    float m_run[TW], l_run[TW];   // running max (log2 units) and this half's running sum, row n16
+    float m_run[TW], l_run[TW][PPW];   // running max (log2 units), running sum per part, row n16
 #pragma unroll
     for (int j = 0; j < TW; j++) {
         m_run[j] = neg_inf;
-        l_run[j] = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < PPW; pp++) l_run[j][pp] = 0.f;
     }
     float* xalpha = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
-    float* xmax = reinterpret_cast<float*>(smem + L::OFF_XMAX);   // [2][T * 16] block maxima
+    float* xmax = reinterpret_cast<float*>(smem + L::OFF_XMAX);   // [4 waves][T * 16] block maxima
 
     // iteration i: QK and softmax of block i (the PV waves work on block i - 1)
     for (int i = 0; i <= w.nblk; i++) {
@@ -770,14 +775,14 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         float bmax[TW];
         if (work) {
             // presence bits of the block's keys, read before the MFMAs so that the LDS latency
-            // hides behind them; this lane's 16 keys: bit 4u + jj <-> key 16 (4 kh + u) + 4 grp + jj
-            const v2i mw = *reinterpret_cast<const v2i*>(smem + L::OFF_KMASK + (i & 3) * 16 + 8 * kh);
+            // hides behind them; this lane's keys: bit 4u + jj <-> key 16 (sub0 + u) + 4 grp + jj
+            const v4i mw = *reinterpret_cast<const v4i*>(smem + L::OFF_KMASK + (i & 3) * 16);
             const uint8_t* kslot = smem;
             // the lane's bases for this slot and key half (kept out of the loop-invariant set so
             // that they are recomputed here rather than held in registers across the loop)
             int kb0 = ka0, kb1 = ka1, kbr = kr0;
             asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(kbr));
-            const int soff = slot * SLOT + (KS * kh) * SUBB;
+            const int soff = slot * SLOT + sub0 * SUBB;
             kb0 += soff;
             kb1 += soff;
             kbr += soff;
@@ -817,10 +822,12 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                         acc[j][sub] = mfma(kf[(f - 1) % RING], qlo[j][st], acc[j][sub]);
                 }
             }
-            // all 64 keys of the half present (the words are the same in every lane) and the
-            // block wholly before both tiles' bounds: nothing to mask
-            const uint32_t all_in = (uint32_t)__builtin_amdgcn_readfirstlane(mw.x) &
-                                    (uint32_t)__builtin_amdgcn_readfirstlane(mw.y);
+            // all of this wave's keys present (the words are the same in every lane; word k holds
+            // subtiles 2 k, 2 k + 1) and the block wholly before the tiles' bounds: nothing to mask
+            uint32_t all_in = ~0u;
+#pragma unroll
+            for (int k = 0; k < KS / 2; k++)
+                all_in &= (uint32_t)__builtin_amdgcn_readfirstlane(mw[sub0 / 2 + k]);
             // ---- mask, this half's block maxima (in-lane, then across the 4 k-groups), to LDS.
             // The row scale is positive, so max(s * scale) = scale * max(s) exactly. ----
 #pragma unroll
@@ -830,13 +837,13 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                     uint32_t vis = 0;
 #pragma unroll
                     for (int u = 0; u < KS; u++) {
-                        // subtile 4 kh + u: word 2 kh + u / 2 of the block, half u % 2
-                        vis |= (((uint32_t)mw[u >> 1] >> (16 * (u & 1) + 4 * grp)) & 0xFu) << (4 * u);
+                        // subtile sub0 + u: word (sub0 + u) / 2 of the block, half u % 2
+                        vis |= (((uint32_t)mw[(sub0 + u) >> 1] >> (16 * (u & 1) + 4 * grp)) & 0xFu) << (4 * u);
                     }
                     const int lim_rel = lr < 0 ? 0 : (lr > BLK ? BLK : (int)lr);
 #pragma unroll
                     for (int u = 0; u < KS; u++) {
-                        const int keep = lim_rel - (16 * (KS * kh + u) + 4 * grp);   // of the 4 in bound
+                        const int keep = lim_rel - (16 * (sub0 + u) + 4 * grp);   // of the 4 in bound
                         const uint32_t nib = keep >= 4 ? 0xFu : (keep <= 0 ? 0u : ((1u << keep) - 1u));
                         vis &= ~(0xFu << (4 * u)) | (nib << (4 * u));
                     }
@@ -852,24 +859,29 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                     bm = fmaxf(bm, fmaxf(fmaxf(acc[j][u][0], acc[j][u][1]), fmaxf(acc[j][u][2], acc[j][u][3])));
                 bmax[j] = wave_max16(bm);
                 if (grp == 0)
-                    xmax[kh * (T * 16) + (qt0 + j) * 16 + (opaque(lane) & 15)] = bmax[j];
+                    xmax[qw * (T * 16) + (qt0 + j) * 16 + (opaque(lane) & 15)] = bmax[j];
             }
         }
-        lds_sync();   // B2: the halves' maxima are published; the PV waves hold P of block i - 1
+        lds_sync();   // B2: the pair's maxima are published; the PV waves hold P of block i - 1
         uint32_t pk[TW][KS];   // E4M3 P of this lane's 4 keys of each subtile
         float alpha[TW];
         if (work) {
 #pragma unroll
             for (int j = 0; j < TW; j++) {
-                // both halves combine the same two maxima (fmaxf is exact and symmetric)
-                const float other = xmax[(kh ^ 1) * (T * 16) + (qt0 + j) * 16 + (opaque(lane) & 15)];
-                const float bm = fmaxf(bmax[j], other) * row_scale[j];
+                // the pair's waves combine the same maxima (fmaxf is exact and symmetric)
+                float bmx = bmax[j];
+#pragma unroll
+                for (int k = 1; k < KW; k++)
+                    bmx = fmaxf(bmx, xmax[(qw / KW * KW + (kq + k) % KW) * (T * 16) + (qt0 + j) * 16 + (opaque(lane) & 15)]);
+                const float bm = bmx * row_scale[j];
                 const float m_new = fmaxf(m_run[j], bm);
                 alpha[j] = (m_run[j] == neg_inf) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
                 const float m_use = (m_new == neg_inf) ? 0.f : m_new;   // exp2(-inf - m_use) = 0
-                // ---- P = 448 exp2(s * scale - m) -> E4M3 (P <= 448: no clamp); this half's row
+                // ---- P = 448 exp2(s * scale - m) -> E4M3 (P <= 448: no clamp); each part's row
                 // sum of the unrounded P in a fixed order ----
-                float bsum = 0.f;
+                float bsum[PPW];
+#pragma unroll
+                for (int pp = 0; pp < PPW; pp++) bsum[pp] = 0.f;
 #pragma unroll
                 for (int u = 0; u < KS; u++) {
                     float pr[4];
@@ -878,10 +890,10 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                         pr[jj] = ANCHOR * __builtin_amdgcn_exp2f(fmaf(acc[j][u][jj], row_scale[j], -m_use));
                     int wp = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
                     pk[j][u] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], wp, true);
-                    bsum = bsum + (((pr[0] + pr[1]) + pr[2]) + pr[3]);
+                    bsum[u >> 1] = bsum[u >> 1] + (((pr[0] + pr[1]) + pr[2]) + pr[3]);
                 }
-                bsum = wave_sum16(bsum);
-                l_run[j] = l_run[j] * alpha[j] + bsum;
+#pragma unroll
+                for (int pp = 0; pp < PPW; pp++) l_run[j][pp] = l_run[j][pp] * alpha[j] + wave_sum16(bsum[pp]);
                 m_run[j] = m_new;
             }
         }
@@ -893,31 +905,33 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
 #pragma unroll
                 for (int u = 0; u < KS; u++)
                     *reinterpret_cast<uint32_t*>(smem + L::OFF_P + (qt0 + j) * PTILE + (lo & 15) * PPITCH +
-                                                 16 * (KS * kh + u) + 4 * (lo >> 4)) = pk[j][u];
-                if (grp == 0 && kh == 0)
+                                                 16 * (sub0 + u) + 4 * (lo >> 4)) = pk[j][u];
+                if (grp == 0 && kq == 0)
                     xalpha[(qt0 + j) * 16 + (lo & 15)] = alpha[j];
             }
         }
     }
 
-    // ---- epilogue: m and the halves' sums to LDS; the row sum is half 0 + half 1 ----
+    // ---- epilogue: m and the parts' sums to LDS; the row sum is ((p0 + p1) + p2) + p3 ----
     float* fm = reinterpret_cast<float*>(smem + L::OFF_FM);
-    float* fl = reinterpret_cast<float*>(smem + L::OFF_FL);   // [2][T * 16]
-    if (active && grp == 0) {
+    float* fl = reinterpret_cast<float*>(smem + L::OFF_FL);   // [4 parts][T * 16]
+    if (grp == 0) {
 #pragma unroll
         for (int j = 0; j < TW; j++) {
-            if (kh == 0)
+            if (kq == 0)
                 fm[(qt0 + j) * 16 + n16] = m_run[j];
-            fl[kh * (T * 16) + (qt0 + j) * 16 + n16] = l_run[j];
+#pragma unroll
+            for (int pp = 0; pp < PPW; pp++)
+                fl[(sub0 / 2 + pp) * (T * 16) + (qt0 + j) * 16 + n16] = l_run[j][pp];
         }
     }
     __syncthreads();   // E1
-    if (!(active && grp == 0 && kh == 0))
+    if (!(grp == 0 && kq == 0))
         return;
 #pragma unroll
     for (int j = 0; j < TW; j++) {
         const int r = (qt0 + j) * 16 + n16;
-        const float l = fl[r] + fl[T * 16 + r];
+        const float l = ((fl[r] + fl[T * 16 + r]) + fl[2 * T * 16 + r]) + fl[3 * T * 16 + r];
         const int64_t orow = w.row_base + 16 * (w.ts * T + qt0 + j) + n16;
         if (w.count == 1) {
             p.lse[orow] = (l > 0.f) ? (m_run[j] - LOG2_ANCHOR + log2f(l)) * LN2 : neg_inf;
@@ -1091,7 +1105,8 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         // o = BF16(O / l * k_scale); the single-split merge (weight exp2(0) = 1) is this exactly
 #pragma unroll
         for (int t = 0; t < T; t++) {
-            const float lt = fl[t * 16 + n16] + fl[T * 16 + t * 16 + n16];
+            const int r = t * 16 + n16;
+            const float lt = ((fl[r] + fl[T * 16 + r]) + fl[2 * T * 16 + r]) + fl[3 * T * 16 + r];
             const float rl = 1.f / lt;   // one division per row
             const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
 #pragma unroll
