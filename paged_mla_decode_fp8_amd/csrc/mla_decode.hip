@@ -685,6 +685,36 @@ __device__ __forceinline__ void convert_q(uint8_t* smem, int tid)
     __syncthreads();   // the operands and the row maxima are in LDS
 }
 
+// The nine row DMA sources of subtile 2 pw + h of a block, from PV wave pw's pointer table (entry
+// 16 (k % 2) + 8 (k / 16) + (k % 16) / 2 holds key k of the wave's 32). Latent instruction i moves
+// keys 16 h + 2 i (lanes 0..31) and 16 h + 2 i + 1 (lanes 32..63), chunk (lane % 32) ^ key; the
+// rope instruction: key 16 h + lane % 16, chunk 32 + lane / 16.
+__device__ inline void subtile_sources(const uint64_t* tab, int h, const uint8_t* (&src)[9])
+{
+    const int ln = lane_now();
+    const int hb = ln >> 5;
+    const uint32_t boff = 16u * (uint32_t)((ln & 31) ^ hb);   // 16 ((lane % 32) ^ key) ^ 32 i
+    const uint64_t* row8 = tab + 16 * hb + 8 * h;             // the 8 keys of this lane's half
+    uint64_t kp[8];
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const v4i two = *reinterpret_cast<const v4i*>(row8 + 2 * m);
+        kp[2 * m] = ((uint64_t)(uint32_t)two.y << 32) | (uint32_t)two.x;
+        kp[2 * m + 1] = ((uint64_t)(uint32_t)two.w << 32) | (uint32_t)two.z;
+    }
+    const int rk = ln & 15;   // rope key 16 h + rk
+    const uint64_t rp = tab[16 * (rk & 1) + 8 * h + (rk >> 1)];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        src[i] = reinterpret_cast<const uint8_t*>(kp[i] + (boff ^ (32u * i)));
+    src[8] = reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (ln >> 4));
+}
+
+__device__ inline void issue_subtile(uint8_t* smem, const uint8_t* const (&src)[9], int blk, int pw, int h)
+{
+    dma9(src, lds_addr(smem + (blk & 1) * SLOT + (2 * pw + h) * SUBB));
+}
+
 // ---- QK waves: Q stage, S^T = K (hi + lo)^T, softmax; P and the rescale factors to LDS ----
 // The QK waves share a tile pair's keys: T <= 2 (one pair of TW = T tiles): wave qw owns subtiles
 // 2 qw, 2 qw + 1 of every block; T = 4 (two pairs): wave qw owns subtiles 4 (qw % 2) .. + 3 of
@@ -752,9 +782,6 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     // + h) ^ n16)) = ka_h ^ (128 st), with ka_h = 512 n16 + 128 (n16 >> 3) + 16 ((2 grp + h) ^
     // (n16 & 7)) (the bits of 128 st meet only the 128 (n16 >> 3) term). Rope: 8192 + 256 (2 (grp
     // & 1) + h) + 16 n16.
-    const int ka0 = 512 * n16 + 128 * (n16 >> 3) + 16 * ((2 * grp) ^ (n16 & 7));
-    const int ka1 = 512 * n16 + 128 * (n16 >> 3) + 16 * ((2 * grp + 1) ^ (n16 & 7));
-    const int kr0 = 8192 + 256 * (2 * (grp & 1)) + 16 * n16;
     const float neg_inf = -INFINITY;
     float m_run[TW], l_run[TW][PPW];   // running max (log2 units), running sum per part, row n16
 #pragma unroll
@@ -778,10 +805,12 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
             // hides behind them; this lane's keys: bit 4u + jj <-> key 16 (sub0 + u) + 4 grp + jj
             const v4i mw = *reinterpret_cast<const v4i*>(smem + L::OFF_KMASK + (i & 3) * 16);
             const uint8_t* kslot = smem;
-            // the lane's bases for this slot and key half (kept out of the loop-invariant set so
-            // that they are recomputed here rather than held in registers across the loop)
-            int kb0 = ka0, kb1 = ka1, kbr = kr0;
-            asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(kbr));
+            // the lane's bases for this slot and key half, recomputed from the lane id here rather
+            // than held in registers across the loop
+            const int ln = lane_now(), r16 = ln & 15, g4 = ln >> 4;
+            int kb0 = 512 * r16 + 128 * (r16 >> 3) + 16 * ((2 * g4) ^ (r16 & 7));
+            int kb1 = 512 * r16 + 128 * (r16 >> 3) + 16 * ((2 * g4 + 1) ^ (r16 & 7));
+            int kbr = 8192 + 256 * (2 * (g4 & 1)) + 16 * r16;
             const int soff = slot * SLOT + sub0 * SUBB;
             kb0 += soff;
             kb1 += soff;
@@ -954,18 +983,32 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
 
     // Gather: this wave moves keys 32 pw .. 32 pw + 31 (subtiles 2 pw, 2 pw + 1) of every block.
     // The raw indices (page ids or row ids) of block b arrive in LDS slot b % 2 by DMA three blocks
-    // ahead; one block ahead, lanes 0..31 turn them into row pointers (the zero row when absent),
-    // which go to the wave's pointer table, and a presence word; the wave then issues the block's
-    // 18 row DMAs with each lane's source read from the table.
+    // ahead; two blocks ahead they become row pointers (the zero row when absent), which go to the
+    // wave's pointer table, and a presence word; one block ahead the wave issues the block's 18 row
+    // DMAs with each lane's source read from the table.
     int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
-    uint64_t* ptab = reinterpret_cast<uint64_t*>(smem + L::OFF_PTAB) + 32 * pw;
+    uint64_t* ptab = reinterpret_cast<uint64_t*>(smem + L::OFF_PTAB) + 32 * pw;   // the wave's pointer table
+    // The gather's scalars (the same arithmetic as index_ptr and key_row), made opaque so that the
+    // loop keeps them in scalar registers instead of reloading them from the kernel arguments
+    uint64_t kv_base = (uint64_t)(uintptr_t)p.kv, zero_row = (uint64_t)(uintptr_t)g_zero_row;
+    uint64_t ibase = (uint64_t)(uintptr_t)(DENSE ? p.table + (int64_t)w.g * p.max_pages : p.rows + (int64_t)w.g * p.K);
+    int64_t nrows = p.num_rows;
+    uint32_t psz = (uint32_t)p.page_size, pmag = p.pg_magic;
+    int ps1 = p.pg_s1, ps2 = p.pg_s2;
+    asm volatile("" : "+s"(kv_base), "+s"(zero_row), "+s"(ibase), "+s"(nrows), "+s"(psz), "+s"(pmag), "+s"(ps1), "+s"(ps2));
+    auto pdiv = [&](uint32_t n) {
+        const uint32_t t = __umulhi(n, pmag);
+        return (t + ((n - t) >> ps1)) >> ps2;
+    };
     auto dma_indices = [&](int blk) {  // raw indices of block blk -> idx slot blk % 2
         const int ln = lane_now();
         const int kk = 32 * pw + ln;
         const int64_t left = w.mine - (int64_t)blk * BLK;
-        if (ln < 32 && kk < left)
-            dma4(index_ptr<DENSE>(p, w.g, w.first + (int64_t)blk * BLK + kk),
-                 lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * pw * 4));
+        if (ln < 32 && kk < left) {
+            const int64_t j = w.first + (int64_t)blk * BLK + kk;
+            const int32_t* ip = reinterpret_cast<const int32_t*>(ibase) + (DENSE ? (int64_t)pdiv((uint32_t)j) : j);
+            dma4(ip, lds_addr(smem + L::OFF_IDX + (blk & 1) * BLK * 4 + 32 * pw * 4));
+        }
     };
     // Lane k < 32: the pointer of key 32 pw + k of block blk (idx: its raw index) into table entry
     // 16 (k % 2) + 8 (k / 16) + (k % 16) / 2, i.e. the keys of latent DMA i of subtile h (keys
@@ -976,39 +1019,44 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         const int kk = 32 * pw + ln;
         const int64_t left = w.mine - (int64_t)blk * BLK;
         const bool in = ln < 32 && kk < left;
-        const int64_t row = key_row<DENSE>(p, w.first + (int64_t)blk * BLK + kk, in, idx);
+        const int64_t j = w.first + (int64_t)blk * BLK + kk;
+        int64_t row = -1;
+        if (in) {
+            if (DENSE) {
+                if (idx >= 0)
+                    row = (int64_t)idx * psz + (int64_t)((uint32_t)j - pdiv((uint32_t)j) * psz);
+            } else {
+                row = idx;
+            }
+        }
+        row = (row >= 0 && row < nrows) ? row : -1;
         const uint32_t word = (uint32_t)__ballot(row >= 0);   // lanes 0..31: keys 32 pw + lane
         if (ln == 0)
             *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 3) * 16 + 4 * pw) = word;
-        const uint64_t ptr = row >= 0 ? (uint64_t)(uintptr_t)(p.kv + row * ROW) : (uint64_t)(uintptr_t)g_zero_row;
+        const uint64_t ptr = row >= 0 ? kv_base + (uint64_t)row * ROW : zero_row;
         if (ln < 32)
             ptab[16 * (ln & 1) + 8 * (ln >> 4) + ((ln & 15) >> 1)] = ptr;
     };
-    // The wave's 18 row DMAs of the block whose pointers are in the table. Latent instruction i of
-    // subtile h moves keys 16 h + 2 i (lanes 0..31) and 16 h + 2 i + 1 (lanes 32..63), chunk
-    // (lane % 32) ^ key; rope instruction: key 16 h + lane % 16, chunk 32 + lane / 16.
-    auto issue_block = [&](int blk) {
+    // The same without branches, for the loop: lane l handles key 32 pw + l % 32 (idx: the raw
+    // index of that key in both halves), so lanes l and l + 32 store the same pointer to the same
+    // entry and every lane stores the presence word; for a block past the item every key is absent.
+    auto key_ptrs_all = [&](int blk, int32_t idx) {
         const int ln = lane_now();
-        const int hb = ln >> 5;
-        const uint32_t boff = 16u * (uint32_t)((ln & 31) ^ hb);   // 16 ((lane % 32) ^ key) ^ 32 i
+        const int kk = 32 * pw + (ln & 31);
+        const int64_t left = w.mine - (int64_t)blk * BLK;
+        const int64_t j = w.first + (int64_t)blk * BLK + kk;
+        const int64_t rd = DENSE ? (int64_t)idx * psz + (int64_t)((uint32_t)j - pdiv((uint32_t)j) * psz) : (int64_t)idx;
+        const bool ok = kk < left && idx >= 0 && rd < nrows;
+        const uint32_t word = (uint32_t)__ballot(ok);
+        *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 3) * 16 + 4 * pw) = word;
+        ptab[16 * (ln & 1) + 8 * ((ln >> 4) & 1) + ((ln & 15) >> 1)] = ok ? kv_base + (uint64_t)rd * ROW : zero_row;
+    };
+    auto issue_block = [&](int blk) {   // the block's 18 row DMAs, pointers from the table
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            const uint64_t* row8 = ptab + 16 * hb + 8 * h;   // the 8 keys of this lane's half
-            uint64_t kp[8];
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                const v4i two = *reinterpret_cast<const v4i*>(row8 + 2 * m);
-                kp[2 * m] = ((uint64_t)(uint32_t)two.y << 32) | (uint32_t)two.x;
-                kp[2 * m + 1] = ((uint64_t)(uint32_t)two.w << 32) | (uint32_t)two.z;
-            }
-            const int rk = ln & 15;   // rope key 16 h + rk
-            const uint64_t rp = ptab[16 * (rk & 1) + 8 * h + (rk >> 1)];
             const uint8_t* src[9];
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                src[i] = reinterpret_cast<const uint8_t*>(kp[i] + (boff ^ (32u * i)));
-            src[8] = reinterpret_cast<const uint8_t*>(rp + 512 + 16 * (ln >> 4));
-            dma9(src, lds_addr(smem + (blk & 1) * SLOT + (2 * pw + h) * SUBB));
+            subtile_sources(ptab, h, src);
+            issue_subtile(smem, src, blk, pw, h);
         }
     };
     if (w.nblk > 0) {
@@ -1049,25 +1097,42 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     const float* xalpha = reinterpret_cast<const float*>(smem + L::OFF_ALPHA);
     v8i vt[8];   // V^T of the block the next iteration multiplies (copied while its slot is valid)
 
-    // iteration i, before B2: the gather of block i + 1, then the PV of block i - 1 (its P and
-    // rescale factors were published before B1; its V^T is in registers), whose MFMAs share the
-    // SIMD's matrix pipe with the QK waves' MFMAs of block i while the row DMAs drain; after B2:
-    // V^T of block i into registers (its slot is refilled only after the next B1)
+    // iteration i, before B2: P and the rescale factors of block i - 1 (published before B1) and
+    // the row DMAs of block i + 1 (its slot's last readers finished before B1); after B2, in one
+    // stretch of code: the PV of block i - 1 (its V^T is in registers), each V^T chunk replaced by
+    // block i's once its MFMAs are issued (the slot is refilled only after the next B1), and the
+    // pointers and presence word of block i + 2; then the indices of block i + 3. The table is read
+    // before B2 and rewritten after it; presence words and index slots alternate by block, away
+    // from the QK waves' reads. With four tiles every iteration runs the whole stretch (the first
+    // multiplies zeros, the last reads an unused slot: registers are too few for a second copy of
+    // the code); otherwise the first and last iterations take the same steps one by one.
+    if (T == 4) {
+#pragma unroll
+        for (int c = 0; c < 8; c++) vt[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
     for (int i = 0; i <= w.nblk; i++) {
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's DMAs of block i (and indices)
         lds_sync();   // B1: block i landed; P of block i - 1 published
-        float alpha[T];   // rescale factors of block i - 1, read before the gather (LDS latency)
+        // block i + 2's indices (landed with this iteration's vmcnt wait; any block's slot is
+        // readable)
+        const int32_t idx2 = idx_lds[(i & 1) * BLK + 32 * pw + (lane_now() & 31)];
+        float alpha[T];
+        v8i pb[T];
+        if (T == 4) {
 #pragma unroll
-        for (int t = 0; t < T; t++) alpha[t] = xalpha[t * 16 + (lane_now() & 15)];
+            for (int t = 0; t < T; t++) pb[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        if (i >= 1) {
+#pragma unroll
+            for (int t = 0; t < T; t++) {
+                const int lo = lane_now();
+                alpha[t] = xalpha[t * 16 + (lo & 15)];
+                const int off = L::OFF_P + t * PTILE + (lo & 15) * PPITCH + 32 * (lo >> 4);
+                pb[t] = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
+            }
+        }
         if (i + 1 < w.nblk)
             issue_block(i + 1);
-        if (i + 3 < w.nblk)
-            dma_indices(i + 3);
-        // pointers of block i + 2 (its indices landed with this iteration's vmcnt wait; the table's
-        // reads for block i + 1 precede these writes; presence words of block b sit in slot b % 4,
-        // away from the QK waves' reads of block i)
-        if (i + 2 < w.nblk)
-            key_ptrs(i + 2, lane_now() < 32 ? idx_lds[(i & 1) * BLK + 32 * pw + lane_now()] : -1);
         if (i >= 1) {
 #pragma unroll
             for (int t = 0; t < T; t++) {
@@ -1077,25 +1142,34 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                     for (int c = 0; c < 8; c++) O[t][c] *= a;
                 }
             }
-            v8i pb[T];
-#pragma unroll
-            for (int t = 0; t < T; t++) {
-                const int lo = lane_now();
-                const int off = L::OFF_P + t * PTILE + (lo & 15) * PPITCH + 32 * (lo >> 4);
-                pb[t] = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
-            }
-#pragma unroll
-            for (int c = 0; c < 8; c++)
-#pragma unroll
-                for (int t = 0; t < T; t++) O[t][c] = mfma(vt[c], pb[t], O[t][c]);
         }
         lds_sync();   // B2: the PV waves hold P of block i - 1; the QK waves' maxima are published
-        if (i < w.nblk) {
-            // the lane's V^T base for block i's slot (recomputed here, not held across the loop)
-            const int b = (i & 1) * SLOT + vbase(lane_now());
+        // the lane's V^T base for block i's slot (recomputed here, not held across the loop)
+        const int b = (i & 1) * SLOT + vbase(lane_now());
+        if (T == 4 || (i >= 1 && i < w.nblk)) {
+            key_ptrs_all(i + 2, idx2);
 #pragma unroll
-            for (int c = 0; c < 8; c++) vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
+            for (int c = 0; c < 8; c++) {
+#pragma unroll
+                for (int t = 0; t < T; t++) O[t][c] = mfma(vt[c], pb[t], O[t][c]);
+                vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
+            }
+        } else {
+            if (i + 2 < w.nblk)
+                key_ptrs_all(i + 2, idx2);
+            if (i >= 1) {
+#pragma unroll
+                for (int c = 0; c < 8; c++)
+#pragma unroll
+                    for (int t = 0; t < T; t++) O[t][c] = mfma(vt[c], pb[t], O[t][c]);
+            }
+            if (i < w.nblk) {
+#pragma unroll
+                for (int c = 0; c < 8; c++) vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
+            }
         }
+        if (i + 3 < w.nblk)
+            dma_indices(i + 3);
     }
 
     // ---- epilogue ----
