@@ -10,6 +10,8 @@ What it computes, and the passages of the vLLM API pages it follows, is stated i
 * ``ONLINE`` -- the pages' split / chunked base-2 online softmax and FP32-style merge, P unrounded.
 * ``METHOD`` -- as ``ONLINE`` with P rounded to E4M3 at the 448 anchor of the running maximum.
 
+With ``q_e4m3=True`` the logits use the E4M3 query (``q_e4m3_row``) in place of the bf16 one.
+
 With ``allowance=True`` the front ends also return, per output element, how far o may move when a
 P that an FP32 implementation can only place to within 2^-13 (relative) of an E4M3 rounding
 midpoint is rounded the other way (METHOD mode; zeros otherwise).
@@ -23,6 +25,7 @@ import subprocess
 import numpy as np
 
 EXACT, ONLINE, METHOD = 0, 1, 2
+_QE4M3 = 16   # flag added to a mode: the E4M3 query
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mla_oracle.c")
@@ -54,6 +57,10 @@ def _load():
         lib.mo_e4m3_encode.restype = ctypes.c_uint8
         lib.mo_bf16_decode.argtypes = [ctypes.c_uint16]
         lib.mo_bf16_decode.restype = ctypes.c_double
+        lib.mo_q_e4m3_bits.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.mo_q_e4m3_bits.restype = None
+        lib.mo_q_shift.argtypes = [ctypes.c_void_p]
+        lib.mo_q_shift.restype = ctypes.c_int
         lib.mo_dense.argtypes = [P, i32, i32, i32, P, i64, i32, f32, P, i32, P, f32, i32, i32, i32,
                                  P, P, P, i64, i32, P, P, P]
         lib.mo_dense.restype = i32
@@ -74,6 +81,17 @@ def e4m3_encode(x: float) -> int:
 
 def bf16_decode(bits: int) -> float:
     return _load().mo_bf16_decode(bits)
+
+
+def q_e4m3_row(q_bits) -> tuple[np.ndarray, int]:
+    """The E4M3 query of one row: ``q_bits`` uint16 bf16 bits [576] -> (FP64 values [576], the
+    row's power-of-two exponent k), qe = dec(E4M3(q * 2^k)) * 2^-k."""
+    q = _as(q_bits, np.uint16).reshape(576)
+    qe = np.zeros(576, np.float64)
+    _load().mo_q_e4m3_bits(_ptr(q), _ptr(qe))
+    qd = np.ascontiguousarray(q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    k = _load().mo_q_shift(_ptr(qd))
+    return qe, k
 
 
 def _ptr(a: np.ndarray | None):
@@ -121,7 +139,7 @@ def _cuts(cuts, groups):
 
 
 def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=METHOD, splits=1,
-          chunk=128, cuts=None, sel=None, threads=None, allowance=False):
+          chunk=128, cuts=None, sel=None, threads=None, allowance=False, q_e4m3=False):
     """Paged dense decode. ``q_bits`` uint16 bf16 bits [B,Q,H,576]; ``kv`` uint8 [num_rows,576];
     ``block_table`` int32 [B,max_pages]; ``seq_lens`` int32 [B].
 
@@ -143,7 +161,8 @@ def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=
     amb = np.zeros_like(o) if allowance else None
     rc = _load().mo_dense(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], int(page_size),
                           float(k_scale), _ptr(table), table.shape[1], _ptr(seq), float(scale),
-                          int(mode), int(splits), int(chunk), _ptr(cp), _ptr(cs), _ptr(sel),
+                          int(mode) | (_QE4M3 if q_e4m3 else 0), int(splits), int(chunk), _ptr(cp),
+                          _ptr(cs), _ptr(sel),
                           0 if sel is None else len(sel), _threads(threads), _ptr(o), _ptr(lse),
                           _ptr(amb))
     if rc != 0:
@@ -152,7 +171,7 @@ def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=
 
 
 def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, chunk=128, cuts=None,
-           sel=None, threads=None, allowance=False):
+           sel=None, threads=None, allowance=False, q_e4m3=False):
     """Top-k sparse decode. ``rows`` int32 [B,Q,K] flat cache rows; ``valid`` int32 [B,Q]. The
     split plan as for ``dense``, with ``cuts`` given per (b, i) row list, in order b*Q+i."""
     q_bits = _as(q_bits, np.uint16)
@@ -167,7 +186,8 @@ def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, ch
     cp, cs = _cuts(cuts, B * Q)
     amb = np.zeros_like(o) if allowance else None
     rc = _load().mo_sparse(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], float(k_scale),
-                           _ptr(rows), rows.shape[2], _ptr(valid), float(scale), int(mode),
+                           _ptr(rows), rows.shape[2], _ptr(valid), float(scale),
+                           int(mode) | (_QE4M3 if q_e4m3 else 0),
                            int(splits), int(chunk), _ptr(cp), _ptr(cs), _ptr(sel),
                            0 if sel is None else len(sel),
                            _threads(threads), _ptr(o), _ptr(lse), _ptr(amb))

@@ -24,6 +24,9 @@
  *               seq_len - qlen + i; a split with no visible key leaves LSE = -inf and o = 0.
  *             - fp8_unpack4: E4M3 to f32 is exact.
  *
+ * The query: the bf16 row as given (q exact in FP64), or, with the MO_QE4M3 flag added to a mode,
+ * its E4M3 form (see mo_q_e4m3 below).
+ *
  * Three modes of the same computation for one query row (b, i, h):
  *   MO_EXACT      the textbook definition: LSE = ln sum_j exp(x_j), o = sum_j softmax(x)_j V_j, with
  *                 x_j = scale * q . K_j, K_j = k_scale * dec(K bytes), V_j = k_scale * dec(V bytes).
@@ -57,6 +60,7 @@
 #define MO_LATENT 512 /* latent bytes = V width */
 
 enum { MO_EXACT = 0, MO_ONLINE = 1, MO_METHOD = 2 };
+enum { MO_QE4M3 = 16 }; /* flag added to a mode: the logits use the E4M3 query */
 
 /* ---- number formats --------------------------------------------------------------------------- */
 
@@ -116,6 +120,48 @@ double mo_bf16_decode(uint16_t h)
     return (double)f;
 }
 
+/* ---- the E4M3 query ---------------------------------------------------------------------------- */
+
+/*
+ * [SPARSE] module docstring, Precision paragraph: FlashInfer's sparse MLA decode takes an E4M3
+ * query. How the bf16 query becomes E4M3 is not stated; the reading taken here uses the per-row
+ * power of two of [AMD] (its query split scales q by 2^k): k is the largest integer with
+ * max_c |q_c| * 2^k <= 448, at most 126, and 0 for an all-zero row. Each value is rounded to E4M3
+ * (nearest, ties to even) at that scale and scaled back: qe_c = dec(E4M3(q_c * 2^k)) * 2^-k.
+ * Scaling by powers of two is exact in FP64 here, so the only rounding is the E4M3 one.
+ */
+int mo_q_shift(const double* qd)
+{
+    double amax = 0.0;
+    for (int c = 0; c < MO_ROW; c++)
+        if (fabs(qd[c]) > amax)
+            amax = fabs(qd[c]);
+    if (amax == 0.0)
+        return 0;
+    int k = 0;
+    while (k < 126 && ldexp(amax, k + 1) <= 448.0)
+        k++;
+    while (ldexp(amax, k) > 448.0)
+        k--;
+    return k;
+}
+
+void mo_q_e4m3(const double* qd, double* qe)
+{
+    const int k = mo_q_shift(qd);
+    for (int c = 0; c < MO_ROW; c++)
+        qe[c] = ldexp(mo_e4m3_decode(mo_e4m3_encode(ldexp(qd[c], k))), -k);
+}
+
+/* bf16 bits of one row -> its E4M3 query (for the tests) */
+void mo_q_e4m3_bits(const uint16_t* q, double* qe)
+{
+    double qd[MO_ROW];
+    for (int c = 0; c < MO_ROW; c++)
+        qd[c] = mo_bf16_decode(q[c]);
+    mo_q_e4m3(qd, qe);
+}
+
 /* ---- one query row ---------------------------------------------------------------------------- */
 
 /* Relative accuracy of P assumed for an FP32 implementation (2^-13: FP32 dot products of 576 terms
@@ -135,6 +181,7 @@ static double rounding_ambiguity(double p)
 
 typedef struct {
     int mode;
+    int qe4m3;  /* the E4M3 query (MO_QE4M3) */
     int splits; /* S >= 1 */
     int chunk;  /* keys per chunk >= 1 */
 } mo_plan;
@@ -167,6 +214,11 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
     double qd[MO_ROW];
     for (int c = 0; c < MO_ROW; c++)
         qd[c] = mo_bf16_decode(q[c]);
+    if (plan->qe4m3) {
+        double qe[MO_ROW];
+        mo_q_e4m3(qd, qe);
+        memcpy(qd, qe, sizeof qd);
+    }
     for (int c = 0; c < MO_LATENT; c++)
         o[c] = 0.0;
 
@@ -445,6 +497,7 @@ static int run_job(mo_job* base)
  * seq_lens [B]. sel: optional list of flat rows (b*Q+i)*H+h (n_sel of them); NULL means every row.
  * cut_ptr / cut_start: optional explicit split starts per key group (dense: group b; sparse: group
  * b*Q+i), which replace the uniform split rule when given.
+ * mode: MO_EXACT, MO_ONLINE or MO_METHOD, plus MO_QE4M3 for the E4M3 query.
  * o [items,512] and lse [items] in FP64; amb (optional, METHOD mode) [items,512] the rounding
  * allowance described at the top.
  */
@@ -470,7 +523,8 @@ int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t 
     jb.seq_lens = seq_lens;
     jb.scale = scale;
     jb.k_scale = k_scale;
-    jb.plan.mode = mode;
+    jb.plan.mode = mode & ~MO_QE4M3;
+    jb.plan.qe4m3 = (mode & MO_QE4M3) != 0;
     jb.plan.splits = splits;
     jb.plan.chunk = chunk;
     jb.cut_ptr = cut_ptr;
@@ -505,7 +559,8 @@ int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t
     jb.valid = valid;
     jb.scale = scale;
     jb.k_scale = k_scale;
-    jb.plan.mode = mode;
+    jb.plan.mode = mode & ~MO_QE4M3;
+    jb.plan.qe4m3 = (mode & MO_QE4M3) != 0;
     jb.plan.splits = splits;
     jb.plan.chunk = chunk;
     jb.cut_ptr = cut_ptr;
