@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12        # B/s, MI355X
 FP8_PEAK = 5.0e15        # dense FP8 MFMA flop/s, MI355X
 FLOP_PER_HEAD_KEY = 2 * 2 * 576 + 2 * 512   # QK with the hi + lo query (two E4M3 passes) + PV
+FLOP_PER_HEAD_KEY_E4M3Q = 2 * 576 + 2 * 512  # QK with the E4M3 query (one pass) + PV
 HEADLINE = "dense_paged"
 METRIC = ("µs/call and KV HBM GB/s (fraction of 8 TB/s peak), dense + top-k sparse MLA "
           "decode")
@@ -48,9 +49,10 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def algorithmic(x):
+def algorithmic(x, q_precision="split"):
     """Algorithmic HBM bytes and MFMA flops of one call: every gathered KV row once per key group,
-    Q read once, o and lse written once, indices / block-table entries read once."""
+    Q read once, o and lse written once, indices / block-table entries read once. The flops count
+    the QK product once per query pass (two for the split query, one for the E4M3 query)."""
     rows = x.B * x.Q * x.H
     q_bytes = rows * 576 * 2
     o_bytes = rows * 512 * 2 + rows * 4
@@ -71,20 +73,21 @@ def algorithmic(x):
     return {
         "kv_bytes": kv_bytes,
         "bytes": kv_bytes + q_bytes + o_bytes + idx_bytes,
-        "flops": head_keys * FLOP_PER_HEAD_KEY,
+        "flops": head_keys * (FLOP_PER_HEAD_KEY_E4M3Q if q_precision == "e4m3" else FLOP_PER_HEAD_KEY),
         "head_keys": head_keys,
     }
 
 
-def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20):
+def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precision="split", x=None):
     import torch
 
     import paged_mla_decode_fp8_amd as mla
     import workloads as wl
 
     w = wl.WORKLOADS[name]
-    x = w.make()
-    alg = algorithmic(x)
+    if x is None:
+        x = w.make()
+    alg = algorithmic(x, q_precision)
     dev = torch.device("cuda:0")
     plan = w.plan
     kv_host = torch.from_numpy(x.kv)
@@ -101,14 +104,14 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20):
 
         def call(k):
             mla.dense(q, kvs[k % copies], table, seq, x.scale, x.k_scale, x.page_size, plan=plan,
-                      o=o, lse=lse, workspace=ws)
+                      o=o, lse=lse, workspace=ws, q_precision=q_precision)
     else:
         rows = torch.from_numpy(x.rows).to(dev)
         valid = torch.from_numpy(x.valid).to(dev)
 
         def call(k):
             mla.sparse(q, kvs[k % copies], rows, valid, x.scale, x.k_scale, plan=plan, o=o,
-                       lse=lse, workspace=ws)
+                       lse=lse, workspace=ws, q_precision=q_precision)
 
     for k in range(warmup):
         call(k)
@@ -231,6 +234,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of the headline workload the CPU oracle is timed on")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the E4M3-query precision runs of every workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (a known-size reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -258,6 +263,7 @@ def main():
     names = [HEADLINE] + names
 
     results = {}
+    variants = {}
     head_x = None
     for name in names:
         res, x = bench_workload(name, args.steps, args.warmup)
@@ -265,6 +271,13 @@ def main():
         print(f"[bench] {name}: {res['us_per_call']} us/call, {res['kv_GBps']} KV GB/s, "
               f"hbm {res['hbm_frac']:.3f}, mfma {res['mfma_frac']:.3f}", file=sys.stderr,
               flush=True)
+        if not args.no_variants:
+            v, _ = bench_workload(name, args.steps, args.warmup, q_precision="e4m3", x=x)
+            variants[name] = {k: v[k] for k in ("us_per_call", "kv_GBps", "hbm_frac", "mfma_frac",
+                                                "alg_flops", "mfma_floor_us")}
+            print(f"[bench] {name} (E4M3 query): {v['us_per_call']} us/call, {v['kv_GBps']} KV "
+                  f"GB/s, hbm {v['hbm_frac']:.3f}, mfma {v['mfma_frac']:.3f}", file=sys.stderr,
+                  flush=True)
         if name == HEADLINE:
             head_x = x
         else:
@@ -310,6 +323,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "workloads": results,
+        "q_e4m3": variants or None,
     }
     print(json.dumps(line))
 

@@ -137,6 +137,35 @@ mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t*
                                const mla_plan_t* plan, void* o, float* lse, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Query precision of the QK product (the argument q_precision of the _q entry points).
+ *   MLA_Q_SPLIT  the AMD page's exact query split (mono.attention.mla_attn, module docstring): per
+ *                query row the power of two 2^k, k the largest integer with max |q| 2^k <= 448 (at
+ *                most 126; 0 for an all-zero row), and q 2^k = hi + lo with hi = E4M3(q 2^k),
+ *                lo = E4M3(q 2^k - hi); the logits see the bf16 query exactly wherever q 2^k - hi
+ *                is an E4M3 value (always for |q 2^k| >= 2^-2). Two FP8 MFMAs per latent step.
+ *   MLA_Q_E4M3   the E4M3 query of the sparse page's Precision paragraph (FlashInfer's precision):
+ *                the logits use E4M3(q 2^k) 2^-k (round to nearest even, same k) in place of q.
+ *                Half the QK MFMAs of MLA_Q_SPLIT; |q - query used| <= 2^-4 |q| per value where
+ *                |q 2^k| >= 2^-6.
+ */
+enum { MLA_Q_SPLIT = 0, MLA_Q_E4M3 = 1 };
+
+/*
+ * mla_decode_dense and mla_decode_sparse with the query precision as an argument (they are these
+ * with MLA_Q_SPLIT). A q_precision other than MLA_Q_SPLIT or MLA_Q_E4M3 returns
+ * MLA_ERR_UNSUPPORTED before anything else is checked. Other arguments, layouts and errors as for
+ * the plain entry points.
+ */
+mla_status_t mla_decode_dense_q(const void* q, const mla_kv_t* kv, const int32_t* block_table,
+                                int max_pages, const int32_t* seq_lens, float scale, int B, int Q,
+                                int H, const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_t* rows, int K,
+                                 const int32_t* valid, float scale, int B, int Q, int H,
+                                 const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name of a status. */
 const char* mla_status_string(mla_status_t status);
 

@@ -74,6 +74,12 @@ def _load():
         lib.mla_decode_sparse.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32, i32,
                                           ctypes.POINTER(_Plan), P, P, P, sz, P]
         lib.mla_decode_sparse.restype = i32
+        lib.mla_decode_dense_q.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32, i32,
+                                           ctypes.POINTER(_Plan), i32, P, P, P, sz, P]
+        lib.mla_decode_dense_q.restype = i32
+        lib.mla_decode_sparse_q.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32, i32,
+                                            ctypes.POINTER(_Plan), i32, P, P, P, sz, P]
+        lib.mla_decode_sparse_q.restype = i32
         _lib = lib
     return _lib
 
@@ -152,6 +158,16 @@ def _check_tensor(name, t, dtype, device):
         raise ValueError(f"{name}: expected a contiguous {dtype} tensor on {device}")
 
 
+# query precisions of the QK product (C ABI MLA_Q_SPLIT, MLA_Q_E4M3)
+Q_PRECISIONS = {"split": 0, "e4m3": 1}
+
+
+def _q_precision(name: str) -> int:
+    if name not in Q_PRECISIONS:
+        raise ValueError(f"q_precision must be one of {sorted(Q_PRECISIONS)}, not {name!r}")
+    return Q_PRECISIONS[name]
+
+
 def _plan_arg(plan):
     if plan is None:
         return None
@@ -160,10 +176,12 @@ def _plan_arg(plan):
 
 def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
           scale: float, k_scale: float, page_size: int, *, plan=None, o=None, lse=None,
-          workspace: torch.Tensor | None = None):
-    """Paged dense decode (C ABI mla_decode_dense). q bf16 [B,Q,H,576]; kv uint8 [rows,576] (or
-    [pages,page_size,576]); block_table int32 [B,max_pages]; seq_lens int32 [B]. Returns
-    (o bf16 [B,Q,H,512], lse f32 [B,Q,H]) on the current stream."""
+          workspace: torch.Tensor | None = None, q_precision: str = "split"):
+    """Paged dense decode (C ABI mla_decode_dense, or mla_decode_dense_q for q_precision "e4m3").
+    q bf16 [B,Q,H,576]; kv uint8 [rows,576] (or [pages,page_size,576]); block_table int32
+    [B,max_pages]; seq_lens int32 [B]. Returns (o bf16 [B,Q,H,512], lse f32 [B,Q,H]) on the
+    current stream."""
+    qp = _q_precision(q_precision)
     dev = q.device
     _check_tensor("q", q, torch.bfloat16, dev)
     _check_tensor("kv", kv, torch.uint8, dev)
@@ -177,18 +195,19 @@ def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens
     if workspace is None:
         workspace = _workspace(dev, stream, True, B, Q, H, pl)
     kvs = _KV(kv.data_ptr(), kv.numel() // 576, int(page_size), float(k_scale))
-    _check(_load().mla_decode_dense(
+    _check(_load().mla_decode_dense_q(
         _ptr(q), ctypes.byref(kvs), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
-        float(scale), B, Q, H, _plan_arg(pl), _ptr(o), _ptr(lse), _ptr(workspace),
+        float(scale), B, Q, H, _plan_arg(pl), qp, _ptr(o), _ptr(lse), _ptr(workspace),
         0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream)))
     return o, lse
 
 
 def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.Tensor,
            scale: float, k_scale: float, *, plan=None, o=None, lse=None,
-           workspace: torch.Tensor | None = None):
-    """Top-k sparse decode (C ABI mla_decode_sparse). rows int32 [B,Q,K] flat cache rows; valid
-    int32 [B,Q]."""
+           workspace: torch.Tensor | None = None, q_precision: str = "split"):
+    """Top-k sparse decode (C ABI mla_decode_sparse, or mla_decode_sparse_q for q_precision
+    "e4m3"). rows int32 [B,Q,K] flat cache rows; valid int32 [B,Q]."""
+    qp = _q_precision(q_precision)
     dev = q.device
     _check_tensor("q", q, torch.bfloat16, dev)
     _check_tensor("kv", kv, torch.uint8, dev)
@@ -203,8 +222,8 @@ def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.T
     if workspace is None:
         workspace = _workspace(dev, stream, False, B, Q, H, pl)
     kvs = _KV(kv.data_ptr(), kv.numel() // 576, 1, float(k_scale))
-    _check(_load().mla_decode_sparse(
+    _check(_load().mla_decode_sparse_q(
         _ptr(q), ctypes.byref(kvs), _ptr(rows), K, _ptr(valid), float(scale), B, Q, H,
-        _plan_arg(pl), _ptr(o), _ptr(lse), _ptr(workspace),
+        _plan_arg(pl), qp, _ptr(o), _ptr(lse), _ptr(workspace),
         0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream)))
     return o, lse

@@ -604,8 +604,8 @@ __device__ inline float group_max(float v)
 // maximum is a reduction inside the lane group. The operands replace the rows in slot 1:
 // [tile][operand][lane][32 B], operands 0..3 the hi steps, 4..7 the lo steps, 8 the rope step
 // (k-groups 0, 1 carry hi, 2, 3 lo); the row maxima go to the P area (free until the first P) for
-// the row scales. Two workgroup barriers.
-template <int T>
+// the row scales. Two workgroup barriers. QE: the E4M3 query, hi alone (lo = 0).
+template <int T, bool QE>
 __device__ __forceinline__ void convert_q(uint8_t* smem, int tid)
 {
     using L = Smem<T>;
@@ -651,7 +651,7 @@ __device__ __forceinline__ void convert_q(uint8_t* smem, int tid)
             const float d2 = bf16_to_f32(qb & 0xFFFF) - b23.x, d3 = bf16_to_f32(qb >> 16) - b23.y;
             v2s lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, d0, d1, sinv, false);
             lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, d2, d3, sinv, true);
-            lo[h] = __builtin_bit_cast(uint32_t, lw);
+            lo[h] = QE ? 0u : __builtin_bit_cast(uint32_t, lw);
         }
         raw[k] = v4i{(int)hi[0], (int)hi[1], (int)lo[0], (int)lo[1]};
     }
@@ -721,8 +721,8 @@ __device__ inline void issue_subtile(uint8_t* smem, const uint8_t* const (&src)[
 // pair qw / 2. Each K fragment read from LDS feeds the MFMAs of the pair's tiles. The waves of a
 // pair exchange their block maxima through LDS (all then hold the same running maximum) and keep
 // a row sum per 32-key part (subtiles 2 p, 2 p + 1), added in part order at the end, so results
-// do not depend on T.
-template <int T, bool DENSE>
+// do not depend on T. QE: the E4M3 query (the hi operands alone; no lo MFMAs).
+template <int T, bool DENSE, bool QE>
 __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Work& w, int qw,
                                         int lane)
 {
@@ -752,7 +752,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's staged Q rows landed
     lds_sync();                          // Q0: every staged row landed
     if (w.nblk > 0)
-        convert_q<T>(smem, qw * 64 + lane);
+        convert_q<T, QE>(smem, qw * 64 + lane);
 
     // ---- the tiles' B operands (exact E4M3 hi + lo of q * 2^k) and row scales from LDS ----
     v8i qhi[TW][4], qlo[TW][4], qrope[TW];
@@ -769,7 +769,8 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
 #pragma unroll
             for (int st = 0; st < 4; st++) {
                 qhi[j][st] = op(st);
-                qlo[j][st] = op(4 + st);
+                if (!QE)
+                    qlo[j][st] = op(4 + st);
             }
             qrope[j] = op(8);
             const float am = __uint_as_float(reinterpret_cast<const uint32_t*>(smem + L::OFF_P)[16 * t + n16]);
@@ -844,7 +845,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                     for (int j = 0; j < TW; j++)
                         acc[j][sub] = mfma(kf[f % RING], st < 4 ? qhi[j][st] : qrope[j], acc[j][sub]);
                 }
-                if (f >= 1 && f - 1 < 4 * KS) {
+                if (!QE && f >= 1 && f - 1 < 4 * KS) {
                     const int st = (f - 1) / KS, sub = (f - 1) % KS;
 #pragma unroll
                     for (int j = 0; j < TW; j++)
@@ -973,7 +974,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
 }
 
 // ---- PV waves: the gather, and O^T += V^T P^T for 128 latent columns of every tile ----
-template <int T, bool DENSE>
+template <int T, bool DENSE, bool QE>
 __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Work& w, int pw,
                                         int lane, const FirstIdx& fi, v4f (&O)[T][8])
 {
@@ -1077,7 +1078,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     }
     lds_sync();   // Q0: the QK waves' staged query rows landed
     if (w.nblk > 0)
-        convert_q<T>(smem, 256 + pw * 64 + lane);
+        convert_q<T, QE>(smem, 256 + pw * 64 + lane);
 
     // This lane's transposed V read of column chunk 8 pw + c, key half rb of subtile 2 grp + sp:
     // LDS unit 32 kk + (cc ^ kk) of the subtile, kk = 8 rb + m, cc = 8 pw + c, m = n16 / 2, plus
@@ -1344,7 +1345,7 @@ __device__ inline const Params& fresh_params()
     return *(const Params*)k;   // loads through it stay scalar (address-space inference)
 }
 
-template <int T, bool DENSE>
+template <int T, bool DENSE, bool QE>
 __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
 {
     using L = Smem<T>;
@@ -1383,7 +1384,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             Work w;
             item(pi, g, pre, w);
             pre += ITEM_BLOCKS + nblocks(w.n_grp);
-            qk_role<T, DENSE>(pi, smem, w, wave, li);
+            qk_role<T, DENSE, QE>(pi, smem, w, wave, li);
             finish_item<T>(pi, smem, w, tid);
             __syncthreads();   // the next item reuses every LDS area
         }
@@ -1402,7 +1403,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
                 for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
             int li = lane;
             asm volatile("" : "+v"(li));
-            pv_role<T, DENSE>(pi, smem, w, wave - 4, li, fi, O);
+            pv_role<T, DENSE, QE>(pi, smem, w, wave - 4, li, fi, O);
             finish_item<T>(pi, smem, w, tid);
             __syncthreads();
         }
@@ -1504,24 +1505,31 @@ void set_page_division(Params& p, int d)
     p.pg_s2 = l - 1 > 0 ? l - 1 : 0;
 }
 
-template <int T, bool DENSE>
+template <int T, bool DENSE, bool QE>
 hipError_t launch_t(const Params& p, hipStream_t stream)
 {
     const int64_t gs_pad = ((int64_t)p.units + 7) / 8 * 8;
     const int64_t grid = gs_pad * p.tilesets;
-    hipLaunchKernelGGL((mla_decode_kernel<T, DENSE>), dim3((unsigned)grid), dim3(THREADS), 0, stream,
+    hipLaunchKernelGGL((mla_decode_kernel<T, DENSE, QE>), dim3((unsigned)grid), dim3(THREADS), 0, stream,
                        p);
     return hipGetLastError();
 }
 
-template <bool DENSE>
-hipError_t launch(int T, const Params& p, hipStream_t stream)
+template <bool DENSE, bool QE>
+hipError_t launch_q(int T, const Params& p, hipStream_t stream)
 {
     switch (T) {
-    case 1: return launch_t<1, DENSE>(p, stream);
-    case 2: return launch_t<2, DENSE>(p, stream);
-    default: return launch_t<4, DENSE>(p, stream);
+    case 1: return launch_t<1, DENSE, QE>(p, stream);
+    case 2: return launch_t<2, DENSE, QE>(p, stream);
+    default: return launch_t<4, DENSE, QE>(p, stream);
     }
+}
+
+template <bool DENSE>
+hipError_t launch(int T, int q_precision, const Params& p, hipStream_t stream)
+{
+    return q_precision == MLA_Q_E4M3 ? launch_q<DENSE, true>(T, p, stream)
+                                     : launch_q<DENSE, false>(T, p, stream);
 }
 
 mla_status_t common_checks(const void* q, const mla_kv_t* kv, int B, int Q, int H, void* o,
@@ -1630,11 +1638,13 @@ mla_status_t mla_plan_sparse(int B, int Q, int H, int K, mla_plan_t* plan)
     return MLA_OK;
 }
 
-mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* block_table,
-                              int max_pages, const int32_t* seq_lens, float scale, int B, int Q,
-                              int H, const mla_plan_t* plan, void* o, float* lse, void* workspace,
-                              size_t workspace_bytes, void* stream)
+mla_status_t mla_decode_dense_q(const void* q, const mla_kv_t* kv, const int32_t* block_table,
+                                int max_pages, const int32_t* seq_lens, float scale, int B, int Q,
+                                int H, const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (q_precision != MLA_Q_SPLIT && q_precision != MLA_Q_E4M3)
+        return MLA_ERR_UNSUPPORTED;
     mla_status_t st = common_checks(q, kv, B, Q, H, o, lse);
     if (st != MLA_OK || B == 0)
         return st;
@@ -1673,16 +1683,18 @@ mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* 
     p.o = (uint16_t*)o;
     p.lse = lse;
     fill_workspace(p, 1, B, Q, H, pl, workspace);
-    if (launch<true>(pl.tiles, p, (hipStream_t)stream) != hipSuccess)
+    if (launch<true>(pl.tiles, q_precision, p, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_LAUNCH;
     return MLA_OK;
 }
 
-mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t* rows, int K,
-                               const int32_t* valid, float scale, int B, int Q, int H,
-                               const mla_plan_t* plan, void* o, float* lse, void* workspace,
-                               size_t workspace_bytes, void* stream)
+mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_t* rows, int K,
+                                 const int32_t* valid, float scale, int B, int Q, int H,
+                                 const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (q_precision != MLA_Q_SPLIT && q_precision != MLA_Q_E4M3)
+        return MLA_ERR_UNSUPPORTED;
     mla_status_t st = common_checks(q, kv, B, Q, H, o, lse);
     if (st != MLA_OK || B == 0)
         return st;
@@ -1720,9 +1732,27 @@ mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t*
     p.o = (uint16_t*)o;
     p.lse = lse;
     fill_workspace(p, 0, B, Q, H, pl, workspace);
-    if (launch<false>(pl.tiles, p, (hipStream_t)stream) != hipSuccess)
+    if (launch<false>(pl.tiles, q_precision, p, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_LAUNCH;
     return MLA_OK;
+}
+
+mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* block_table,
+                              int max_pages, const int32_t* seq_lens, float scale, int B, int Q,
+                              int H, const mla_plan_t* plan, void* o, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    return mla_decode_dense_q(q, kv, block_table, max_pages, seq_lens, scale, B, Q, H, plan,
+                              MLA_Q_SPLIT, o, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t* rows, int K,
+                               const int32_t* valid, float scale, int B, int Q, int H,
+                               const mla_plan_t* plan, void* o, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    return mla_decode_sparse_q(q, kv, rows, K, valid, scale, B, Q, H, plan, MLA_Q_SPLIT, o, lse,
+                               workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -90,6 +90,26 @@ def test_bad_arguments_return_status_without_launching():
     assert _sparse(B=0) == OK                        # nothing to do, nothing launched
 
 
+def test_query_precision_entry_points_check_the_precision_first():
+    lib = mla._load()
+    kvs = _kv()
+    for bad in (-1, 2, 7):
+        assert lib.mla_decode_dense_q(None, ctypes.byref(kvs), None, 0, None, 0.07, 2, 1, 16, None,
+                                      bad, None, None, None, 0, None) == UNSUPPORTED
+        assert lib.mla_decode_sparse_q(None, ctypes.byref(kvs), None, 0, None, 0.07, 2, 1, 16, None,
+                                       bad, None, None, None, 0, None) == UNSUPPORTED
+    for good in (0, 1):
+        # then the same checks as the plain entry points
+        assert lib.mla_decode_dense_q(None, ctypes.byref(kvs), 0x2000, 4, 0x3000, 0.07, 2, 1, 16,
+                                      None, good, 0x4000, 0x5000, None, 0, None) == NULL
+        assert lib.mla_decode_sparse_q(0x1000, ctypes.byref(kvs), 0x2000, 0, 0x3000, 0.07, 2, 1, 16,
+                                       None, good, 0x4000, 0x5000, None, 0, None) == SHAPE
+        assert lib.mla_decode_sparse_q(0x1000, ctypes.byref(kvs), 0x2000, 8, 0x3000, 0.07, 0, 1, 16,
+                                       None, good, 0x4000, 0x5000, None, 0, None) == OK
+    with pytest.raises(ValueError):
+        mla._q_precision("fp8")
+
+
 def test_workspace_sizes_and_plans():
     for dense in (True, False):
         assert mla.workspace_bytes(dense, 4, 5, 16, (1, 1)) == 0
