@@ -296,7 +296,7 @@ def main():
         "unit": unit,
         "frac": round(achieved / peak, 4),
         "traffic": read_traffic(HEADLINE),
-        "kernel": "mla_decode_kernel<4, dense>",
+        "kernel": "mla_decode_kernel<4, true, false> (dense, split query)",
         "hbm_frac": h["hbm_frac"],
         "mfma_frac": h["mfma_frac"],
     }
