@@ -61,6 +61,10 @@ def _load():
         lib.mo_q_e4m3_bits.restype = None
         lib.mo_q_shift.argtypes = [ctypes.c_void_p]
         lib.mo_q_shift.restype = ctypes.c_int
+        lib.mo_combine_f64.argtypes = [P, P, i32, i64, P, P]
+        lib.mo_combine_f64.restype = None
+        lib.mo_combine.argtypes = [P, P, i32, i64, P, P]
+        lib.mo_combine.restype = None
         lib.mo_dense.argtypes = [P, i32, i32, i32, P, i64, i32, f32, P, i32, P, f32, i32, i32, i32,
                                  P, P, P, i64, i32, P, P, P]
         lib.mo_dense.restype = i32
@@ -194,3 +198,25 @@ def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, ch
     if rc != 0:
         raise ValueError("oracle: bad arguments")
     return _shape(B, Q, H, sel, o, lse, amb)
+
+
+def combine(o_parts, lse_parts):
+    """Merge of R partial decodes of the same rows over disjoint key parts (decode-context
+    parallelism): ``o_parts`` [R, ..., 512] as float64 values, or uint16 bf16 bits (the decode's
+    output format); ``lse_parts`` [R, ...] natural-log LSEs. Returns (o [..., 512], lse [...]) in
+    float64."""
+    o_parts = np.asarray(o_parts)
+    lse_parts = np.asarray(lse_parts)
+    R = o_parts.shape[0]
+    lead = o_parts.shape[1:-1]
+    assert o_parts.shape[-1] == 512 and lse_parts.shape == (R, *lead)
+    rows = int(np.prod(lead)) if lead else 1
+    o = np.zeros((rows, 512), np.float64)
+    lse = np.zeros((rows,), np.float64)
+    if o_parts.dtype == np.uint16:
+        _load().mo_combine(_ptr(_as(o_parts, np.uint16)), _ptr(_as(lse_parts, np.float32)), R, rows,
+                           _ptr(o), _ptr(lse))
+    else:
+        _load().mo_combine_f64(_ptr(_as(o_parts, np.float64)), _ptr(_as(lse_parts, np.float64)), R,
+                               rows, _ptr(o), _ptr(lse))
+    return o.reshape(*lead, 512), lse.reshape(lead)

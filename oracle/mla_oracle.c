@@ -19,6 +19,9 @@
  *             - SparseDcpDecode.merge: the fixed-order FP32 combine of the splits. Its identity
  *               (weights exp2(m_s - top)) holds for any division of the keys into consecutive
  *               splits, so a plan may also be given as explicit split boundaries per key group.
+ *             - module docstring, "push" and SparseDcpDecode: with decode-context parallelism each
+ *               rank decodes its share of a row's keys and sends the merged row (o, LSE) to the
+ *               head's owner, which merges the ranks' rows (mo_combine below).
  *   [AMD]     vllm.models.kimi_k3.amd.specialized_decode.mono.attention.mla_attn
  *             - module docstring: position i of a request's qlen query rows sees keys up to
  *               seq_len - qlen + i; a split with no visible key leaves LSE = -inf and o = 0.
@@ -572,4 +575,66 @@ int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t
     jb.amb = amb;
     jb.nthreads = threads;
     return run_job(&jb);
+}
+
+/* ---- combine of partial decodes (decode-context parallel merge) ------------------------------ */
+
+/*
+ * R partial results of the same query rows, each over a disjoint part of the rows' keys (a rank's
+ * share), merged the way the split partials are ([SPARSE] module docstring and merge: weights
+ * exp2(m_s - top), divided by the weighted total), here with natural-log LSEs, in rank order:
+ *   M = max_r lse_r;  w_r = exp(lse_r - M), 0 where lse_r = -inf;  L = sum_r w_r;
+ *   o = sum_r w_r o_r / L;  lse = M + ln L.
+ * A row with no partial holding a key (every lse_r = -inf) gets o = +0 and lse = -inf. A partial
+ * with lse_r = -inf is skipped without reading its o row (the page's push mode sends only the LSE
+ * of such a row).
+ * o_parts [R, rows, 512], lse_parts [R, rows]; o [rows, 512], lse [rows].
+ */
+void mo_combine_f64(const double* o_parts, const double* lse_parts, int R, int64_t rows, double* o,
+                    double* lse)
+{
+    for (int64_t i = 0; i < rows; i++) {
+        double M = -INFINITY;
+        for (int r = 0; r < R; r++)
+            if (lse_parts[(size_t)r * rows + i] > M)
+                M = lse_parts[(size_t)r * rows + i];
+        double* oi = o + (size_t)i * MO_LATENT;
+        for (int c = 0; c < MO_LATENT; c++)
+            oi[c] = 0.0;
+        if (M == -INFINITY) {
+            lse[i] = -INFINITY;
+            continue;
+        }
+        double L = 0.0;
+        for (int r = 0; r < R; r++) {
+            const double l = lse_parts[(size_t)r * rows + i];
+            if (l == -INFINITY)
+                continue; /* a rank without keys sends only its LSE: its o row is not read */
+            const double w = exp(l - M);
+            L += w;
+            const double* orow = o_parts + ((size_t)r * rows + i) * MO_LATENT;
+            for (int c = 0; c < MO_LATENT; c++)
+                oi[c] += w * orow[c];
+        }
+        for (int c = 0; c < MO_LATENT; c++)
+            oi[c] /= L;
+        lse[i] = M + log(L);
+    }
+}
+
+/* The same from the decode's output formats: o_parts bf16 bits, lse_parts FP32 (both exact in
+ * FP64). */
+void mo_combine(const uint16_t* o_parts, const float* lse_parts, int R, int64_t rows, double* o,
+                double* lse)
+{
+    const size_t n = (size_t)R * rows;
+    double* od = (double*)malloc(sizeof(double) * n * MO_LATENT + 1);
+    double* ld = (double*)malloc(sizeof(double) * n + 1);
+    for (size_t k = 0; k < n * MO_LATENT; k++)
+        od[k] = mo_bf16_decode(o_parts[k]);
+    for (size_t k = 0; k < n; k++)
+        ld[k] = (double)lse_parts[k];
+    mo_combine_f64(od, ld, R, rows, o, lse);
+    free(od);
+    free(ld);
 }
