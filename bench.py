@@ -170,6 +170,58 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
     return res, x
 
 
+# The decode-context-parallel combine: R ranks' (o, LSE) partials of the latency checkpoint's
+# rows (B=4, Q=5, H=16: one rank's share at DCP8) and of the top-k workload's rows (B=32, Q=5, H=64).
+COMBINE_CASES = {"dcp8_latency_rows": (8, 4 * 5 * 16), "dcp8_topk_rows": (8, 32 * 5 * 64)}
+
+
+def bench_combine(R, rows, steps, warmup, min_rotation_bytes=768 << 20, seed=0):
+    """mla.combine on synthetic partials (bf16 o ~ N(0,1) * 3, LSE ~ N(0,16), 10 % of the rank
+    rows empty), timed like the decode: graph replay over rotated input copies."""
+    import torch
+
+    import paged_mla_decode_fp8_amd as mla
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(seed)
+    o_host = (torch.randn((R, rows, 512), generator=g) * 3).to(torch.bfloat16)
+    lse_host = torch.randn((R, rows), generator=g) * 4
+    lse_host[torch.rand((R, rows), generator=g) < 0.1] = -math.inf
+    in_bytes = R * rows * (512 * 2 + 4)
+    copies = max(1, min(8, math.ceil(min_rotation_bytes / in_bytes)))
+    parts = [(o_host.to(dev), lse_host.to(dev)) for _ in range(copies)]
+    o = torch.empty((rows, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+
+    def call(k):
+        mla.combine(parts[k % copies][0], parts[k % copies][1], o=o, lse=lse)
+
+    for k in range(warmup):
+        call(k)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(copies):
+            call(k)
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / (reps * copies) * 1e3
+    alg = in_bytes + rows * (512 * 2 + 4)
+    del graph, parts
+    torch.cuda.empty_cache()
+    return {"R": R, "rows": rows, "us_per_call": round(us, 3), "alg_bytes": alg,
+            "GBps": round(alg / (us * 1e-6) / 1e9, 2), "hbm_frac": round(alg / (us * 1e-6) / HBM_PEAK, 4),
+            "hbm_floor_us": round(alg / HBM_PEAK * 1e6, 3), "input_copies_rotated": copies}
+
+
 def read_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this workload, or
     None if there is none or the kernel source changed since it was taken."""
@@ -236,6 +288,8 @@ def main():
                     help="query rows of the headline workload the CPU oracle is timed on")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the E4M3-query precision runs of every workload")
+    ap.add_argument("--no-combine", action="store_true",
+                    help="skip the decode-context-parallel combine runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (a known-size reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -283,6 +337,14 @@ def main():
         else:
             del x
 
+    combine = {}
+    if not args.no_combine:
+        for cname, (R, rows) in COMBINE_CASES.items():
+            combine[cname] = bench_combine(R, rows, args.steps, args.warmup)
+            c = combine[cname]
+            print(f"[bench] combine {cname} (R={R}, rows={rows}): {c['us_per_call']} us/call, "
+                  f"{c['GBps']} GB/s, hbm {c['hbm_frac']:.3f}", file=sys.stderr, flush=True)
+
     h = results[HEADLINE]
     sec = h["us_per_call"] * 1e-6
     if h["bound"] == "hbm":
@@ -324,6 +386,7 @@ def main():
         "cpu_baseline": cpu,
         "workloads": results,
         "q_e4m3": variants or None,
+        "dcp_combine": combine or None,
     }
     print(json.dumps(line))
 

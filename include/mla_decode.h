@@ -166,6 +166,26 @@ mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_
                                  const mla_plan_t* plan, int q_precision, void* o, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Combine of R partial decodes of the same query rows over disjoint parts of their keys: the
+ * decode-context-parallel merge at a row's owner (vllm.models.kimi_k3.nvidia.specialized_decode.
+ * cutedsl.dsa.attn_sparse, module docstring and "push": each rank decodes its share of the keys and
+ * sends the row's (o, LSE); the owner merges them as the split partials are merged). In rank order,
+ * FP32: M = max_r lse_r, w_r = exp(lse_r - M), o = BF16_RNE(sum_r w_r o_r / sum_r w_r),
+ * lse = M + ln(sum_r w_r). A partial with lse_r = -inf (a rank holding none of the row's keys) is
+ * skipped: its o row may hold anything (NaN included) and never enters the sums; a row that no
+ * rank holds a key of gets o = +0 and lse = -inf.
+ *   o_parts    device bf16 [R, rows, 512] (rank-major; each rank's rows as mla_decode_* writes o,
+ *              flattened), 16-byte aligned.
+ *   lse_parts  device float [R, rows]: natural-log LSEs as mla_decode_* writes them.
+ *   o, lse     device bf16 [rows, 512] (16-byte aligned) and float [rows].
+ * R >= 1; rows >= 0 (0: nothing launched). Errors: MLA_ERR_SHAPE (R < 1, rows < 0 or above
+ * 4 * (2^31 - 1)), MLA_ERR_NULL, MLA_ERR_ALIGN, MLA_ERR_LAUNCH. Asynchronous on `stream`; no
+ * workspace.
+ */
+mla_status_t mla_combine(const void* o_parts, const float* lse_parts, int R, int64_t rows, void* o,
+                         float* lse, void* stream);
+
 /* A static, human-readable name of a status. */
 const char* mla_status_string(mla_status_t status);
 

@@ -80,6 +80,8 @@ def _load():
         lib.mla_decode_sparse_q.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32, i32,
                                             ctypes.POINTER(_Plan), i32, P, P, P, sz, P]
         lib.mla_decode_sparse_q.restype = i32
+        lib.mla_combine.argtypes = [P, P, i32, ctypes.c_int64, P, P, P]
+        lib.mla_combine.restype = i32
         _lib = lib
     return _lib
 
@@ -144,12 +146,20 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _out_tensor(name, t, shape, dtype, device):
+    """A caller's output tensor must have exactly the shape the kernel writes."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _check_tensor(name, t, dtype, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _outputs(q, o, lse):
     B, Q, H, _ = q.shape
-    if o is None:
-        o = torch.empty((B, Q, H, 512), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
+    o = _out_tensor("o", o, (B, Q, H, 512), torch.bfloat16, q.device)
+    lse = _out_tensor("lse", lse, (B, Q, H), torch.float32, q.device)
     return o, lse
 
 
@@ -226,4 +236,26 @@ def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.T
         _ptr(q), ctypes.byref(kvs), _ptr(rows), K, _ptr(valid), float(scale), B, Q, H,
         _plan_arg(pl), qp, _ptr(o), _ptr(lse), _ptr(workspace),
         0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream)))
+    return o, lse
+
+
+def combine(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, o=None, lse=None):
+    """Merge of R partial decodes of the same rows (C ABI mla_combine): o_parts bf16 [R, ..., 512],
+    lse_parts f32 [R, ...] (natural log). Returns (o bf16 [..., 512], lse f32 [...]) on the
+    current stream."""
+    dev = o_parts.device
+    _check_tensor("o_parts", o_parts, torch.bfloat16, dev)
+    _check_tensor("lse_parts", lse_parts, torch.float32, dev)
+    R = o_parts.shape[0]
+    lead = tuple(o_parts.shape[1:-1])
+    if o_parts.shape[-1] != 512 or tuple(lse_parts.shape) != (R, *lead):
+        raise ValueError("o_parts must be [R, ..., 512] and lse_parts [R, ...]")
+    rows = 1
+    for d in lead:
+        rows *= d
+    o = _out_tensor("o", o, (*lead, 512), torch.bfloat16, dev)
+    lse = _out_tensor("lse", lse, lead, torch.float32, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(_load().mla_combine(_ptr(o_parts), _ptr(lse_parts), R, rows, _ptr(o), _ptr(lse),
+                               ctypes.c_void_p(stream)))
     return o, lse

@@ -7,6 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "mla_decode.hip")
+SOURCES = [SRC, os.path.join(HERE, "csrc", "mla_combine.hip")]
 HEADER = os.path.join(ROOT, "include", "mla_decode.h")
 LIB = os.path.join(HERE, "libmla_decode.so")
 
@@ -20,12 +21,13 @@ HIPCC_FLAGS = [
 def build(force: bool = True) -> str:
     """Compile the library (always, unless force=False and it is newer than its sources)."""
     if not force and os.path.exists(LIB):
-        newest = max(os.path.getmtime(SRC), os.path.getmtime(HEADER), os.path.getmtime(__file__))
+        newest = max(max(os.path.getmtime(f) for f in SOURCES), os.path.getmtime(HEADER),
+                     os.path.getmtime(__file__))
         if os.path.getmtime(LIB) >= newest:
             return LIB
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SOURCES]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB

@@ -149,3 +149,30 @@ def test_chooser_picks_the_benchmark_plans():
         p = mla.plan_dense(B, Q, H, n, 64) if kind == "dense" else mla.plan_sparse(B, Q, H, n)
         w = wl.WORKLOADS[name]
         assert (p.splits, p.tiles, p.mode) == w.plan, name
+
+
+def test_combine_checks_arguments_without_launching():
+    lib = mla._load()
+    c = lib.mla_combine
+    assert c(0x1000, 0x2000, 0, 4, 0x3000, 0x4000, None) == SHAPE      # R < 1
+    assert c(0x1000, 0x2000, 2, -1, 0x3000, 0x4000, None) == SHAPE     # rows < 0
+    assert c(0x1000, 0x2000, 2, 1 << 40, 0x3000, 0x4000, None) == SHAPE
+    assert c(None, None, 2, 0, None, None, None) == OK                  # nothing to do
+    assert c(None, 0x2000, 2, 4, 0x3000, 0x4000, None) == NULL
+    assert c(0x1000, 0x2000, 2, 4, 0x3000, None, None) == NULL
+    assert c(0x1008, 0x2000, 2, 4, 0x3000, 0x4000, None) == ALIGN
+    assert c(0x1000, 0x2002, 2, 4, 0x3000, 0x4000, None) == ALIGN
+    assert c(0x1000, 0x2000, 2, 4, 0x3004, 0x4000, None) == ALIGN
+
+
+def test_binding_rejects_output_tensors_of_the_wrong_shape():
+    import torch
+    q = torch.zeros(2, 1, 16, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mla._outputs(q, torch.zeros(2, 1, 16, 511, dtype=torch.bfloat16), None)
+    with pytest.raises(ValueError):
+        mla._outputs(q, None, torch.zeros(2, 16, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        mla._outputs(q, torch.zeros(2, 1, 16, 512, dtype=torch.float32), None)
+    o, lse = mla._outputs(q, None, None)
+    assert tuple(o.shape) == (2, 1, 16, 512) and tuple(lse.shape) == (2, 1, 16)
