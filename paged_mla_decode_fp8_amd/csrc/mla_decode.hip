@@ -551,6 +551,12 @@ __device__ inline int64_t partial_o_offset(int slot, int pw, int t, int c, int l
     return ((((int64_t)slot * 4 + pw) * T + t) * 8 + c) * 256 + 4 * lane;
 }
 
+// Where an item found last before its epilogue keeps its own (m, l) rows in LDS: right after its O
+// partial (both in the KV slots, free once the block loop is done). Offset in floats.
+template <int T>
+__device__ constexpr int own_ml_offset() { return 4 * T * 8 * 256; }
+static_assert((own_ml_offset<4>() + 4 * 16 * 2) * 4 <= 2 * SLOT, "own partial fits the KV slots");
+
 // Q staging: the tile set's T * 16 query rows (bf16, 1152 B each, from row row0 of q) are DMA'd by
 // the QK waves into KV slot 1, which stays free until iteration 0 issues the DMA of block 1. LDS
 // unit (16 bytes) 72 r + c of row r holds the row's unit c ^ s(r) for the latent units c < 64,
@@ -955,6 +961,17 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                 fl[(sub0 / 2 + pp) * (T * 16) + (qt0 + j) * 16 + n16] = l_run[j][pp];
         }
     }
+    int* misc = reinterpret_cast<int*>(smem + L::OFF_MISC);
+    if (w.count > 1 && qw == 0 && lane == 0) {
+        // A split item that finds every other item of its (group, tile set) counted in is the
+        // last: it keeps its partial in LDS and merges at once (no store, release or count).
+        const uint32_t seen = __hip_atomic_load(p.ws_cnt + (int64_t)w.g * p.tilesets + w.ts,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = seen == (uint32_t)(w.count - 1);
+        if (last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the others' released partials
+        misc[1] = last ? 1 : 0;
+    }
     __syncthreads();   // E1
     if (!(grp == 0 && kq == 0))
         return;
@@ -966,9 +983,10 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         if (w.count == 1) {
             p.lse[orow] = (l > 0.f) ? (m_run[j] - LOG2_ANCHOR + log2f(l)) * LN2 : neg_inf;
         } else {
-            const int64_t prow = (int64_t)w.slot * (T * 16) + r;
-            p.ws_ml[prow * 2 + 0] = m_run[j];
-            p.ws_ml[prow * 2 + 1] = l;
+            float* dst = misc[1] == 0 ? p.ws_ml + ((int64_t)w.slot * (T * 16) + r) * 2
+                                      : reinterpret_cast<float*>(smem) + own_ml_offset<T>() + r * 2;
+            dst[0] = m_run[j];
+            dst[1] = l;
         }
     }
 }
@@ -1200,22 +1218,40 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         }
         return;
     }
+    // a split item: the partial to the workspace, or, for the item found last before E1, to the
+    // KV slots (free now, 128 KB for four tiles) for its own merge
+    const bool last = reinterpret_cast<const int*>(smem + L::OFF_MISC)[1] != 0;
 #pragma unroll
     for (int t = 0; t < T; t++)
 #pragma unroll
-        for (int c = 0; c < 8; c++)
-            *reinterpret_cast<v4f*>(p.ws_o + partial_o_offset<T>(w.slot, pw, t, c, lane)) = O[t][c];
+        for (int c = 0; c < 8; c++) {
+            if (last)
+                *reinterpret_cast<v4f*>(smem + 4 * partial_o_offset<T>(0, pw, t, c, lane)) = O[t][c];
+            else
+                *reinterpret_cast<v4f*>(p.ws_o + partial_o_offset<T>(w.slot, pw, t, c, lane)) = O[t][c];
+        }
 }
 
 // The last arriving item of a (group, tile set) merges the group's FP32 partials in split order.
 // Thread (wave c, lane) owns column block c of every column quarter and tile for rows
 // 16 t + lane % 16: per contributor it weighs T rows and issues 4 T contiguous loads at once.
+// own_lds: this item's own partial is in LDS, in the workspace's layout at the start of the KV
+// slots (O, then (m, l) at own_ml_offset<T>()), rather than in the workspace; the loads go through
+// generic pointers so that one code path reads both.
 template <int T>
-__device__ void merge_splits(const Params& p, const Work& w, int tid)
+__device__ void merge_splits(const Params& p, const Work& w, int tid, const uint8_t* smem, bool own_lds)
 {
     const float neg_inf = -INFINITY;
     const int lane = tid & 63, c = tid >> 6;
     const int n16 = lane & 15, grp = lane >> 4;
+    auto o_base = [&](int slot) -> const float* {
+        return (own_lds && slot == w.slot) ? reinterpret_cast<const float*>(smem)
+                                           : p.ws_o + partial_o_offset<T>(slot, 0, 0, 0, 0);
+    };
+    auto ml_base = [&](int slot) -> const float* {
+        return (own_lds && slot == w.slot) ? reinterpret_cast<const float*>(smem) + own_ml_offset<T>()
+                                           : p.ws_ml + (int64_t)slot * (T * 16) * 2;
+    };
     // per contributor: its (m, l) for the T rows and its 4 T partial loads
     struct Part {
         v2f ml[T];
@@ -1223,14 +1259,16 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid)
     };
     auto load_part = [&](int q, Part& pt) {
         const int slot = contributor_slot(p, w, q);
+        const float* mlb = ml_base(slot);
+        const float* ob = o_base(slot);
 #pragma unroll
         for (int t = 0; t < T; t++)
-            pt.ml[t] = *reinterpret_cast<const v2f*>(p.ws_ml + ((int64_t)slot * (T * 16) + 16 * t + n16) * 2);
+            pt.ml[t] = *reinterpret_cast<const v2f*>(mlb + (16 * t + n16) * 2);
 #pragma unroll
         for (int pw = 0; pw < 4; pw++)
 #pragma unroll
             for (int t = 0; t < T; t++)
-                pt.x[pw][t] = *reinterpret_cast<const v4f*>(p.ws_o + partial_o_offset<T>(slot, pw, t, c, lane));
+                pt.x[pw][t] = *reinterpret_cast<const v4f*>(ob + partial_o_offset<T>(0, pw, t, c, lane));
     };
     // One round trip for the common case: the first two contributors' partials and every
     // contributor's maximum are requested before any of them is used.
@@ -1245,9 +1283,9 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid)
         total[t] = 0.f;
     }
     for (int q = 2; q < w.count; q++) {
-        const int64_t prow = (int64_t)contributor_slot(p, w, q) * (T * 16);
+        const float* mlb = ml_base(contributor_slot(p, w, q));
 #pragma unroll
-        for (int t = 0; t < T; t++) top[t] = fmaxf(top[t], p.ws_ml[(prow + 16 * t + n16) * 2]);
+        for (int t = 0; t < T; t++) top[t] = fmaxf(top[t], mlb[(16 * t + n16) * 2]);
     }
     if (w.count > 1) {
 #pragma unroll
@@ -1312,12 +1350,20 @@ __device__ __forceinline__ void finish_item(const Params& p, uint8_t* smem, cons
     using L = Smem<T>;
     if (w.count == 1)
         return;
+    int* misc = reinterpret_cast<int*>(smem + L::OFF_MISC);
+    uint32_t* cnt = p.ws_cnt + (int64_t)w.g * p.tilesets + w.ts;
+    if (misc[1] != 0) {
+        // found last before E1 (its acquire made there): the partial is in LDS; merge now
+        __syncthreads();   // E2: the PV waves' LDS copies of O
+        merge_splits<T>(p, w, tid, smem, true);
+        if (tid == 0)
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     // a split item: every thread's partial stores completed (vmcnt(0)) before the barrier; one
     // thread then releases them at agent scope and counts this item in; the last arriver merges.
     __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();   // E2
-    int* misc = reinterpret_cast<int*>(smem + L::OFF_MISC);
-    uint32_t* cnt = p.ws_cnt + (int64_t)w.g * p.tilesets + w.ts;
     if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1327,7 +1373,7 @@ __device__ __forceinline__ void finish_item(const Params& p, uint8_t* smem, cons
     __syncthreads();   // E3
     if (misc[0] == 0)
         return;
-    merge_splits<T>(p, w, tid);
+    merge_splits<T>(p, w, tid, smem, false);
     if (tid == 0)
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
