@@ -222,6 +222,57 @@ def bench_combine(R, rows, steps, warmup, min_rotation_bytes=768 << 20, seed=0):
             "hbm_floor_us": round(alg / HBM_PEAK * 1e6, 3), "input_copies_rotated": copies}
 
 
+# The top-k producer at the top-k workload's shape: B=32 requests x Q=5 rows of indexer logits over
+# a 32768-position context, K=2048, positions remapped through 64-row pages (request b's position p
+# is cache row b * 32768 + p, as in that workload's cache).
+TOPK_CASE = {"B": 32, "Q": 5, "N": 32768, "K": 2048, "page": 64}
+
+
+def bench_topk(steps, warmup, seed=0):
+    """mla.topk_rows on synthetic bf16 logits ~ N(0,1), causal row ends (row (b, i) sees
+    N - Q + i + 1 positions), timed by graph replay (the 10 MB of logits stay L2/MALL-resident)."""
+    import torch
+
+    import paged_mla_decode_fp8_amd as mla
+
+    c = TOPK_CASE
+    B, Q, N, K, page = c["B"], c["Q"], c["N"], c["K"], c["page"]
+    R = B * Q
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(seed)
+    logits = torch.randn((R, N), generator=g).to(torch.bfloat16).to(dev)
+    ends = torch.tensor([N - Q + (r % Q) + 1 for r in range(R)], dtype=torch.int32, device=dev)
+    pages = N // page
+    table = (torch.arange(B * pages, dtype=torch.int32).view(B, pages)).to(dev)
+    rows = torch.empty((R, K), dtype=torch.int32, device=dev)
+    valid = torch.empty((R,), dtype=torch.int32, device=dev)
+
+    def call():
+        mla.topk_rows(logits, ends, K, block_table=table, page_size=page, q_per_request=Q,
+                      num_rows=B * N, rows=rows, valid=valid)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / steps * 1e3
+    alg = R * N * 2 + R * K * 4 + R * 8 + B * pages * 4
+    del graph
+    return {**c, "rows": R, "us_per_call": round(us, 3), "alg_bytes": alg,
+            "GBps": round(alg / (us * 1e-6) / 1e9, 2), "hbm_floor_us": round(alg / HBM_PEAK * 1e6, 3)}
+
+
 def read_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this workload, or
     None if there is none or the kernel source changed since it was taken."""
@@ -289,7 +340,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the E4M3-query precision runs of every workload")
     ap.add_argument("--no-combine", action="store_true",
-                    help="skip the decode-context-parallel combine runs")
+                    help="skip the decode-context-parallel combine and top-k producer runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (a known-size reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -344,6 +395,11 @@ def main():
             c = combine[cname]
             print(f"[bench] combine {cname} (R={R}, rows={rows}): {c['us_per_call']} us/call, "
                   f"{c['GBps']} GB/s, hbm {c['hbm_frac']:.3f}", file=sys.stderr, flush=True)
+        topk_res = bench_topk(args.steps, args.warmup)
+        print(f"[bench] top-k producer ({topk_res['rows']} rows x {topk_res['N']} -> "
+              f"{topk_res['K']}): {topk_res['us_per_call']} us/call", file=sys.stderr, flush=True)
+    else:
+        topk_res = None
 
     h = results[HEADLINE]
     sec = h["us_per_call"] * 1e-6
@@ -387,6 +443,7 @@ def main():
         "workloads": results,
         "q_e4m3": variants or None,
         "dcp_combine": combine or None,
+        "topk_producer": topk_res,
     }
     print(json.dumps(line))
 

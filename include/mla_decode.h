@@ -186,6 +186,32 @@ mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_
 mla_status_t mla_combine(const void* o_parts, const float* lse_parts, int R, int64_t rows, void* o,
                          float* lse, void* stream);
 
+/*
+ * Top-k selection of key positions from bf16 indexer logits, remapped to cache rows: the index
+ * lists (rows, valid) mla_decode_sparse reads. (vllm.models.kimi_k3.nvidia.specialized_decode.
+ * cutedsl.dsa.topk_exchange, push_local_topk and the merge's radix select; vllm.model_executor.
+ * kernels.attention.dsa.sparse_mqa_logits, the remap.) For logits row r (request b = r / Q):
+ *   - candidates: the non-NaN values at columns [0, min(row_ends[r], N)), ranked by the 16-bit
+ *     order key of their bits (positive: bits | 0x8000, negative: ~bits; -0 just below +0);
+ *   - fewer than K candidates: all of them, in column order; otherwise the threshold key v is the
+ *     K-th largest, and the list is every column above v in column order, then the lowest columns
+ *     equal to v, in column order, up to K in all;
+ *   - each selected column j becomes cache row block_table[b, j / page_size] * page_size +
+ *     j % page_size (-1 when its page index is >= max_pages, its page id is negative or its row is
+ *     >= num_rows); with block_table NULL the column itself;
+ *   - rows_out[r, 0 .. count) holds the list, rows_out[r, count .. K) holds -1, valid_out[r] =
+ *     count (min(K, candidates)).
+ *   logits     device bf16 [R, N], 16-byte aligned; N a multiple of 8.
+ *   row_ends   device int32 [R]; block_table device int32 [ceil(R / Q), max_pages] or NULL.
+ *   rows_out   device int32 [R, K]; valid_out device int32 [R].
+ * Errors: MLA_ERR_SHAPE (R < 0, N < 8 or not a multiple of 8, K < 1, Q < 1, or with a table
+ * max_pages < 1, page_size < 1, num_rows < 0 or max_pages * page_size above 2^31 - 1),
+ * MLA_ERR_NULL, MLA_ERR_ALIGN, MLA_ERR_LAUNCH. R = 0 launches nothing. Asynchronous on `stream`.
+ */
+mla_status_t mla_topk_rows(const void* logits, const int32_t* row_ends, int R, int N, int K,
+                           const int32_t* block_table, int max_pages, int page_size, int Q,
+                           int64_t num_rows, int32_t* rows_out, int32_t* valid_out, void* stream);
+
 /* A static, human-readable name of a status. */
 const char* mla_status_string(mla_status_t status);
 

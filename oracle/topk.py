@@ -13,8 +13,8 @@ What it computes (vLLM API pages, cited by title and section):
   column whose key is above ``v`` is selected, and of the columns whose key equals ``v`` the
   lowest-numbered ones fill the remaining places (the tie rule). The selected columns come out in
   that order: the columns above the threshold in increasing column order, then the threshold
-  columns in increasing column order. A row with at most K candidates selects all of them, in
-  column order.
+  columns in increasing column order. A row with fewer than K candidates selects all of them, in
+  column order (the threshold is found only once K candidates are reached).
 * ``vllm.model_executor.kernels.attention.dsa.sparse_mqa_logits`` -- the remap of selected
   columns to positions and the -1 padding of the lists (columns outside the row's range become
   -1). Here the positions are a request's key positions, turned into cache rows through the
@@ -48,7 +48,7 @@ def select_row(bits_row: np.ndarray, row_end: int, k: int) -> np.ndarray:
     cols = np.arange(n)
     cols = cols[~is_nan(bits_row[:n])]
     keys = order_key(bits_row[:n])[cols]
-    if cols.size <= k:
+    if cols.size < k:
         return cols.copy()
     # rank by (key descending, column ascending); the k-th is the threshold
     order = np.lexsort((cols, -keys))

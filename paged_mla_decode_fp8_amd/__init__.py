@@ -82,6 +82,9 @@ def _load():
         lib.mla_decode_sparse_q.restype = i32
         lib.mla_combine.argtypes = [P, P, i32, ctypes.c_int64, P, P, P]
         lib.mla_combine.restype = i32
+        lib.mla_topk_rows.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, ctypes.c_int64, P, P,
+                                      P]
+        lib.mla_topk_rows.restype = i32
         _lib = lib
     return _lib
 
@@ -259,3 +262,30 @@ def combine(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, o=None, lse=None)
     _check(_load().mla_combine(_ptr(o_parts), _ptr(lse_parts), R, rows, _ptr(o), _ptr(lse),
                                ctypes.c_void_p(stream)))
     return o, lse
+
+
+def topk_rows(logits: torch.Tensor, row_ends: torch.Tensor, k: int, *, block_table=None,
+              page_size: int = 1, q_per_request: int = 1, num_rows: int = 0, rows=None,
+              valid=None):
+    """Top-k key positions of bf16 logits [R, N] (C ABI mla_topk_rows), remapped to cache rows
+    through ``block_table`` [R / q_per_request, max_pages] when given. Returns (rows int32 [R, k]
+    with -1 padding, valid int32 [R]) on the current stream."""
+    dev = logits.device
+    _check_tensor("logits", logits, torch.bfloat16, dev)
+    _check_tensor("row_ends", row_ends, torch.int32, dev)
+    R, N = logits.shape
+    if tuple(row_ends.shape) != (R,):
+        raise ValueError("row_ends must be [R]")
+    max_pages = 0
+    if block_table is not None:
+        _check_tensor("block_table", block_table, torch.int32, dev)
+        max_pages = block_table.shape[1]
+        if block_table.shape[0] * q_per_request < R:
+            raise ValueError("block_table needs a row per request")
+    rows = _out_tensor("rows", rows, (R, k), torch.int32, dev)
+    valid = _out_tensor("valid", valid, (R,), torch.int32, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(_load().mla_topk_rows(_ptr(logits), _ptr(row_ends), R, N, int(k), _ptr(block_table),
+                                 max_pages, int(page_size), int(q_per_request), int(num_rows),
+                                 _ptr(rows), _ptr(valid), ctypes.c_void_p(stream)))
+    return rows, valid

@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "mla_decode.hip")
-SOURCES = [SRC, os.path.join(HERE, "csrc", "mla_combine.hip")]
+SOURCES = [SRC, os.path.join(HERE, "csrc", "mla_combine.hip"), os.path.join(HERE, "csrc", "mla_topk.hip")]
 HEADER = os.path.join(ROOT, "include", "mla_decode.h")
 LIB = os.path.join(HERE, "libmla_decode.so")
 

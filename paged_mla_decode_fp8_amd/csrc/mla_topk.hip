@@ -1,0 +1,286 @@
+// Top-k selection of key positions from bf16 indexer logits and their remap to cache rows (gfx950):
+// the index lists the top-k sparse decode reads.
+//
+// What it computes (vLLM API pages, cited by title and section):
+//   vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.topk_exchange, push_local_topk and
+//   the merge's radix select: a row's candidates are its non-NaN bf16 logits at columns
+//   [0, min(row_end, N)); each is ranked by a 16-bit order key of its bits; the threshold v is the
+//   K-th largest key; the columns above v are all selected and the lowest-numbered columns equal
+//   to v fill the remaining places; the output lists the columns above v in increasing column
+//   order, then those equal to v in increasing column order. A row with fewer than K candidates
+//   selects all of them, in column order.
+//   vllm.model_executor.kernels.attention.dsa.sparse_mqa_logits, the remap: selected columns
+//   become positions, and places without a valid position hold -1. Here position j of request b
+//   is cache row table[b, j / page_size] * page_size + j % page_size (the dense decode's rule).
+// The order key (a reading: the pages do not print it) is the monotone map of the sign-magnitude
+// pattern to an unsigned integer: positive bits | 0x8000, negative ~bits.
+//
+// One 512-thread workgroup per row. The row is taken in spans of 32768 columns; in a span thread t
+// owns the 64 consecutive columns 64 t .. 64 t + 63 (eight 16-byte loads), whose order keys it
+// forms once and keeps packed two to a register (0 for NaN and past the row end), so a row of at
+// most 32768 columns is read from memory once for all three passes. The threshold comes
+// from two radix histograms in LDS: the key's top 12 bits (4096 bins: sign, exponent and three
+// fraction bits, so the LDS atomics of clustered values spread over many bins), then its low 4
+// bits among the keys in the chosen bin. The ordered output: per thread two 64-bit masks (columns
+// above / equal to the threshold), one workgroup prefix sum per span of their popcounts (wave
+// prefix by lane shuffles, then the eight wave totals through LDS) and the set bits in ascending
+// order: thread order is column order, so the lists come out in column order without a sort.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mla_decode.h"
+
+namespace {
+
+constexpr int TK_THREADS = 512;
+constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int TK_VEC = 8;                         // 16-byte loads (8 columns each) per thread
+constexpr int TK_OWN = 8 * TK_VEC;                // columns per thread per span
+constexpr int TK_SPAN = TK_THREADS * TK_OWN;      // 32768 columns
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+constexpr int TK_HI_BITS = 12;                    // first radix digit: key bits 15..4
+constexpr int TK_LO_BITS = 16 - TK_HI_BITS;       // second digit: key bits 3..0
+constexpr int TK_BINS = 1 << TK_HI_BITS;
+constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the threshold search (8)
+
+struct TkShared {
+    uint32_t hist[TK_BINS + 1];   // the last counter takes the NaN / past-the-end columns (unused)
+    int wave_tot[TK_WAVES];
+    int sel[4];   // first-digit bin, keys above it, second-digit bin, keys above the threshold
+};
+
+// the order key of a bf16 pattern (16 bits), or 0 for NaN (no valid key is 0: -inf maps to 0x7F)
+__device__ inline uint32_t tk_key(uint32_t b)
+{
+    if ((b & 0x7FFFu) > 0x7F80u)
+        return 0u;
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order (and the total).
+__device__ inline int tk_scan(int x, TkShared& sh, int& total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int v = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += y;
+    }
+    if (lane == 63)
+        sh.wave_tot[wave] = v;
+    __syncthreads();
+    int off = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; w++) {
+        const int t = sh.wave_tot[w];
+        off += w < wave ? t : 0;
+        total += t;
+    }
+    __syncthreads();   // wave_tot is reused by the next scan
+    return off + v - x;
+}
+
+constexpr int TK_KW = TK_OWN / 2;                 // key registers per thread (two keys each)
+
+// The order keys of this thread's 64 columns of the span starting at s0: kw[i] holds column 2 i in
+// its low half and column 2 i + 1 in its high half (0 past the row end).
+__device__ inline void tk_keys(const uint16_t* row, int n, int s0, uint32_t (&kw)[TK_KW])
+{
+    const int c = s0 + TK_OWN * (int)threadIdx.x;
+    v4i_t raw[TK_VEC];
+#pragma unroll
+    for (int m = 0; m < TK_VEC; m++) {
+        raw[m] = v4i_t{0, 0, 0, 0};
+        if (c + 8 * m < n)   // n <= N and N % 8 == 0: the whole 16-byte vector lies in the row
+            raw[m] = *reinterpret_cast<const v4i_t*>(row + c + 8 * m);
+    }
+#pragma unroll
+    for (int i = 0; i < TK_KW; i++) {
+        const uint32_t w = (uint32_t)raw[i >> 2][i & 3];
+        const int col = c + 2 * i;
+        const uint32_t lo = col < n ? tk_key(w & 0xFFFFu) : 0u;
+        const uint32_t hi = col + 1 < n ? tk_key(w >> 16) : 0u;
+        kw[i] = lo | (hi << 16);
+    }
+}
+
+// Of the nbins bins (counts in sh.hist), the highest bin b whose count together with the bins
+// above it reaches need; sh.sel[slot] = b (-1 if none), sh.sel[slot + 1] = the count above b.
+// Thread t looks at bins nbins - 1 - TK_BPT t - i, i = 0 .. TK_BPT - 1 (from the top).
+__device__ inline void tk_pick_bin(TkShared& sh, int nbins, int need, int slot)
+{
+    const int t = threadIdx.x;
+    int c[TK_BPT];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < TK_BPT; i++) {
+        const int bin = nbins - 1 - TK_BPT * t - i;
+        c[i] = bin >= 0 ? (int)sh.hist[bin] : 0;
+        mine += c[i];
+    }
+    int total;
+    int excl = tk_scan(mine, sh, total);
+    if (t == 0) {
+        sh.sel[slot] = -1;
+        sh.sel[slot + 1] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TK_BPT; i++) {
+        if (c[i] > 0 && excl < need && excl + c[i] >= need) {
+            sh.sel[slot] = nbins - 1 - TK_BPT * t - i;
+            sh.sel[slot + 1] = excl;
+        }
+        excl += c[i];
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
+    const uint16_t* __restrict__ logits, const int32_t* __restrict__ row_ends, int N, int K,
+    const int32_t* __restrict__ table, int max_pages, int page_size, int Q, int64_t num_rows,
+    int32_t* __restrict__ rows_out, int32_t* __restrict__ valid_out)
+{
+    __shared__ TkShared sh;
+    const int r = blockIdx.x;
+    const int t = threadIdx.x;
+    const uint16_t* row = logits + (int64_t)r * N;
+    int n = row_ends[r];
+    n = n < 0 ? 0 : (n > N ? N : n);
+    int32_t* out = rows_out + (int64_t)r * K;
+    const int b = r / Q;
+    // a row of one span stays in registers for all three passes
+    const bool resident = n <= TK_SPAN;
+    uint32_t kw[TK_KW];
+    if (resident)
+        tk_keys(row, n, 0, kw);
+
+    // pass 1: histogram of the candidates' first digits (NaN and columns past the end skipped)
+    for (int i = t; i <= TK_BINS; i += TK_THREADS)
+        sh.hist[i] = 0u;
+    __syncthreads();
+    for (int s0 = 0; s0 < n; s0 += TK_SPAN) {
+        if (!resident)
+            tk_keys(row, n, s0, kw);
+#pragma unroll
+        for (int e = 0; e < TK_OWN; e++) {
+            const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            atomicAdd(&sh.hist[k != 0u ? k >> TK_LO_BITS : TK_BINS], 1u);   // no branch
+        }
+    }
+    __syncthreads();
+    // the threshold: v = 0 selects every candidate (fewer than K of them)
+    uint32_t v = 0u;
+    int c_gt = 0;
+    tk_pick_bin(sh, TK_BINS, K, 0);
+    const int b1 = sh.sel[0];
+    if (b1 >= 0) {
+        const int above = sh.sel[1];
+        // pass 2: histogram of the second digits of the keys in bin b1
+        if (t < (1 << TK_LO_BITS))
+            sh.hist[t] = 0u;
+        __syncthreads();
+        for (int s0 = 0; s0 < n; s0 += TK_SPAN) {
+            if (!resident)
+                tk_keys(row, n, s0, kw);
+#pragma unroll
+            for (int e = 0; e < TK_OWN; e++) {
+                const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                if (k != 0u && (int)(k >> TK_LO_BITS) == b1)
+                    atomicAdd(&sh.hist[k & ((1u << TK_LO_BITS) - 1u)], 1u);
+            }
+        }
+        __syncthreads();
+        tk_pick_bin(sh, 1 << TK_LO_BITS, K - above, 2);
+        v = ((uint32_t)b1 << TK_LO_BITS) | (uint32_t)sh.sel[2];
+        c_gt = above + sh.sel[3];
+    }
+    // pass 3: the selected columns in order, remapped to cache rows
+    int gt_run = 0, eq_run = 0;
+    const int eq_room = K - c_gt;
+    for (int s0 = 0; s0 < n; s0 += TK_SPAN) {
+        if (!resident)
+            tk_keys(row, n, s0, kw);
+        // bit e of the masks: column e of this thread's part is above / equal to the threshold
+        // (a key equal to v is never 0: v = 0 only when every candidate is taken)
+        uint32_t gm[2] = {0u, 0u}, em[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < TK_OWN; e++) {
+            const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            gm[e >> 5] |= (k > v ? 1u : 0u) << (e & 31);
+            em[e >> 5] |= (k == v && v != 0u ? 1u : 0u) << (e & 31);
+        }
+        uint64_t gtm = ((uint64_t)gm[1] << 32) | gm[0];
+        uint64_t eqm = ((uint64_t)em[1] << 32) | em[0];
+        int tot_gt, tot_eq;
+        int pg = gt_run + tk_scan(__builtin_popcountll(gtm), sh, tot_gt);
+        int pe = eq_run + tk_scan(__builtin_popcountll(eqm), sh, tot_eq);
+        const int cbase = s0 + TK_OWN * t;
+        for (; gtm; gtm &= gtm - 1)   // in column order
+            out[pg++] = cbase + __builtin_ctzll(gtm);
+        for (; eqm && pe < eq_room; eqm &= eqm - 1)
+            out[c_gt + pe++] = cbase + __builtin_ctzll(eqm);
+        gt_run += tot_gt;
+        eq_run += tot_eq;
+    }
+    const int count = b1 >= 0 ? K : gt_run;
+    // the columns -> cache rows, each thread a strided share of the list (its writes are the
+    // workgroup's, visible after the barrier)
+    __syncthreads();
+    for (int i = t; i < K; i += TK_THREADS) {
+        int32_t rr = -1;
+        if (i < count) {
+            const int j = out[i];
+            rr = j;
+            if (table) {
+                const int pgi = j / page_size;
+                rr = -1;
+                if (pgi < max_pages) {
+                    const int64_t page = table[(int64_t)b * max_pages + pgi];
+                    const int64_t cr = page * page_size + j % page_size;
+                    if (page >= 0 && cr < num_rows)
+                        rr = (int32_t)cr;
+                }
+            }
+        }
+        out[i] = rr;
+    }
+    if (t == 0)
+        valid_out[r] = count;
+}
+
+bool tk_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_topk_rows(const void* logits, const int32_t* row_ends, int R, int N, int K,
+                           const int32_t* block_table, int max_pages, int page_size, int Q,
+                           int64_t num_rows, int32_t* rows_out, int32_t* valid_out, void* stream)
+{
+    if (R < 0 || N < 8 || N % 8 != 0 || K < 1 || Q < 1 || R > 0x7FFFFFFF)
+        return MLA_ERR_SHAPE;
+    if (block_table && (max_pages < 1 || page_size < 1 || num_rows < 0 ||
+                        (int64_t)max_pages * page_size > 0x7FFFFFFF))
+        return MLA_ERR_SHAPE;
+    if (R == 0)
+        return MLA_OK;
+    if (!logits || !row_ends || !rows_out || !valid_out)
+        return MLA_ERR_NULL;
+    if (!tk_aligned(logits, 16) || !tk_aligned(row_ends, 4) || !tk_aligned(rows_out, 4) ||
+        !tk_aligned(valid_out, 4) || !tk_aligned(block_table, 4))
+        return MLA_ERR_ALIGN;
+    hipLaunchKernelGGL(mla_topk_kernel, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
+                       (const uint16_t*)logits, row_ends, N, K, block_table, max_pages, page_size, Q,
+                       num_rows, rows_out, valid_out);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

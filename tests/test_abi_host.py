@@ -176,3 +176,25 @@ def test_binding_rejects_output_tensors_of_the_wrong_shape():
         mla._outputs(q, torch.zeros(2, 1, 16, 512, dtype=torch.float32), None)
     o, lse = mla._outputs(q, None, None)
     assert tuple(o.shape) == (2, 1, 16, 512) and tuple(lse.shape) == (2, 1, 16)
+
+
+def test_topk_checks_arguments_without_launching():
+    lib = mla._load()
+    f = lib.mla_topk_rows
+    args = lambda **kw: dict(dict(lg=0x1000, re=0x2000, R=4, N=64, K=8, tb=None, mp=0, ps=1, Q=1,  # noqa: E731
+                                  nr=0, ro=0x3000, vo=0x4000), **kw)
+    call = lambda a: f(a["lg"], a["re"], a["R"], a["N"], a["K"], a["tb"], a["mp"], a["ps"], a["Q"],  # noqa: E731
+                       a["nr"], a["ro"], a["vo"], None)
+    assert call(args(R=-1)) == SHAPE
+    assert call(args(N=60)) == SHAPE           # not a multiple of 8
+    assert call(args(N=0)) == SHAPE
+    assert call(args(K=0)) == SHAPE
+    assert call(args(Q=0)) == SHAPE
+    assert call(args(tb=0x5000, mp=0)) == SHAPE
+    assert call(args(tb=0x5000, mp=4, ps=0)) == SHAPE
+    assert call(args(tb=0x5000, mp=1 << 20, ps=1 << 12)) == SHAPE
+    assert call(args(R=0, lg=None)) == OK
+    assert call(args(lg=None)) == NULL
+    assert call(args(vo=None)) == NULL
+    assert call(args(lg=0x1008)) == ALIGN
+    assert call(args(ro=0x3002)) == ALIGN

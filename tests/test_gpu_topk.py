@@ -1,0 +1,103 @@
+"""GPU parity of the top-k producer (C ABI mla_topk_rows) against the oracle's select and remap,
+bit-exact (index work), and end to end: logits -> top-k rows -> mla_decode_sparse against the
+oracle's decode over the oracle's lists."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_mla_decode_fp8_amd as mla
+import workloads as wl
+from gpu_util import assert_parity, run_oracle, say, upload
+from oracle import topk as otopk
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _logits(R, N, seed, tie_levels=None, nan_frac=0.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, N)).astype(np.float32)
+    if tie_levels:
+        x = np.round(x * tie_levels) / tie_levels
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    if nan_frac:
+        bits[rng.random((R, N)) < nan_frac] = 0x7FC0
+    return bits
+
+
+def _run(bits, ends, k, **kw):
+    lg = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    re = torch.from_numpy(np.asarray(ends, np.int32)).to(DEV)
+    rows, valid = mla.topk_rows(lg, re, k, **kw)
+    torch.cuda.synchronize()
+    return rows.cpu().numpy(), valid.cpu().numpy()
+
+
+CASES = [
+    # R, N, K, ends, ties, nan
+    (3, 8, 1, [8, 3, 0], None, 0.0),
+    (4, 64, 7, [64, 7, 6, 100], 4, 0.1),
+    (5, 4096, 64, [4096, 4095, 64, 63, 1], None, 0.0),
+    (3, 4104, 100, [4104, 4097, 4100], 2, 0.05),
+    (4, 32768, 2048, [32768, 32764, 2048, 20000], None, 0.01),
+    (2, 32768, 2048, [32768, 32768], 1, 0.0),          # massive ties: values in {-3..3}
+    (2, 512, 1000, [512, 300], None, 0.0),             # K > N
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_topk_select_is_bit_exact(case):
+    R, N, K, ends, ties, nan = CASES[case]
+    say("topk", R, N, K, ends)
+    bits = _logits(R, N, seed=40 + case, tie_levels=ties, nan_frac=nan)
+    # poison: +inf past each row's end must never be chosen
+    for r, e in enumerate(ends):
+        if e < N:
+            bits[r, max(e, 0):] = 0x7F80
+    rows, valid = _run(bits, ends, K)
+    ref, cnt = otopk.select(bits, np.asarray(ends), K)
+    assert np.array_equal(valid, cnt)
+    assert np.array_equal(rows, ref)
+
+
+def test_topk_remap_through_a_page_table_is_bit_exact():
+    B, Q, N, K, page = 3, 2, 2048, 128, 64
+    rng = np.random.default_rng(5)
+    pages = N // page
+    table = rng.permutation(B * pages).astype(np.int32).reshape(B, pages)
+    table[2, -3:] = 2 ** 31 - 1
+    num_rows = B * pages * page
+    bits = _logits(B * Q, N, seed=77, tie_levels=8)
+    ends = rng.integers(0, N + 1, size=B * Q).astype(np.int32)
+    rows, valid = _run(bits, ends, K, block_table=torch.from_numpy(table).to(DEV), page_size=page,
+                       q_per_request=Q, num_rows=num_rows)
+    cols, cnt = otopk.select(bits, ends, K)
+    assert np.array_equal(valid, cnt)
+    assert np.array_equal(rows, otopk.remap(cols, table, page, Q, num_rows))
+
+
+def test_topk_then_sparse_decode_matches_the_oracle():
+    """Indexer logits -> top-k cache rows -> sparse decode, against the oracle's decode over the
+    oracle's lists (the lists themselves are bit-exact)."""
+    B, Q, H, ctx, K, page = 2, 3, 32, 3000, 512, 64
+    x = wl.dense_case(B, Q, H, [ctx, 2100], page, seed=123)
+    rng = np.random.default_rng(8)
+    N = ((ctx + 7) // 8) * 8
+    bits = _logits(B * Q, N, seed=99)
+    seq = x.seq_lens.astype(np.int64)
+    ends = np.array([seq[r // Q] - Q + (r % Q) + 1 for r in range(B * Q)], np.int32)   # causal
+    dev = upload(x)
+    rows, valid = mla.topk_rows(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV),
+                                torch.from_numpy(ends).to(DEV), K, block_table=dev["table"],
+                                page_size=page, q_per_request=Q, num_rows=x.kv.shape[0])
+    o, lse = mla.sparse(dev["q"], dev["kv"], rows.view(B, Q, K), valid.view(B, Q), x.scale,
+                        x.k_scale, plan=(1, 2))
+    torch.cuda.synchronize()
+    cols, cnt = otopk.select(bits, ends, K)
+    ref_rows = otopk.remap(cols, x.block_table, page, Q, x.kv.shape[0])
+    assert np.array_equal(rows.cpu().numpy(), ref_rows) and np.array_equal(valid.cpu().numpy(), cnt)
+    o_ref, lse_ref, amb = oracle.sparse(x.q_bits, x.kv, x.k_scale, ref_rows.reshape(B, Q, K),
+                                        cnt.reshape(B, Q), x.scale, mode=oracle.METHOD, chunk=128,
+                                        allowance=True)
+    assert_parity(o, lse, o_ref, lse_ref, amb, what="top-k -> sparse decode")

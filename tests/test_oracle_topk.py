@@ -28,16 +28,17 @@ def test_order_key_follows_the_values_for_every_bf16_pattern():
 
 
 def _brute(bits_row, row_end, k):
-    """Plain Python: candidates are the non-NaN columns below the row end; the k best by (value
-    descending, then -0 below +0, column ascending); output: those strictly above the k-th one's
-    (value, sign) in column order, then those tied with it in column order."""
+    """Plain Python: candidates are the non-NaN columns below the row end; fewer than k: all, in
+    column order; else the k best by (value descending, then -0 below +0, column ascending),
+    output as those strictly above the k-th one's (value, sign) in column order, then those tied
+    with it in column order."""
     n = max(0, min(row_end, len(bits_row)))
     def rank(c):
         val = VALS[bits_row[c]]
         neg_zero = val == 0 and bits_row[c] == 0x8000
         return (val, 0 if neg_zero else 1)
     cand = [c for c in range(n) if not np.isnan(VALS[bits_row[c]])]
-    if len(cand) <= k:
+    if len(cand) < k:
         return cand
     best = sorted(cand, key=lambda c: (tuple(-x for x in rank(c)), c))[:k]
     thr = rank(best[-1])
@@ -73,6 +74,13 @@ def test_select_on_random_values_and_the_padded_lists():
         assert np.all(cols[r, cnt[r]:] == -1)
     assert cnt[2] == 40 and list(cols[2, :40]) == list(range(40))   # fewer candidates than K
     assert cnt[3] == 0
+
+
+def test_exactly_k_candidates_come_out_in_threshold_order():
+    # 1.0, 2.0, 1.0, 3.0 with k = 4: the threshold is 1.0; above it columns 1, 3, then 0, 2
+    bits = np.array([0x3F80, 0x4000, 0x3F80, 0x4040], np.uint16)
+    assert list(topk.select_row(bits, 4, 4)) == [1, 3, 0, 2]
+    assert list(topk.select_row(bits, 4, 5)) == [0, 1, 2, 3]   # fewer than k: column order
 
 
 def test_remap_follows_the_page_table():
