@@ -11,6 +11,7 @@ What it computes, and the passages of the vLLM API pages it follows, is stated i
 * ``METHOD`` -- as ``ONLINE`` with P rounded to E4M3 at the 448 anchor of the running maximum.
 
 With ``q_e4m3=True`` the logits use the E4M3 query (``q_e4m3_row``) in place of the bf16 one.
+With ``p_split=True`` (METHOD mode) each P meets V as E4M3 hi + lo (``p_used``) instead of E4M3.
 
 With ``allowance=True`` the front ends also return, per output element, how far o may move when a
 P that an FP32 implementation can only place to within 2^-13 (relative) of an E4M3 rounding
@@ -26,6 +27,7 @@ import numpy as np
 
 EXACT, ONLINE, METHOD = 0, 1, 2
 _QE4M3 = 16   # flag added to a mode: the E4M3 query
+_PSPLIT = 32  # flag added to METHOD: P as E4M3 hi + lo
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mla_oracle.c")
@@ -59,6 +61,8 @@ def _load():
         lib.mo_bf16_decode.restype = ctypes.c_double
         lib.mo_q_e4m3_bits.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         lib.mo_q_e4m3_bits.restype = None
+        lib.mo_p_used.argtypes = [ctypes.c_double, ctypes.c_int]
+        lib.mo_p_used.restype = ctypes.c_double
         lib.mo_q_shift.argtypes = [ctypes.c_void_p]
         lib.mo_q_shift.restype = ctypes.c_int
         lib.mo_combine_f64.argtypes = [P, P, i32, i64, P, P]
@@ -85,6 +89,18 @@ def e4m3_encode(x: float) -> int:
 
 def bf16_decode(bits: int) -> float:
     return _load().mo_bf16_decode(bits)
+
+
+def p_used(p: float, split: bool) -> float:
+    """The P that meets V in METHOD mode for a P of ``p`` (rounded to FP32 first): E4M3(p), or with
+    ``split`` hi + lo, hi = E4M3(p), lo = E4M3(p - hi)."""
+    return _load().mo_p_used(float(p), int(bool(split)))
+
+
+def _flags(mode, q_e4m3, p_split):
+    if p_split and int(mode) != METHOD:
+        raise ValueError("p_split applies to METHOD mode only")
+    return int(mode) | (_QE4M3 if q_e4m3 else 0) | (_PSPLIT if p_split else 0)
 
 
 def q_e4m3_row(q_bits) -> tuple[np.ndarray, int]:
@@ -143,7 +159,8 @@ def _cuts(cuts, groups):
 
 
 def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=METHOD, splits=1,
-          chunk=128, cuts=None, sel=None, threads=None, allowance=False, q_e4m3=False):
+          chunk=128, cuts=None, sel=None, threads=None, allowance=False, q_e4m3=False,
+          p_split=False):
     """Paged dense decode. ``q_bits`` uint16 bf16 bits [B,Q,H,576]; ``kv`` uint8 [num_rows,576];
     ``block_table`` int32 [B,max_pages]; ``seq_lens`` int32 [B].
 
@@ -165,7 +182,7 @@ def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=
     amb = np.zeros_like(o) if allowance else None
     rc = _load().mo_dense(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], int(page_size),
                           float(k_scale), _ptr(table), table.shape[1], _ptr(seq), float(scale),
-                          int(mode) | (_QE4M3 if q_e4m3 else 0), int(splits), int(chunk), _ptr(cp),
+                          _flags(mode, q_e4m3, p_split), int(splits), int(chunk), _ptr(cp),
                           _ptr(cs), _ptr(sel),
                           0 if sel is None else len(sel), _threads(threads), _ptr(o), _ptr(lse),
                           _ptr(amb))
@@ -175,7 +192,7 @@ def dense(q_bits, kv, page_size, k_scale, block_table, seq_lens, scale, *, mode=
 
 
 def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, chunk=128, cuts=None,
-           sel=None, threads=None, allowance=False, q_e4m3=False):
+           sel=None, threads=None, allowance=False, q_e4m3=False, p_split=False):
     """Top-k sparse decode. ``rows`` int32 [B,Q,K] flat cache rows; ``valid`` int32 [B,Q]. The
     split plan as for ``dense``, with ``cuts`` given per (b, i) row list, in order b*Q+i."""
     q_bits = _as(q_bits, np.uint16)
@@ -191,7 +208,7 @@ def sparse(q_bits, kv, k_scale, rows, valid, scale, *, mode=METHOD, splits=1, ch
     amb = np.zeros_like(o) if allowance else None
     rc = _load().mo_sparse(_ptr(q_bits), B, Q, H, _ptr(kv), kv.shape[0], float(k_scale),
                            _ptr(rows), rows.shape[2], _ptr(valid), float(scale),
-                           int(mode) | (_QE4M3 if q_e4m3 else 0),
+                           _flags(mode, q_e4m3, p_split),
                            int(splits), int(chunk), _ptr(cp), _ptr(cs), _ptr(sel),
                            0 if sel is None else len(sel),
                            _threads(threads), _ptr(o), _ptr(lse), _ptr(amb))

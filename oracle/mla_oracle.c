@@ -26,6 +26,9 @@
  *             - module docstring: position i of a request's qlen query rows sees keys up to
  *               seq_len - qlen + i; a split with no visible key leaves LSE = -inf and o = 0.
  *             - fp8_unpack4: E4M3 to f32 is exact.
+ *             - module docstring and fp8_split4: P (scaled by a power of two) goes to the PV
+ *               product as two E4M3 values, hi and lo, with P ~ hi + lo; V meets both. With the
+ *               MO_PSPLIT flag the METHOD mode takes this form of P (mo_p_split below).
  *
  * The query: the bf16 row as given (q exact in FP64), or, with the MO_QE4M3 flag added to a mode,
  * its E4M3 form (see mo_q_e4m3 below).
@@ -35,8 +38,9 @@
  *                 x_j = scale * q . K_j, K_j = k_scale * dec(K bytes), V_j = k_scale * dec(V bytes).
  *   MO_ONLINE     the pages' split / chunked online softmax and merge, P not rounded (equals MO_EXACT
  *                 up to FP64 rounding for every split plan: the split-merge identity).
- *   MO_METHOD     MO_ONLINE with each P rounded to E4M3 before it multiplies V. The rounding decision
- *                 is taken on P rounded to FP32, the precision the pages compute P in.
+ *   MO_METHOD     MO_ONLINE with each P rounded to E4M3 before it multiplies V (with MO_PSPLIT: split
+ *                 into E4M3 hi + lo, see mo_p_used). The rounding decision is taken on P rounded to
+ *                 FP32, the precision the pages compute P in.
  *                 Optionally also a per-element allowance: an implementation that forms the logits
  *                 in FP32 gets P only to a relative accuracy of about MO_P_REL_ERR, and where a P
  *                 lies that close to an E4M3 rounding midpoint either rounding is a correct result.
@@ -64,6 +68,7 @@
 
 enum { MO_EXACT = 0, MO_ONLINE = 1, MO_METHOD = 2 };
 enum { MO_QE4M3 = 16 }; /* flag added to a mode: the logits use the E4M3 query */
+enum { MO_PSPLIT = 32 }; /* flag added to MO_METHOD: P enters PV as E4M3 hi + lo */
 
 /* ---- number formats --------------------------------------------------------------------------- */
 
@@ -167,17 +172,34 @@ void mo_q_e4m3_bits(const uint16_t* q, double* qe)
 
 /* ---- one query row ---------------------------------------------------------------------------- */
 
+/* The P that meets V in METHOD mode, from P rounded to FP32 (the pages compute P in FP32):
+ *   plain: E4M3(P);
+ *   split: hi + lo with hi = E4M3(P), lo = E4M3(P - hi) (P - hi is exact: both are FP32 values
+ *          within a factor of two of each other, or hi = 0).
+ * Either way a monotone non-decreasing function of P: within one hi value lo follows P, and where
+ * hi steps up by u at a midpoint, lo steps down from +u/2 to -u/2 (both E4M3 values), so the sum
+ * does not move there. */
+double mo_p_used(double p, int split)
+{
+    const double pf = (double)(float)p;
+    const double hi = mo_e4m3_decode(mo_e4m3_encode(pf));
+    if (!split)
+        return hi;
+    return hi + mo_e4m3_decode(mo_e4m3_encode(pf - hi));
+}
+
 /* Relative accuracy of P assumed for an FP32 implementation (2^-13: FP32 dot products of 576 terms
  * and an FP32 exp2 stay well inside it for logits of the sizes seen here). */
 #define MO_P_REL_ERR (1.0 / 8192.0)
 
-/* The largest change of the E4M3 value of P (rounded to FP32) when P moves by up to MO_P_REL_ERR
- * relative: 0 unless a rounding midpoint lies within that distance. */
-static double rounding_ambiguity(double p)
+/* The largest change of the P used (mo_p_used) when P moves by up to MO_P_REL_ERR relative: 0
+ * unless a rounding midpoint lies within that distance. mo_p_used is monotone, so the ends of the
+ * interval bound every point inside it. */
+static double rounding_ambiguity(double p, int split)
 {
-    const double c0 = mo_e4m3_decode(mo_e4m3_encode((double)(float)p));
-    const double lo = mo_e4m3_decode(mo_e4m3_encode((double)(float)(p * (1.0 - MO_P_REL_ERR))));
-    const double hi = mo_e4m3_decode(mo_e4m3_encode((double)(float)(p * (1.0 + MO_P_REL_ERR))));
+    const double c0 = mo_p_used(p, split);
+    const double lo = mo_p_used(p * (1.0 - MO_P_REL_ERR), split);
+    const double hi = mo_p_used(p * (1.0 + MO_P_REL_ERR), split);
     const double a = fabs(lo - c0), b = fabs(hi - c0);
     return a > b ? a : b;
 }
@@ -185,6 +207,7 @@ static double rounding_ambiguity(double p)
 typedef struct {
     int mode;
     int qe4m3;  /* the E4M3 query (MO_QE4M3) */
+    int psplit; /* P as E4M3 hi + lo (MO_PSPLIT) */
     int splits; /* S >= 1 */
     int chunk;  /* keys per chunk >= 1 */
 } mo_plan;
@@ -325,11 +348,11 @@ static void row_eval(const uint16_t* q, const uint8_t* kv, const int64_t* keyrow
                     continue;
                 double pq = p[t];
                 if (plan->mode == MO_METHOD)
-                    pq = mo_e4m3_decode(mo_e4m3_encode((double)(float)p[t]));
+                    pq = mo_p_used(p[t], plan->psplit);
                 const uint8_t* vr = kv + (size_t)keyrow[base + t] * MO_ROW;
                 for (int c = 0; c < MO_LATENT; c++)
                     O[c] += pq * mo_e4m3_decode(vr[c]);
-                const double d = (amb && plan->mode == MO_METHOD) ? rounding_ambiguity(p[t]) : 0.0;
+                const double d = (amb && plan->mode == MO_METHOD) ? rounding_ambiguity(p[t], plan->psplit) : 0.0;
                 if (d > 0.0)
                     for (int c = 0; c < MO_LATENT; c++)
                         A[c] += d * fabs(mo_e4m3_decode(vr[c]));
@@ -500,7 +523,8 @@ static int run_job(mo_job* base)
  * seq_lens [B]. sel: optional list of flat rows (b*Q+i)*H+h (n_sel of them); NULL means every row.
  * cut_ptr / cut_start: optional explicit split starts per key group (dense: group b; sparse: group
  * b*Q+i), which replace the uniform split rule when given.
- * mode: MO_EXACT, MO_ONLINE or MO_METHOD, plus MO_QE4M3 for the E4M3 query.
+ * mode: MO_EXACT, MO_ONLINE or MO_METHOD, plus MO_QE4M3 for the E4M3 query and (METHOD only)
+ * MO_PSPLIT for P as E4M3 hi + lo.
  * o [items,512] and lse [items] in FP64; amb (optional, METHOD mode) [items,512] the rounding
  * allowance described at the top.
  */
@@ -526,8 +550,9 @@ int mo_dense(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t 
     jb.seq_lens = seq_lens;
     jb.scale = scale;
     jb.k_scale = k_scale;
-    jb.plan.mode = mode & ~MO_QE4M3;
+    jb.plan.mode = mode & ~(MO_QE4M3 | MO_PSPLIT);
     jb.plan.qe4m3 = (mode & MO_QE4M3) != 0;
+    jb.plan.psplit = (mode & MO_PSPLIT) != 0;
     jb.plan.splits = splits;
     jb.plan.chunk = chunk;
     jb.cut_ptr = cut_ptr;
@@ -562,8 +587,9 @@ int mo_sparse(const uint16_t* q, int B, int Q, int H, const uint8_t* kv, int64_t
     jb.valid = valid;
     jb.scale = scale;
     jb.k_scale = k_scale;
-    jb.plan.mode = mode & ~MO_QE4M3;
+    jb.plan.mode = mode & ~(MO_QE4M3 | MO_PSPLIT);
     jb.plan.qe4m3 = (mode & MO_QE4M3) != 0;
+    jb.plan.psplit = (mode & MO_PSPLIT) != 0;
     jb.plan.splits = splits;
     jb.plan.chunk = chunk;
     jb.cut_ptr = cut_ptr;
