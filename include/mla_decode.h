@@ -138,7 +138,8 @@ mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t*
                                size_t workspace_bytes, void* stream);
 
 /*
- * Query precision of the QK product (the argument q_precision of the _q entry points).
+ * Precision flags of the _q entry points (the argument precision: one query flag plus one P flag).
+ * Query precision of the QK product:
  *   MLA_Q_SPLIT  the AMD page's exact query split (mono.attention.mla_attn, module docstring): per
  *                query row the power of two 2^k, k the largest integer with max |q| 2^k <= 448 (at
  *                most 126; 0 for an all-zero row), and q 2^k = hi + lo with hi = E4M3(q 2^k),
@@ -148,22 +149,30 @@ mla_status_t mla_decode_sparse(const void* q, const mla_kv_t* kv, const int32_t*
  *                the logits use E4M3(q 2^k) 2^-k (round to nearest even, same k) in place of q.
  *                Half the QK MFMAs of MLA_Q_SPLIT; |q - query used| <= 2^-4 |q| per value where
  *                |q 2^k| >= 2^-6.
+ * Precision of P = 448 exp2(x - m) in the PV product (the row sums always take P unrounded, FP32):
+ *   MLA_P_E4M3   E4M3(P), round to nearest even (the sparse page's module docstring).
+ *   MLA_P_SPLIT  E4M3 hi + lo with hi = E4M3(P), lo = E4M3(P - hi) (the AMD page's module docstring
+ *                and fp8_split4): V meets both, two FP8 MFMAs per PV step; |P - (hi + lo)| <=
+ *                max(2^-8 P, 2^-10) against 2^-4 P for MLA_P_E4M3. The P lo tile takes LDS that
+ *                four tiles per workgroup leave no room for: a plan with tiles = 4 returns
+ *                MLA_ERR_UNSUPPORTED, and with plan = NULL the planner's choice runs with tiles =
+ *                min(tiles, 2) (size the workspace for that plan).
  */
-enum { MLA_Q_SPLIT = 0, MLA_Q_E4M3 = 1 };
+enum { MLA_Q_SPLIT = 0, MLA_Q_E4M3 = 1, MLA_P_E4M3 = 0, MLA_P_SPLIT = 2 };
 
 /*
- * mla_decode_dense and mla_decode_sparse with the query precision as an argument (they are these
- * with MLA_Q_SPLIT). A q_precision other than MLA_Q_SPLIT or MLA_Q_E4M3 returns
- * MLA_ERR_UNSUPPORTED before anything else is checked. Other arguments, layouts and errors as for
- * the plain entry points.
+ * mla_decode_dense and mla_decode_sparse with the precision as an argument (they are these with
+ * MLA_Q_SPLIT | MLA_P_E4M3). A precision with bits other than MLA_Q_E4M3 and MLA_P_SPLIT, or
+ * MLA_P_SPLIT with a plan of four tiles, returns MLA_ERR_UNSUPPORTED before anything else is
+ * checked. Other arguments, layouts and errors as for the plain entry points.
  */
 mla_status_t mla_decode_dense_q(const void* q, const mla_kv_t* kv, const int32_t* block_table,
                                 int max_pages, const int32_t* seq_lens, float scale, int B, int Q,
-                                int H, const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                int H, const mla_plan_t* plan, int precision, void* o, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
 mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_t* rows, int K,
                                  const int32_t* valid, float scale, int B, int Q, int H,
-                                 const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                 const mla_plan_t* plan, int precision, void* o, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -171,14 +171,31 @@ def _check_tensor(name, t, dtype, device):
         raise ValueError(f"{name}: expected a contiguous {dtype} tensor on {device}")
 
 
-# query precisions of the QK product (C ABI MLA_Q_SPLIT, MLA_Q_E4M3)
+# query precisions of the QK product (C ABI MLA_Q_SPLIT, MLA_Q_E4M3) and P precisions of the PV
+# product (MLA_P_E4M3, MLA_P_SPLIT); the entry points take their sum
 Q_PRECISIONS = {"split": 0, "e4m3": 1}
+P_PRECISIONS = {"e4m3": 0, "split": 2}
+
+
+def _precision(q_precision: str, p_precision: str) -> int:
+    if q_precision not in Q_PRECISIONS:
+        raise ValueError(f"q_precision must be one of {sorted(Q_PRECISIONS)}, not {q_precision!r}")
+    if p_precision not in P_PRECISIONS:
+        raise ValueError(f"p_precision must be one of {sorted(P_PRECISIONS)}, not {p_precision!r}")
+    return Q_PRECISIONS[q_precision] | P_PRECISIONS[p_precision]
 
 
 def _q_precision(name: str) -> int:
-    if name not in Q_PRECISIONS:
-        raise ValueError(f"q_precision must be one of {sorted(Q_PRECISIONS)}, not {name!r}")
-    return Q_PRECISIONS[name]
+    return _precision(name, "e4m3")
+
+
+def cap_plan(plan, p_precision: str = "e4m3") -> Plan:
+    """The plan a call runs: with P as E4M3 hi + lo, at most two tiles per workgroup (the P lo
+    tile does not fit in LDS beside four)."""
+    pl = _as_plan(plan)
+    if P_PRECISIONS.get(p_precision) == P_PRECISIONS["split"] and pl.tiles == 4:
+        pl = pl._replace(tiles=2)
+    return pl
 
 
 def _plan_arg(plan):
@@ -189,12 +206,13 @@ def _plan_arg(plan):
 
 def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
           scale: float, k_scale: float, page_size: int, *, plan=None, o=None, lse=None,
-          workspace: torch.Tensor | None = None, q_precision: str = "split"):
-    """Paged dense decode (C ABI mla_decode_dense, or mla_decode_dense_q for q_precision "e4m3").
+          workspace: torch.Tensor | None = None, q_precision: str = "split",
+          p_precision: str = "e4m3"):
+    """Paged dense decode (C ABI mla_decode_dense_q; mla_decode_dense is its default precision).
     q bf16 [B,Q,H,576]; kv uint8 [rows,576] (or [pages,page_size,576]); block_table int32
     [B,max_pages]; seq_lens int32 [B]. Returns (o bf16 [B,Q,H,512], lse f32 [B,Q,H]) on the
-    current stream."""
-    qp = _q_precision(q_precision)
+    current stream. With p_precision "split" a plan of four tiles runs as two (cap_plan)."""
+    qp = _precision(q_precision, p_precision)
     dev = q.device
     _check_tensor("q", q, torch.bfloat16, dev)
     _check_tensor("kv", kv, torch.uint8, dev)
@@ -204,7 +222,8 @@ def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens
     assert D == 576
     o, lse = _outputs(q, o, lse)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    pl = _as_plan(plan) if plan is not None else plan_dense(B, Q, H, block_table.shape[1], page_size)
+    pl = cap_plan(plan if plan is not None else plan_dense(B, Q, H, block_table.shape[1], page_size),
+                  p_precision)
     if workspace is None:
         workspace = _workspace(dev, stream, True, B, Q, H, pl)
     kvs = _KV(kv.data_ptr(), kv.numel() // 576, int(page_size), float(k_scale))
@@ -217,10 +236,11 @@ def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens
 
 def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.Tensor,
            scale: float, k_scale: float, *, plan=None, o=None, lse=None,
-           workspace: torch.Tensor | None = None, q_precision: str = "split"):
-    """Top-k sparse decode (C ABI mla_decode_sparse, or mla_decode_sparse_q for q_precision
-    "e4m3"). rows int32 [B,Q,K] flat cache rows; valid int32 [B,Q]."""
-    qp = _q_precision(q_precision)
+           workspace: torch.Tensor | None = None, q_precision: str = "split",
+           p_precision: str = "e4m3"):
+    """Top-k sparse decode (C ABI mla_decode_sparse_q; mla_decode_sparse is its default
+    precision). rows int32 [B,Q,K] flat cache rows; valid int32 [B,Q]. Precisions as for dense."""
+    qp = _precision(q_precision, p_precision)
     dev = q.device
     _check_tensor("q", q, torch.bfloat16, dev)
     _check_tensor("kv", kv, torch.uint8, dev)
@@ -231,7 +251,7 @@ def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.T
     K = rows.shape[2]
     o, lse = _outputs(q, o, lse)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    pl = _as_plan(plan) if plan is not None else plan_sparse(B, Q, H, K)
+    pl = cap_plan(plan if plan is not None else plan_sparse(B, Q, H, K), p_precision)
     if workspace is None:
         workspace = _workspace(dev, stream, False, B, Q, H, pl)
     kvs = _KV(kv.data_ptr(), kv.numel() // 576, 1, float(k_scale))

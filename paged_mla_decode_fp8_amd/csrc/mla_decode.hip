@@ -106,7 +106,7 @@ struct Params {
 // since 0 * NaN would poison the PV sum).
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[ROW];
 
-template <int T>
+template <int T, bool PS = false>
 struct Smem {
     static constexpr int OFF_KV = 0;
     static constexpr int OFF_P = 2 * SLOT;                     // E4M3 P [T][16][PPITCH]
@@ -118,9 +118,14 @@ struct Smem {
     static constexpr int OFF_IDX = OFF_KMASK + 4 * 16;         // int32 [2][BLK] raw key indices
     static constexpr int OFF_PTAB = OFF_IDX + 2 * BLK * 4;     // uint64 [4 waves][32] key pointers
     static constexpr int OFF_MISC = OFF_PTAB + 4 * 32 * 8;     // int [4]
-    static constexpr int BYTES = OFF_MISC + 16;
+    // E4M3 P lo [T][16][PPITCH] when P goes to PV as hi + lo (after everything else, so that the
+    // other offsets do not depend on it)
+    static constexpr int OFF_PLO = (OFF_MISC + 16 + 15) / 16 * 16;
+    static constexpr int BYTES = PS ? OFF_PLO + T * PTILE : OFF_MISC + 16;
 };
 static_assert(Smem<4>::BYTES <= 163840, "LDS budget");
+static_assert(Smem<2, true>::BYTES <= 163840, "LDS budget (P hi + lo, at most two tiles)");
+static_assert(Smem<4, true>::BYTES > 163840, "four tiles with P hi + lo would fit: allow them");
 
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -728,7 +733,7 @@ __device__ inline void issue_subtile(uint8_t* smem, const uint8_t* const (&src)[
 // pair exchange their block maxima through LDS (all then hold the same running maximum) and keep
 // a row sum per 32-key part (subtiles 2 p, 2 p + 1), added in part order at the end, so results
 // do not depend on T. QE: the E4M3 query (the hi operands alone; no lo MFMAs).
-template <int T, bool DENSE, bool QE>
+template <int T, bool DENSE, bool QE, bool PS>
 __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Work& w, int qw,
                                         int lane)
 {
@@ -900,6 +905,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         }
         lds_sync();   // B2: the pair's maxima are published; the PV waves hold P of block i - 1
         uint32_t pk[TW][KS];   // E4M3 P of this lane's 4 keys of each subtile
+        uint32_t pkl[TW][KS];  // with PS: E4M3 lo = E4M3(P - hi) of the same keys
         float alpha[TW];
         if (work) {
 #pragma unroll
@@ -926,6 +932,13 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                         pr[jj] = ANCHOR * __builtin_amdgcn_exp2f(fmaf(acc[j][u][jj], row_scale[j], -m_use));
                     int wp = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
                     pk[j][u] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], wp, true);
+                    if (PS) {
+                        // P - hi is exact in FP32 (hi is within a factor of two of P, or 0)
+                        const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk[j][u], false);
+                        const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk[j][u], true);
+                        int wl = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] - h01.x, pr[1] - h01.y, 0, false);
+                        pkl[j][u] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pr[2] - h23.x, pr[3] - h23.y, wl, true);
+                    }
                     bsum[u >> 1] = bsum[u >> 1] + (((pr[0] + pr[1]) + pr[2]) + pr[3]);
                 }
 #pragma unroll
@@ -942,6 +955,12 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                 for (int u = 0; u < KS; u++)
                     *reinterpret_cast<uint32_t*>(smem + L::OFF_P + (qt0 + j) * PTILE + (lo & 15) * PPITCH +
                                                  16 * (sub0 + u) + 4 * (lo >> 4)) = pk[j][u];
+                if (PS) {
+#pragma unroll
+                    for (int u = 0; u < KS; u++)
+                        *reinterpret_cast<uint32_t*>(smem + L::OFF_PLO + (qt0 + j) * PTILE + (lo & 15) * PPITCH +
+                                                     16 * (sub0 + u) + 4 * (lo >> 4)) = pkl[j][u];
+                }
                 if (grp == 0 && kq == 0)
                     xalpha[(qt0 + j) * 16 + (lo & 15)] = alpha[j];
             }
@@ -992,7 +1011,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
 }
 
 // ---- PV waves: the gather, and O^T += V^T P^T for 128 latent columns of every tile ----
-template <int T, bool DENSE, bool QE>
+template <int T, bool DENSE, bool QE, bool PS>
 __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Work& w, int pw,
                                         int lane, const FirstIdx& fi, v4f (&O)[T][8])
 {
@@ -1137,6 +1156,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         const int32_t idx2 = idx_lds[(i & 1) * BLK + 32 * pw + (lane_now() & 31)];
         float alpha[T];
         v8i pb[T];
+        v8i pl[T];   // with PS: P lo
         if (T == 4) {
 #pragma unroll
             for (int t = 0; t < T; t++) pb[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -1148,6 +1168,10 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                 alpha[t] = xalpha[t * 16 + (lo & 15)];
                 const int off = L::OFF_P + t * PTILE + (lo & 15) * PPITCH + 32 * (lo >> 4);
                 pb[t] = cat(lds_read16(smem, off), lds_read16(smem, off + 16));
+                if (PS) {
+                    const int offl = off - L::OFF_P + L::OFF_PLO;
+                    pl[t] = cat(lds_read16(smem, offl), lds_read16(smem, offl + 16));
+                }
             }
         }
         if (i + 1 < w.nblk)
@@ -1170,7 +1194,11 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
 #pragma unroll
             for (int c = 0; c < 8; c++) {
 #pragma unroll
-                for (int t = 0; t < T; t++) O[t][c] = mfma(vt[c], pb[t], O[t][c]);
+                for (int t = 0; t < T; t++) {
+                    O[t][c] = mfma(vt[c], pb[t], O[t][c]);
+                    if (PS)
+                        O[t][c] = mfma(vt[c], pl[t], O[t][c]);
+                }
                 vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
             }
         } else {
@@ -1180,7 +1208,11 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
 #pragma unroll
                 for (int c = 0; c < 8; c++)
 #pragma unroll
-                    for (int t = 0; t < T; t++) O[t][c] = mfma(vt[c], pb[t], O[t][c]);
+                    for (int t = 0; t < T; t++) {
+                        O[t][c] = mfma(vt[c], pb[t], O[t][c]);
+                        if (PS)
+                            O[t][c] = mfma(vt[c], pl[t], O[t][c]);
+                    }
             }
             if (i < w.nblk) {
 #pragma unroll
@@ -1391,11 +1423,10 @@ __device__ inline const Params& fresh_params()
     return *(const Params*)k;   // loads through it stay scalar (address-space inference)
 }
 
-template <int T, bool DENSE, bool QE>
+template <int T, bool DENSE, bool QE, bool PS>
 __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
 {
-    using L = Smem<T>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<T, PS>::BYTES];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -1430,7 +1461,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             Work w;
             item(pi, g, pre, w);
             pre += ITEM_BLOCKS + nblocks(w.n_grp);
-            qk_role<T, DENSE, QE>(pi, smem, w, wave, li);
+            qk_role<T, DENSE, QE, PS>(pi, smem, w, wave, li);
             finish_item<T>(pi, smem, w, tid);
             __syncthreads();   // the next item reuses every LDS area
         }
@@ -1449,7 +1480,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
                 for (int c = 0; c < 8; c++) O[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
             int li = lane;
             asm volatile("" : "+v"(li));
-            pv_role<T, DENSE, QE>(pi, smem, w, wave - 4, li, fi, O);
+            pv_role<T, DENSE, QE, PS>(pi, smem, w, wave - 4, li, fi, O);
             finish_item<T>(pi, smem, w, tid);
             __syncthreads();
         }
@@ -1551,32 +1582,38 @@ void set_page_division(Params& p, int d)
     p.pg_s2 = l - 1 > 0 ? l - 1 : 0;
 }
 
-template <int T, bool DENSE, bool QE>
+template <int T, bool DENSE, bool QE, bool PS>
 hipError_t launch_t(const Params& p, hipStream_t stream)
 {
     const int64_t gs_pad = ((int64_t)p.units + 7) / 8 * 8;
     const int64_t grid = gs_pad * p.tilesets;
-    hipLaunchKernelGGL((mla_decode_kernel<T, DENSE, QE>), dim3((unsigned)grid), dim3(THREADS), 0, stream,
-                       p);
+    hipLaunchKernelGGL((mla_decode_kernel<T, DENSE, QE, PS>), dim3((unsigned)grid), dim3(THREADS), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
 template <bool DENSE, bool QE>
-hipError_t launch_q(int T, const Params& p, hipStream_t stream)
+hipError_t launch_q(int T, bool ps, const Params& p, hipStream_t stream)
 {
+    if (ps)   // at most two tiles (the entry points cap the plan)
+        return T == 1 ? launch_t<1, DENSE, QE, true>(p, stream) : launch_t<2, DENSE, QE, true>(p, stream);
     switch (T) {
-    case 1: return launch_t<1, DENSE, QE>(p, stream);
-    case 2: return launch_t<2, DENSE, QE>(p, stream);
-    default: return launch_t<4, DENSE, QE>(p, stream);
+    case 1: return launch_t<1, DENSE, QE, false>(p, stream);
+    case 2: return launch_t<2, DENSE, QE, false>(p, stream);
+    default: return launch_t<4, DENSE, QE, false>(p, stream);
     }
 }
 
 template <bool DENSE>
-hipError_t launch(int T, int q_precision, const Params& p, hipStream_t stream)
+hipError_t launch(int T, int precision, const Params& p, hipStream_t stream)
 {
-    return q_precision == MLA_Q_E4M3 ? launch_q<DENSE, true>(T, p, stream)
-                                     : launch_q<DENSE, false>(T, p, stream);
+    const bool ps = (precision & MLA_P_SPLIT) != 0;
+    return (precision & MLA_Q_E4M3) ? launch_q<DENSE, true>(T, ps, p, stream)
+                                    : launch_q<DENSE, false>(T, ps, p, stream);
 }
+
+// The precision flags the entry points take.
+bool precision_ok(int precision) { return (precision & ~(MLA_Q_E4M3 | MLA_P_SPLIT)) == 0; }
 
 mla_status_t common_checks(const void* q, const mla_kv_t* kv, int B, int Q, int H, void* o,
                            float* lse)
@@ -1686,10 +1723,10 @@ mla_status_t mla_plan_sparse(int B, int Q, int H, int K, mla_plan_t* plan)
 
 mla_status_t mla_decode_dense_q(const void* q, const mla_kv_t* kv, const int32_t* block_table,
                                 int max_pages, const int32_t* seq_lens, float scale, int B, int Q,
-                                int H, const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                int H, const mla_plan_t* plan, int precision, void* o, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (q_precision != MLA_Q_SPLIT && q_precision != MLA_Q_E4M3)
+    if (!precision_ok(precision) || ((precision & MLA_P_SPLIT) && plan && plan->tiles == 4))
         return MLA_ERR_UNSUPPORTED;
     mla_status_t st = common_checks(q, kv, B, Q, H, o, lse);
     if (st != MLA_OK || B == 0)
@@ -1702,6 +1739,8 @@ mla_status_t mla_decode_dense_q(const void* q, const mla_kv_t* kv, const int32_t
         return MLA_ERR_ALIGN;
     mla_plan_t chosen;
     mla_plan_dense(B, Q, H, max_pages, kv->page_size, &chosen);
+    if ((precision & MLA_P_SPLIT) && chosen.tiles == 4)
+        chosen.tiles = 2;
     mla_plan_t pl;
     st = finish_plan(plan, chosen, 1, B, Q * H / 16, (int64_t)max_pages * kv->page_size, B, Q, H,
                      workspace, workspace_bytes, &pl);
@@ -1729,17 +1768,17 @@ mla_status_t mla_decode_dense_q(const void* q, const mla_kv_t* kv, const int32_t
     p.o = (uint16_t*)o;
     p.lse = lse;
     fill_workspace(p, 1, B, Q, H, pl, workspace);
-    if (launch<true>(pl.tiles, q_precision, p, (hipStream_t)stream) != hipSuccess)
+    if (launch<true>(pl.tiles, precision, p, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_LAUNCH;
     return MLA_OK;
 }
 
 mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_t* rows, int K,
                                  const int32_t* valid, float scale, int B, int Q, int H,
-                                 const mla_plan_t* plan, int q_precision, void* o, float* lse,
+                                 const mla_plan_t* plan, int precision, void* o, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (q_precision != MLA_Q_SPLIT && q_precision != MLA_Q_E4M3)
+    if (!precision_ok(precision) || ((precision & MLA_P_SPLIT) && plan && plan->tiles == 4))
         return MLA_ERR_UNSUPPORTED;
     mla_status_t st = common_checks(q, kv, B, Q, H, o, lse);
     if (st != MLA_OK || B == 0)
@@ -1752,6 +1791,8 @@ mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_
         return MLA_ERR_ALIGN;
     mla_plan_t chosen;
     mla_plan_sparse(B, Q, H, K, &chosen);
+    if ((precision & MLA_P_SPLIT) && chosen.tiles == 4)
+        chosen.tiles = 2;
     mla_plan_t pl;
     st = finish_plan(plan, chosen, 0, B * Q, H / 16, K, B, Q, H, workspace, workspace_bytes, &pl);
     if (st != MLA_OK)
@@ -1778,7 +1819,7 @@ mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_
     p.o = (uint16_t*)o;
     p.lse = lse;
     fill_workspace(p, 0, B, Q, H, pl, workspace);
-    if (launch<false>(pl.tiles, q_precision, p, (hipStream_t)stream) != hipSuccess)
+    if (launch<false>(pl.tiles, precision, p, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_LAUNCH;
     return MLA_OK;
 }

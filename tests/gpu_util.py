@@ -34,13 +34,13 @@ def upload(x, device="cuda:0"):
     return d
 
 
-def run_gpu(x, dev, plan, q_precision="split"):
+def run_gpu(x, dev, plan, q_precision="split", p_precision="e4m3"):
     if x.kind == "dense":
         o, lse = mla.dense(dev["q"], dev["kv"], dev["table"], dev["seq"], x.scale, x.k_scale,
-                           x.page_size, plan=plan, q_precision=q_precision)
+                           x.page_size, plan=plan, q_precision=q_precision, p_precision=p_precision)
     else:
         o, lse = mla.sparse(dev["q"], dev["kv"], dev["rows"], dev["valid"], x.scale, x.k_scale,
-                            plan=plan, q_precision=q_precision)
+                            plan=plan, q_precision=q_precision, p_precision=p_precision)
     torch.cuda.synchronize()
     return o, lse
 
@@ -82,15 +82,17 @@ def balanced_cuts(x, pieces: int):
     return out
 
 
-def run_oracle(x, plan, sel=None, mode=oracle.METHOD, q_e4m3=False):
+def run_oracle(x, plan, sel=None, mode=oracle.METHOD, q_e4m3=False, p_split=False):
     """The oracle on the same inputs under the same split plan ((splits, tiles[, mode])): o, LSE
     and the per-element rounding allowance (o may move by that much where a P lies within FP32
     accuracy of an E4M3 rounding midpoint, so either rounding is correct). q_e4m3: the oracle's
-    E4M3 query."""
+    E4M3 query; p_split: P as E4M3 hi + lo."""
     plan = tuple(plan)
     kw = {"splits": plan[0], "allowance": True, "q_e4m3": q_e4m3}
     if len(plan) > 2 and plan[2] == BALANCED:
         kw = {"cuts": balanced_cuts(x, plan[0]), "allowance": True, "q_e4m3": q_e4m3}
+    if p_split:
+        kw["p_split"] = True
     if x.kind == "dense":
         return oracle.dense(x.q_bits, x.kv, x.page_size, x.k_scale, x.block_table, x.seq_lens,
                             x.scale, mode=mode, chunk=CHUNK, sel=sel, **kw)

@@ -93,12 +93,19 @@ def test_bad_arguments_return_status_without_launching():
 def test_query_precision_entry_points_check_the_precision_first():
     lib = mla._load()
     kvs = _kv()
-    for bad in (-1, 2, 7):
+    for bad in (-1, 4, 7, 8):
         assert lib.mla_decode_dense_q(None, ctypes.byref(kvs), None, 0, None, 0.07, 2, 1, 16, None,
                                       bad, None, None, None, 0, None) == UNSUPPORTED
         assert lib.mla_decode_sparse_q(None, ctypes.byref(kvs), None, 0, None, 0.07, 2, 1, 16, None,
                                        bad, None, None, None, 0, None) == UNSUPPORTED
-    for good in (0, 1):
+    # P as hi + lo with a plan of four tiles: refused before anything else is checked
+    four = ctypes.byref(mla._plan_struct((1, 4)))
+    for prec in (2, 3):
+        assert lib.mla_decode_dense_q(None, ctypes.byref(kvs), None, 0, None, 0.07, 2, 1, 64, four,
+                                      prec, None, None, None, 0, None) == UNSUPPORTED
+        assert lib.mla_decode_sparse_q(None, ctypes.byref(kvs), None, 0, None, 0.07, 2, 1, 64, four,
+                                       prec, None, None, None, 0, None) == UNSUPPORTED
+    for good in (0, 1, 2, 3):
         # then the same checks as the plain entry points
         assert lib.mla_decode_dense_q(None, ctypes.byref(kvs), 0x2000, 4, 0x3000, 0.07, 2, 1, 16,
                                       None, good, 0x4000, 0x5000, None, 0, None) == NULL
@@ -108,6 +115,12 @@ def test_query_precision_entry_points_check_the_precision_first():
                                        None, good, 0x4000, 0x5000, None, 0, None) == OK
     with pytest.raises(ValueError):
         mla._q_precision("fp8")
+    with pytest.raises(ValueError):
+        mla._precision("split", "bf16")
+    assert [mla._precision(a, b) for a in ("split", "e4m3") for b in ("e4m3", "split")] == [0, 2, 1, 3]
+    # the binding runs P hi + lo with at most two tiles
+    assert mla.cap_plan((3, 4), "split") == mla.Plan(3, 2) and mla.cap_plan((3, 4)) == mla.Plan(3, 4)
+    assert mla.cap_plan((3, 1, 1), "split") == mla.Plan(3, 1, 1)
 
 
 def test_workspace_sizes_and_plans():

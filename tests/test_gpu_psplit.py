@@ -1,0 +1,106 @@
+"""GPU parity of P as E4M3 hi + lo (C ABI mla_decode_dense_q / mla_decode_sparse_q with
+MLA_P_SPLIT, with either query precision) against the oracle's METHOD mode with the same P form
+under the same split plan, with the default tolerance, plus: determinism and tiles invariance, and
+the point of the variant, a result closer to the textbook softmax than with E4M3 P on the same
+inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import BALANCED, as_f64, assert_parity, bits, run_gpu, run_oracle, say, upload
+
+pytestmark = pytest.mark.gpu
+
+SPLIT = "split"
+
+
+def _parity(x, plan, what, q_precision="split", sel=None):
+    say(what, "(P hi + lo, query", q_precision + ")", x.kind, "B,Q,H =", x.B, x.Q, x.H, "plan", plan)
+    dev = upload(x)
+    o, lse = run_gpu(x, dev, plan, q_precision=q_precision, p_precision=SPLIT)
+    o_ref, lse_ref, amb = run_oracle(x, plan, sel=sel, q_e4m3=q_precision == "e4m3", p_split=True)
+    return assert_parity(o, lse, o_ref, lse_ref, amb, sel=sel, what=what), o, lse
+
+
+@pytest.mark.parametrize("qp", ["split", "e4m3"])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_tiny_and_latency_sparse(splits, qp):
+    _parity(wl.tiny_sparse(), (splits, 1), f"tiny_sparse S={splits}", qp)
+    _parity(wl.latency_sparse(), (splits, 1), f"latency_sparse S={splits}", qp)
+
+
+SPARSE_CASES = [
+    (1, 1, 16, 1, [[1]], 64, (1, 1)),
+    (2, 3, 16, 33, [[0, 1, 15], [16, 17, 33]], 200, (1, 1)),
+    (2, 2, 32, 129, [[127, 128], [129, 31]], 500, (2, 2)),
+    (3, 2, 64, 300, [[300, 257, 0], [1, 2, 255]], 4096, (3, 2)),
+    (2, 1, 128, 1000, [[1000], [999]], 8000, (4, 2)),
+    (2, 2, 64, 1500, [[1500, 700], [1, 1200]], 9000, (9, 2, BALANCED)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPARSE_CASES)))
+def test_sparse_cases(case):
+    B, Q, H, K, valid, rows, plan = SPARSE_CASES[case]
+    x = wl.sparse_case(B, Q, H, K, valid, rows, seed=1700 + case)
+    _parity(x, plan, f"sparse case {case}", "e4m3" if case % 2 else "split")
+
+
+DENSE_CASES = [
+    (1, 1, 16, [1], 64, (1, 1)),
+    (2, 4, 16, [130, 3], 16, (2, 2)),
+    (3, 2, 32, [500, 64, 1], 64, (3, 2)),
+    (2, 3, 64, [0, 700], 32, (2, 2)),
+    (1, 2, 128, [2100], 64, (5, 1)),
+    (3, 4, 32, [2000, 5, 900], 16, (11, 2, BALANCED)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DENSE_CASES)))
+def test_dense_cases(case):
+    B, Q, H, seq, page, plan = DENSE_CASES[case]
+    x = wl.dense_case(B, Q, H, seq, page, seed=1800 + case)
+    _parity(x, plan, f"dense case {case}", "e4m3" if case % 2 else "split")
+
+
+def test_determinism_and_tiles_invariance():
+    x = wl.dense_case(2, 2, 64, [700, 333], 64, seed=1901)
+    say("P hi + lo determinism and tiles", x.kind)
+    dev = upload(x)
+    ref = run_gpu(x, dev, (3, 2), p_precision=SPLIT)
+    for plan in ((3, 2), (3, 1), (3, 4)):      # four tiles run as two
+        o, lse = run_gpu(x, dev, plan, p_precision=SPLIT)
+        assert np.array_equal(bits(o), bits(ref[0]))
+        assert np.array_equal(lse.cpu().numpy(), ref[1].cpu().numpy())
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_closer_to_the_textbook_softmax_than_e4m3_p(seed):
+    """Same inputs, both P precisions, against the oracle's EXACT mode: the mean error of hi + lo
+    is well below that of E4M3 P (whose P error is up to 2^-4 relative against 2^-8)."""
+    x = wl.sparse_case(2, 2, 64, 2000, [[2000, 1500], [700, 1999]], 20000, seed=1950 + seed)
+    say("P hi + lo accuracy", x.kind, "seed", seed)
+    dev = upload(x)
+    o_ex, _ = oracle.sparse(x.q_bits, x.kv, x.k_scale, x.rows, x.valid, x.scale, mode=oracle.EXACT)
+    o_ex = o_ex.reshape(-1, 512)
+    err = {}
+    for pp in ("e4m3", SPLIT):
+        o, _ = run_gpu(x, dev, (2, 2), p_precision=pp)
+        err[pp] = float(np.mean(np.abs(as_f64(o).reshape(-1, 512) - o_ex)))
+    say("mean |o - o_exact|:", err)
+    assert err[SPLIT] < 0.5 * err["e4m3"]
+
+
+@pytest.mark.parametrize("name", ["dense_paged", "topk_sparse", "long_dense"])
+def test_full_size_workloads_sampled(name):
+    w = wl.WORKLOADS[name]
+    x = w.make()
+    rng = np.random.default_rng(15)
+    n_rows = x.B * x.Q * x.H
+    sel = np.unique(np.concatenate([rng.choice(n_rows, 16, replace=False), [0, n_rows - 1]]))
+    plan = tuple(w.plan)
+    if plan[1] == 4:
+        plan = (plan[0], 2) + plan[2:]
+    _parity(x, plan, f"{name} sampled", sel=sel)
