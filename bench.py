@@ -34,6 +34,7 @@ HBM_PEAK = 8.0e12        # B/s, MI355X
 FP8_PEAK = 5.0e15        # dense FP8 MFMA flop/s, MI355X
 FLOP_PER_HEAD_KEY = 2 * 2 * 576 + 2 * 512   # QK with the hi + lo query (two E4M3 passes) + PV
 FLOP_PER_HEAD_KEY_E4M3Q = 2 * 576 + 2 * 512  # QK with the E4M3 query (one pass) + PV
+FLOP_PER_HEAD_KEY_PLO = 2 * 512                # PV's second pass with P as E4M3 hi + lo
 HEADLINE = "dense_paged"
 METRIC = ("µs/call and KV HBM GB/s (fraction of 8 TB/s peak), dense + top-k sparse MLA "
           "decode")
@@ -49,10 +50,11 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def algorithmic(x, q_precision="split"):
+def algorithmic(x, q_precision="split", p_precision="e4m3"):
     """Algorithmic HBM bytes and MFMA flops of one call: every gathered KV row once per key group,
     Q read once, o and lse written once, indices / block-table entries read once. The flops count
-    the QK product once per query pass (two for the split query, one for the E4M3 query)."""
+    the QK product once per query pass (two for the split query, one for the E4M3 query) and the
+    PV product once per P pass (two for P as hi + lo)."""
     rows = x.B * x.Q * x.H
     q_bytes = rows * 576 * 2
     o_bytes = rows * 512 * 2 + rows * 4
@@ -73,12 +75,14 @@ def algorithmic(x, q_precision="split"):
     return {
         "kv_bytes": kv_bytes,
         "bytes": kv_bytes + q_bytes + o_bytes + idx_bytes,
-        "flops": head_keys * (FLOP_PER_HEAD_KEY_E4M3Q if q_precision == "e4m3" else FLOP_PER_HEAD_KEY),
+        "flops": head_keys * ((FLOP_PER_HEAD_KEY_E4M3Q if q_precision == "e4m3" else FLOP_PER_HEAD_KEY)
+                              + (FLOP_PER_HEAD_KEY_PLO if p_precision == "split" else 0)),
         "head_keys": head_keys,
     }
 
 
-def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precision="split", x=None):
+def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precision="split", x=None,
+                   p_precision="e4m3"):
     import torch
 
     import paged_mla_decode_fp8_amd as mla
@@ -87,9 +91,9 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
     w = wl.WORKLOADS[name]
     if x is None:
         x = w.make()
-    alg = algorithmic(x, q_precision)
+    alg = algorithmic(x, q_precision, p_precision)
     dev = torch.device("cuda:0")
-    plan = w.plan
+    plan = mla.cap_plan(w.plan, p_precision)
     kv_host = torch.from_numpy(x.kv)
     copies = max(1, min(8, math.ceil(min_rotation_bytes / max(1, x.kv.nbytes))))
     kvs = [kv_host.to(dev) for _ in range(copies)]
@@ -104,14 +108,14 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
 
         def call(k):
             mla.dense(q, kvs[k % copies], table, seq, x.scale, x.k_scale, x.page_size, plan=plan,
-                      o=o, lse=lse, workspace=ws, q_precision=q_precision)
+                      o=o, lse=lse, workspace=ws, q_precision=q_precision, p_precision=p_precision)
     else:
         rows = torch.from_numpy(x.rows).to(dev)
         valid = torch.from_numpy(x.valid).to(dev)
 
         def call(k):
             mla.sparse(q, kvs[k % copies], rows, valid, x.scale, x.k_scale, plan=plan, o=o,
-                       lse=lse, workspace=ws, q_precision=q_precision)
+                       lse=lse, workspace=ws, q_precision=q_precision, p_precision=p_precision)
 
     for k in range(warmup):
         call(k)
@@ -338,7 +342,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of the headline workload the CPU oracle is timed on")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the E4M3-query precision runs of every workload")
+                    help="skip the E4M3-query and P hi + lo precision runs of every workload")
     ap.add_argument("--no-combine", action="store_true",
                     help="skip the decode-context-parallel combine and top-k producer runs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -369,6 +373,7 @@ def main():
 
     results = {}
     variants = {}
+    p_variants = {}
     head_x = None
     for name in names:
         res, x = bench_workload(name, args.steps, args.warmup)
@@ -381,6 +386,12 @@ def main():
             variants[name] = {k: v[k] for k in ("us_per_call", "kv_GBps", "hbm_frac", "mfma_frac",
                                                 "alg_flops", "mfma_floor_us")}
             print(f"[bench] {name} (E4M3 query): {v['us_per_call']} us/call, {v['kv_GBps']} KV "
+                  f"GB/s, hbm {v['hbm_frac']:.3f}, mfma {v['mfma_frac']:.3f}", file=sys.stderr,
+                  flush=True)
+            v, _ = bench_workload(name, args.steps, args.warmup, p_precision="split", x=x)
+            p_variants[name] = {k: v[k] for k in ("us_per_call", "kv_GBps", "hbm_frac", "mfma_frac",
+                                                  "alg_flops", "mfma_floor_us", "plan")}
+            print(f"[bench] {name} (P hi + lo): {v['us_per_call']} us/call, {v['kv_GBps']} KV "
                   f"GB/s, hbm {v['hbm_frac']:.3f}, mfma {v['mfma_frac']:.3f}", file=sys.stderr,
                   flush=True)
         if name == HEADLINE:
@@ -414,7 +425,7 @@ def main():
         "unit": unit,
         "frac": round(achieved / peak, 4),
         "traffic": read_traffic(HEADLINE),
-        "kernel": "mla_decode_kernel<4, true, false> (dense, split query)",
+        "kernel": "mla_decode_kernel<4, true, false, false> (dense, split query, E4M3 P)",
         "hbm_frac": h["hbm_frac"],
         "mfma_frac": h["mfma_frac"],
     }
@@ -442,6 +453,7 @@ def main():
         "cpu_baseline": cpu,
         "workloads": results,
         "q_e4m3": variants or None,
+        "p_split": p_variants or None,
         "dcp_combine": combine or None,
         "topk_producer": topk_res,
     }
