@@ -15,15 +15,15 @@
 // The order key (a reading: the pages do not print it) is the monotone map of the sign-magnitude
 // pattern to an unsigned integer: positive bits | 0x8000, negative ~bits.
 //
-// One 512-thread workgroup per row. The row is taken in spans of 32768 columns; in a span thread t
-// owns the 64 consecutive columns 64 t .. 64 t + 63 (eight 16-byte loads), whose order keys it
+// One 1024-thread workgroup per row. The row is taken in spans of 32768 columns; in a span thread
+// t owns the 32 consecutive columns 32 t .. 32 t + 31 (four 16-byte loads), whose order keys it
 // forms once and keeps packed two to a register (0 for NaN and past the row end), so a row of at
 // most 32768 columns is read from memory once for all three passes. The threshold comes
 // from two radix histograms in LDS: the key's top 12 bits (4096 bins: sign, exponent and three
 // fraction bits, so the LDS atomics of clustered values spread over many bins), then its low 4
 // bits among the keys in the chosen bin. The ordered output: per thread two 64-bit masks (columns
 // above / equal to the threshold), one workgroup prefix sum per span of their popcounts (wave
-// prefix by lane shuffles, then the eight wave totals through LDS) and the set bits in ascending
+// prefix by lane shuffles, then the 16 wave totals through LDS) and the set bits in ascending
 // order: thread order is column order, so the lists come out in column order without a sort.
 #include <hip/hip_runtime.h>
 
@@ -33,9 +33,9 @@
 
 namespace {
 
-constexpr int TK_THREADS = 512;
+constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_VEC = 8;                         // 16-byte loads (8 columns each) per thread
+constexpr int TK_VEC = 4;                         // 16-byte loads (8 columns each) per thread
 constexpr int TK_OWN = 8 * TK_VEC;                // columns per thread per span
 constexpr int TK_SPAN = TK_THREADS * TK_OWN;      // 32768 columns
 
@@ -44,7 +44,7 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 constexpr int TK_HI_BITS = 12;                    // first radix digit: key bits 15..4
 constexpr int TK_LO_BITS = 16 - TK_HI_BITS;       // second digit: key bits 3..0
 constexpr int TK_BINS = 1 << TK_HI_BITS;
-constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the threshold search (8)
+constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the threshold search (4)
 
 struct TkShared {
     uint32_t hist[TK_BINS + 1];   // the last counter takes the NaN / past-the-end columns (unused)
@@ -88,7 +88,7 @@ __device__ inline int tk_scan(int x, TkShared& sh, int& total)
 
 constexpr int TK_KW = TK_OWN / 2;                 // key registers per thread (two keys each)
 
-// The order keys of this thread's 64 columns of the span starting at s0: kw[i] holds column 2 i in
+// The order keys of this thread's 32 columns of the span starting at s0: kw[i] holds column 2 i in
 // its low half and column 2 i + 1 in its high half (0 past the row end).
 __device__ inline void tk_keys(const uint16_t* row, int n, int s0, uint32_t (&kw)[TK_KW])
 {
