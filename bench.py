@@ -2,15 +2,19 @@
 
 One step = one decode call (mla_decode_dense / mla_decode_sparse through the C ABI) over one batch
 of the workload: Q-stage, KV gather, QK, softmax, PV, split emit and FP32 merge all run inside it.
-The headline line is the dense paged workload (B=64, Q=1, H=128, page 64, seq_len U[1024, 8192]);
-the other four workloads are timed the same way and reported under "workloads".
+The headline line is the long-context dense causal verify workload (B=8, Q=4 causal rows, H=128,
+seq_len 131072, page 64; the largest of the five, MFMA-bound with the split query); the other four
+workloads are timed the same way and reported under "workloads".
 
 Timing is cold with respect to the 256 MB Infinity Cache: the timed calls rotate over several
 copies of the KV cache (together well above 256 MB), all resident in HBM before timing starts.
 HIP events on the stream the kernel runs on bracket the timed calls. The reported time per call is
 measured on a HIP graph that holds one call per KV copy, replayed back to back (the GPU time per
 call, with no host launch work in between); the time of K eager launches from Python is reported
-beside it (us_per_call_eager), and for the large workloads the two agree.
+beside it (us_per_call_eager), and for the large workloads the two agree. Also reported per
+workload: the spread of the time per call over individually timed graph replays (p10 / p50 / p90,
+each replay being one call per KV copy) and the hot time per call (every call on one KV copy, so
+whatever of it fits stays in the caches).
 
 Prints ONE JSON line.
 """
@@ -35,7 +39,7 @@ FP8_PEAK = 5.0e15        # dense FP8 MFMA flop/s, MI355X
 FLOP_PER_HEAD_KEY = 2 * 2 * 576 + 2 * 512   # QK with the hi + lo query (two E4M3 passes) + PV
 FLOP_PER_HEAD_KEY_E4M3Q = 2 * 576 + 2 * 512  # QK with the E4M3 query (one pass) + PV
 FLOP_PER_HEAD_KEY_PLO = 2 * 512                # PV's second pass with P as E4M3 hi + lo
-HEADLINE = "dense_paged"
+HEADLINE = "long_dense"
 METRIC = ("µs/call and KV HBM GB/s (fraction of 8 TB/s peak), dense + top-k sparse MLA "
           "decode")
 KERNEL_SRC = os.path.join(ROOT, "paged_mla_decode_fp8_amd", "csrc", "mla_decode.hip")
@@ -149,7 +153,30 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / (reps * copies)
+    # the spread: each replay timed on its own (events between replays, recorded back to back)
+    n_dist = max(16, reps)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    marks[0].record(stream)
+    for r in range(n_dist):
+        graph.replay()
+        marks[r + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([marks[r].elapsed_time(marks[r + 1]) / copies for r in range(n_dist)])
     del graph
+    # hot: the same number of calls, all on KV copy 0
+    hot = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(hot):
+        for k in range(copies):
+            call(0)
+    torch.cuda.synchronize()
+    hot.replay()
+    start.record(stream)
+    for _ in range(reps):
+        hot.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_hot = start.elapsed_time(end) / (reps * copies)
+    del hot
     sec = ms * 1e-3
     res = {
         "workload": name,
@@ -158,6 +185,9 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
                  "mode": "balanced" if plan[2] == mla.BALANCED else "uniform"},
         "us_per_call": round(ms * 1e3, 3),
         "us_per_call_eager": round(ms_eager * 1e3, 3),
+        "us_per_call_hot": round(ms_hot * 1e3, 3),
+        "us_p10_p50_p90": [round(float(np.percentile(per_call, q)) * 1e3, 3) for q in (10, 50, 90)],
+        "spread_samples": f"{n_dist} graph replays of {copies} call(s) each (one per KV copy)",
         "kv_bytes": alg["kv_bytes"],
         "alg_bytes": alg["bytes"],
         "alg_flops": alg["flops"],
@@ -291,44 +321,95 @@ def read_traffic(workload: str):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(x, budget_rows=1024, seed=0):
-    """The FP64 oracle (as it stands, METHOD mode, one split per row) on a random sample of the
-    workload's query rows, on every core of this process's affinity mask; the time per full call
-    is scaled from the sample by the rows' key counts."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Host threads the CPU oracle may use: the cores of this process's affinity mask, at most 16 (the
+# host share of one GPU on a shared GPU host).
+MAX_CPU_THREADS = 16
+
+
+def cpu_baseline(x, seconds=15.0, single_seconds=4.0, seed=0):
+    """The FP64 oracle (as it stands, METHOD mode, one split per row) on a bounded random sample of
+    the workload's query rows: batches of one row per thread until about ``seconds`` of wall time
+    have passed, on every core of this process's affinity mask (at most 16); then single rows on
+    one thread for about ``single_seconds``. The time per full call is scaled from each sample by
+    the rows' key counts."""
     import oracle
 
-    threads = len(os.sched_getaffinity(0))
+    threads = max(1, min(MAX_CPU_THREADS, len(os.sched_getaffinity(0))))
     n_rows = x.B * x.Q * x.H
-    rng = np.random.default_rng(seed)
-    sel = np.sort(rng.choice(n_rows, min(budget_rows, n_rows), replace=False))
+    order = np.random.default_rng(seed).permutation(n_rows)
     if x.kind == "dense":
         seq = np.clip(x.seq_lens.astype(np.int64), 0, x.block_table.shape[1] * x.page_size)
-        keys_of = lambda r: seq[r // (x.Q * x.H)]  # noqa: E731
+        keys = np.repeat(seq, x.Q * x.H)
     else:
-        cnt = np.clip(x.valid.astype(np.int64), 0, x.rows.shape[2]).reshape(-1)
-        keys_of = lambda r: cnt[r // x.H]  # noqa: E731
-    all_keys = sum(int(keys_of(r)) for r in range(n_rows))
-    sample_keys = sum(int(keys_of(r)) for r in sel)
-    t0 = time.perf_counter()
-    if x.kind == "dense":
-        oracle.dense(x.q_bits, x.kv, x.page_size, x.k_scale, x.block_table, x.seq_lens, x.scale,
-                     mode=oracle.METHOD, splits=1, sel=sel, threads=threads)
-    else:
-        oracle.sparse(x.q_bits, x.kv, x.k_scale, x.rows, x.valid, x.scale, mode=oracle.METHOD,
-                      splits=1, sel=sel, threads=threads)
-    dt = time.perf_counter() - t0
-    per_call = dt * all_keys / max(1, sample_keys)
+        keys = np.repeat(np.clip(x.valid.astype(np.int64), 0, x.rows.shape[2]).reshape(-1), x.H)
+    all_keys = int(keys.sum())
+
+    def run(sel, nthreads):
+        sel = np.sort(sel)
+        if x.kind == "dense":
+            oracle.dense(x.q_bits, x.kv, x.page_size, x.k_scale, x.block_table, x.seq_lens,
+                         x.scale, mode=oracle.METHOD, splits=1, sel=sel, threads=nthreads)
+        else:
+            oracle.sparse(x.q_bits, x.kv, x.k_scale, x.rows, x.valid, x.scale,
+                          mode=oracle.METHOD, splits=1, sel=sel, threads=nthreads)
+
+    def timed(nthreads, batch, budget, pos):
+        t0 = time.perf_counter()
+        used = 0
+        while used < n_rows and (used == 0 or time.perf_counter() - t0 < budget):
+            sel = order[pos + used: pos + used + batch]
+            if sel.size == 0:
+                break
+            run(sel, nthreads)
+            used += sel.size
+        dt = time.perf_counter() - t0
+        sample_keys = int(keys[order[pos: pos + used]].sum())
+        return used, dt, dt * all_keys / max(1, sample_keys)
+
+    used, dt, per_call = timed(threads, threads, seconds, 0)
+    used1, dt1, per_call1 = timed(1, 1, single_seconds, used if used < n_rows else 0)
     kv_bytes = algorithmic(x)["kv_bytes"]
     return {
-        "value": round(kv_bytes / per_call / 1e9, 4),
+        "value": float(f"{kv_bytes / per_call / 1e9:.4g}"),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{len(sel)} of {n_rows} query rows (uniform random, seed {seed}), METHOD "
-                   f"mode, one split per row; "
-                   f"{dt:.2f} s measured, scaled by key counts to {per_call:.2f} s per call"),
+        "sample": (f"{used} of {n_rows} query rows (uniform random, seed {seed}), METHOD mode, one "
+                   f"split per row, {threads} threads: {dt:.2f} s measured, scaled by key counts "
+                   f"to {per_call:.1f} s per call; single thread: {used1} rows in "
+                   f"{dt1:.2f} s, {per_call1:.1f} s per call"),
         "us_per_call": round(per_call * 1e6, 1),
+        "single_thread": {"value": float(f"{kv_bytes / per_call1 / 1e9:.4g}"), "unit": "GB/s",
+                          "us_per_call": round(per_call1 * 1e6, 1), "rows": used1},
+        "cpu_model": cpu_model(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
     }
+
+
+def headline_config(x, res):
+    """The headline workload's shape, from its inputs."""
+    cfg = {"workload": res["workload"], "description": res["description"], "kind": x.kind,
+           "B": x.B, "Q": x.Q, "H": x.H}
+    if x.kind == "dense":
+        seq = np.unique(x.seq_lens)
+        cfg.update(page_size=x.page_size, max_pages=int(x.block_table.shape[1]),
+                   seq_len=int(seq[0]) if seq.size == 1 else f"{int(seq.min())}..{int(seq.max())}",
+                   causal_rows=x.Q)
+    else:
+        cfg.update(K=int(x.rows.shape[2]), cache_rows=int(x.kv.shape[0]))
+    cfg.update(kv_bytes=res["kv_bytes"], plan=res["plan"], parallelism="single GPU")
+    return cfg
 
 
 def main():
@@ -339,8 +420,9 @@ def main():
     ap.add_argument("--workloads", default="all",
                     help="comma-separated workload names, or 'all' (headline first)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=8192,
-                    help="query rows of the headline workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall time of the CPU oracle sample on all threads (a single-thread sample "
+                         "of about 4 s follows)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the E4M3-query and P hi + lo precision runs of every workload")
     ap.add_argument("--no-combine", action="store_true",
@@ -425,13 +507,15 @@ def main():
         "unit": unit,
         "frac": round(achieved / peak, 4),
         "traffic": read_traffic(HEADLINE),
-        "kernel": "mla_decode_kernel<4, true, false, false> (dense, split query, E4M3 P)",
+        "kernel": (f"mla_decode_kernel<{h['plan']['tiles']}, {str(head_x.kind == 'dense').lower()}, "
+                   f"false, false> ({head_x.kind}, split query, E4M3 P)"),
         "hbm_frac": h["hbm_frac"],
         "mfma_frac": h["mfma_frac"],
     }
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(head_x, budget_rows=args.cpu_rows)
+        cpu = cpu_baseline(head_x, seconds=args.cpu_seconds)
+        print(f"[bench] cpu oracle: {cpu['sample']}", file=sys.stderr, flush=True)
     line = {
         "metric": METRIC,
         "value": h["kv_GBps"],
@@ -446,9 +530,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic (seeded; E4M3 cache of N(0,1)/0.05, bf16 N(0,1) queries)",
-        "config": {"workload": HEADLINE, "B": 64, "Q": 1, "H": 128, "page_size": 64,
-                   "seq_len": "U[1024,8192]", "kv_bytes": h["kv_bytes"],
-                   "plan": h["plan"], "parallelism": "single GPU"},
+        "config": headline_config(head_x, h),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "workloads": results,

@@ -107,9 +107,11 @@ size_t mla_workspace_zero_bytes(int dense, int B, int Q, int H, const mla_plan_t
  *                request b, head h.
  *   kv           the cache (see mla_kv_t); page_size >= 1.
  *   block_table  device int32 [B, max_pages]: page ids of request b's keys; key j is cache row
- *                block_table[b, j / page_size] * page_size + j % page_size. Only entries covering
- *                keys < seq_len are read. A page id whose row falls outside [0, num_rows) makes its
- *                keys absent (they contribute nothing and are not read).
+ *                block_table[b, j / page_size] * page_size + j % page_size. The whole [B,
+ *                max_pages] table must be allocated: entries covering keys < seq_len are used;
+ *                others may be read (the kernel fetches the first blocks' entries before it
+ *                knows seq_len) but never change the result. A page id whose row falls outside
+ *                [0, num_rows) makes its keys absent (they contribute nothing and are not read).
  *   seq_lens     device int32 [B]: keys of request b, clamped to [0, max_pages * page_size].
  *   scale        softmax scale multiplying q . K (k_scale is applied on top).
  *   plan         NULL for mla_plan_dense()'s choice.
@@ -128,7 +130,9 @@ mla_status_t mla_decode_dense(const void* q, const mla_kv_t* kv, const int32_t* 
  * Top-k sparse decode.
  *   rows   device int32 [B, Q, K]: flat cache rows of the keys of position i of request b; the
  *          first valid[b, i] entries are used (in order); an entry outside [0, num_rows) is an
- *          absent key (contributes nothing, is not read). Duplicate entries count once each.
+ *          absent key (contributes nothing, is not read). Duplicate entries count once each. The
+ *          whole [B, Q, K] array must be allocated: entries past valid[b, i] may be read but
+ *          never change the result.
  *   valid  device int32 [B, Q]: the count of each list, clamped to [0, K].
  *   Other arguments as for mla_decode_dense; all H heads of (b, i) share the list.
  */

@@ -118,13 +118,19 @@ def _ptr(a: np.ndarray | None):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+# Worker threads by default: the cores of this process's affinity mask, at most 16 (the host share
+# of one GPU on a shared GPU host).
+MAX_THREADS = 16
+
+
 def _threads(threads):
     if threads is not None:
         return int(threads)
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_THREADS, n))
 
 
 def _as(a, dtype):

@@ -171,6 +171,36 @@ def _check_tensor(name, t, dtype, device):
         raise ValueError(f"{name}: expected a contiguous {dtype} tensor on {device}")
 
 
+def _query_shape(q):
+    if q.dim() != 4 or q.shape[3] != 576:
+        raise ValueError(f"q: expected [B, Q, H, 576], got {tuple(q.shape)}")
+    return tuple(q.shape[:3])
+
+
+def _kv_rows(kv):
+    if kv.numel() % 576 != 0 or kv.shape[-1] != 576:
+        raise ValueError(f"kv: expected rows of 576 bytes, got {tuple(kv.shape)}")
+
+
+def _dense_index_shapes(B, kv, block_table, seq_lens):
+    """The kernel reads seq_lens[b] and block_table[b, :] for every request b < B."""
+    _kv_rows(kv)
+    if block_table.dim() != 2 or block_table.shape[0] < B or block_table.shape[1] < 1:
+        raise ValueError(f"block_table: expected [>= {B}, max_pages >= 1], got "
+                         f"{tuple(block_table.shape)}")
+    if tuple(seq_lens.shape) != (B,):
+        raise ValueError(f"seq_lens: expected [{B}], got {tuple(seq_lens.shape)}")
+
+
+def _sparse_index_shapes(B, Q, kv, rows, valid):
+    """The kernel reads valid[b, i] and rows[b, i, :] for every list (b, i)."""
+    _kv_rows(kv)
+    if rows.dim() != 3 or tuple(rows.shape[:2]) != (B, Q) or rows.shape[2] < 1:
+        raise ValueError(f"rows: expected [{B}, {Q}, K >= 1], got {tuple(rows.shape)}")
+    if tuple(valid.shape) != (B, Q):
+        raise ValueError(f"valid: expected [{B}, {Q}], got {tuple(valid.shape)}")
+
+
 # query precisions of the QK product (C ABI MLA_Q_SPLIT, MLA_Q_E4M3) and P precisions of the PV
 # product (MLA_P_E4M3, MLA_P_SPLIT); the entry points take their sum
 Q_PRECISIONS = {"split": 0, "e4m3": 1}
@@ -218,8 +248,8 @@ def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens
     _check_tensor("kv", kv, torch.uint8, dev)
     _check_tensor("block_table", block_table, torch.int32, dev)
     _check_tensor("seq_lens", seq_lens, torch.int32, dev)
-    B, Q, H, D = q.shape
-    assert D == 576
+    B, Q, H = _query_shape(q)
+    _dense_index_shapes(B, kv, block_table, seq_lens)
     o, lse = _outputs(q, o, lse)
     stream = torch.cuda.current_stream(dev).cuda_stream
     pl = cap_plan(plan if plan is not None else plan_dense(B, Q, H, block_table.shape[1], page_size),
@@ -246,8 +276,8 @@ def sparse(q: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, valid: torch.T
     _check_tensor("kv", kv, torch.uint8, dev)
     _check_tensor("rows", rows, torch.int32, dev)
     _check_tensor("valid", valid, torch.int32, dev)
-    B, Q, H, D = q.shape
-    assert D == 576
+    B, Q, H = _query_shape(q)
+    _sparse_index_shapes(B, Q, kv, rows, valid)
     K = rows.shape[2]
     o, lse = _outputs(q, o, lse)
     stream = torch.cuda.current_stream(dev).cuda_stream

@@ -62,6 +62,22 @@ def group_keys(x) -> np.ndarray:
     return np.clip(x.valid.reshape(-1).astype(np.int64), 0, x.rows.shape[2])
 
 
+def sample_rows(x, n_min=256, seed=0):
+    """Flat query rows (b * Q + i) * H + h of a full-size workload for a sampled comparison: at
+    least n_min rows, covering every request and position (every key group's rows, with heads drawn
+    at random per position), plus the first and last row and, for sparse lists with no key, their
+    first and last head."""
+    rng = np.random.default_rng(seed)
+    groups = x.B * x.Q
+    per = max(1, min(x.H, -(-n_min // groups)))
+    sel = [(g * x.H + rng.choice(x.H, per, replace=False)) for g in range(groups)]
+    sel.append(np.array([0, groups * x.H - 1]))
+    if x.kind == "sparse":
+        empty = np.flatnonzero(x.valid.reshape(-1) <= 0)
+        sel += [empty * x.H, empty * x.H + x.H - 1]
+    return np.unique(np.concatenate(sel)).astype(np.int64)
+
+
 ITEM_BLOCKS = 4   # virtual blocks a key group's run starts with under the balanced plan
 
 

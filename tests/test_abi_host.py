@@ -211,3 +211,35 @@ def test_topk_checks_arguments_without_launching():
     assert call(args(vo=None)) == NULL
     assert call(args(lg=0x1008)) == ALIGN
     assert call(args(ro=0x3002)) == ALIGN
+
+
+def test_binding_rejects_index_tensors_of_the_wrong_shape():
+    """The kernels read seq_lens / block_table (dense) and valid / rows (sparse) for every key
+    group that q implies: short or misshapen index tensors are refused before any launch."""
+    import torch
+    B, Q, H = 2, 3, 16
+    q = torch.zeros(B, Q, H, 576, dtype=torch.bfloat16)
+    kv = torch.zeros(64, 576, dtype=torch.uint8)
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)  # noqa: E731
+    dense = lambda table, seq, kv=kv, q=q: mla.dense(q, kv, table, seq, 0.07, 0.05, 16)  # noqa: E731
+    sparse = lambda rows, valid, kv=kv, q=q: mla.sparse(q, kv, rows, valid, 0.07, 0.05)  # noqa: E731
+    with pytest.raises(ValueError, match="block_table"):
+        dense(i32(B - 1, 4), i32(B))               # a request without a table row
+    with pytest.raises(ValueError, match="block_table"):
+        dense(i32(B * 4), i32(B))                  # not 2-D
+    with pytest.raises(ValueError, match="seq_lens"):
+        dense(i32(B, 4), i32(B - 1))
+    with pytest.raises(ValueError, match="seq_lens"):
+        dense(i32(B, 4), i32(B, 1))
+    with pytest.raises(ValueError, match="rows"):
+        sparse(i32(B, Q - 1, 8), i32(B, Q))
+    with pytest.raises(ValueError, match="rows"):
+        sparse(i32(B * Q, 8), i32(B, Q))
+    with pytest.raises(ValueError, match="valid"):
+        sparse(i32(B, Q, 8), i32(B * Q))
+    with pytest.raises(ValueError, match="valid"):
+        sparse(i32(B, Q, 8), i32(B, Q - 1))
+    with pytest.raises(ValueError, match="q"):
+        sparse(i32(B, Q, 8), i32(B, Q), q=torch.zeros(B, Q, H, 512, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="kv"):
+        sparse(i32(B, Q, 8), i32(B, Q), kv=torch.zeros(64, 512, dtype=torch.uint8))

@@ -37,10 +37,10 @@ def _check(o_gpu, lse_gpu, o_ref, lse_ref, o_parts_bits, what):
     # FP32 accumulation then one bf16 rounding: within 2^-8 |o| plus FP32-level cancellation
     parts = torch.from_numpy(o_parts_bits.view(np.int16)).view(torch.bfloat16).float().numpy()
     big = np.nan_to_num(np.abs(parts), nan=0.0).max(axis=0).reshape(-1, 512).max(axis=1, keepdims=True)
-    err = np.abs(og - o_ref)[~empty]
+    err = np.abs(og[~empty] - o_ref[~empty])
     tol = (2.0 ** -8 * np.abs(o_ref) + 1e-6 * big)[~empty]
     assert np.all(err <= tol), f"{what}: max o err {err.max():.3g}"
-    lerr = np.abs(lg - lse_ref)[~empty]
+    lerr = np.abs(lg[~empty] - lse_ref[~empty])   # masked first: -inf - -inf is NaN
     assert lerr.size == 0 or lerr.max() <= 1e-5 * np.maximum(1.0, np.abs(lse_ref[~empty])).max(), what
 
 

@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import (BALANCED, assert_parity, bits, run_gpu, run_oracle, say, upload)
+from gpu_util import (BALANCED, assert_parity, bits, run_gpu, run_oracle, sample_rows, say,
+                      upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -260,17 +261,14 @@ def test_balanced_one_piece_per_group_equals_uniform_single_split():
 
 # ---- full-size named workloads, sampled rows ---------------------------------------------------
 
+@pytest.mark.timeout(900)   # the FP64 oracle over 256+ rows of 131072 keys takes about a minute
 @pytest.mark.parametrize("name", ["dense_paged", "topk_sparse", "long_dense"])
 def test_full_size_workloads_sampled(name):
     w = wl.WORKLOADS[name]
     x = w.make()
-    rng = np.random.default_rng(3)
-    n_rows = x.B * x.Q * x.H
-    sel = np.unique(np.concatenate([rng.choice(n_rows, 24, replace=False), [0, n_rows - 1]]))
-    if name == "topk_sparse":
-        empty = np.flatnonzero(x.valid.reshape(-1) == 0)[:2]
-        sel = np.unique(np.concatenate([sel, empty * x.H, empty * x.H + x.H - 1]))
-    _parity(x, w.plan, f"{name} sampled", sel=sel)
+    sel = sample_rows(x, 256, seed=3)
+    assert len(sel) >= 256
+    _parity(x, w.plan, f"{name} sampled ({len(sel)} rows)", sel=sel)
 
 
 def test_workspace_reused_across_shapes_with_zero_prefix_contract():
@@ -294,3 +292,89 @@ def test_workspace_reused_across_shapes_with_zero_prefix_contract():
         assert_parity(o, lse, o_ref, lse_ref, amb, what="workspace reuse")
         # the call left its counter prefix zero
         assert int(ws[:zero].count_nonzero()) == 0
+
+
+# ---- a cache of more than 4 GiB: row offsets beyond 2^32 bytes -----------------------------------
+
+BIG_ROWS = 8_000_000                      # 4.608e9 bytes of cache
+FIRST_HIGH_ROW = -(-(1 << 32) // 576)     # 7456541: the first row whose offset needs 33 bits
+
+
+def _big_pool(n_compact_rows, rng, n_low=None):
+    """An increasing injection of the compact cache's rows into the big pool: most land at rows
+    whose byte offset is >= 2^32, a few low, the last at the pool's final row."""
+    n_low = n_compact_rows // 8 if n_low is None else n_low
+    low = np.sort(rng.choice(FIRST_HIGH_ROW, n_low, replace=False))
+    high = np.sort(rng.choice(np.arange(FIRST_HIGH_ROW, BIG_ROWS - 1), n_compact_rows - n_low - 1,
+                              replace=False))
+    return np.concatenate([low, high, [BIG_ROWS - 1]]).astype(np.int64)
+
+
+def _poisoned_pool():
+    big = torch.empty((BIG_ROWS, 576), dtype=torch.uint8, device="cuda:0")
+    big.fill_(0x7F)                        # E4M3 NaN in every row no key reads
+    return big
+
+
+def test_sparse_decode_over_a_cache_beyond_4gib():
+    """The same lists and rows, once in a compact cache and once scattered over an 8M-row
+    (4.6 GB) pool with most rows past byte offset 2^32: the decode must read the same bytes, so
+    both runs give the same bits, and both match the oracle on the compact cache."""
+    rng = np.random.default_rng(1700)
+    x = wl.sparse_case(2, 3, 32, 400, [[400, 1, 257], [129, 0, 399]], 3000, seed=1700)
+    where = _big_pool(x.kv.shape[0], rng)
+    big = _poisoned_pool()
+    big[torch.from_numpy(where).to("cuda:0")] = torch.from_numpy(x.kv).to("cuda:0")
+    xb = wl.Inputs("sparse", x.q_bits, None, x.k_scale, x.scale,
+                   rows=where[x.rows].astype(np.int32), valid=x.valid)
+    assert xb.rows.max() >= FIRST_HIGH_ROW
+    for plan in ((1, 2), (3, 1), (5, 2, BALANCED)):
+        say("cache beyond 4 GiB, sparse", plan)
+        small = run_gpu(x, upload(x), plan)
+        devb = upload(wl.Inputs("sparse", x.q_bits, x.kv[:1], x.k_scale, x.scale, rows=xb.rows,
+                                valid=x.valid))
+        devb["kv"] = big
+        got = run_gpu(xb, devb, plan)
+        assert np.array_equal(bits(got[0]), bits(small[0])), plan
+        assert np.array_equal(got[1].cpu().numpy().view(np.uint32),
+                              small[1].cpu().numpy().view(np.uint32)), plan
+        o_ref, lse_ref, amb = run_oracle(x, plan)
+        assert_parity(got[0], got[1], o_ref, lse_ref, amb, what=f"sparse beyond 4 GiB {plan}")
+    del big
+    torch.cuda.empty_cache()
+
+
+def test_dense_decode_over_a_cache_beyond_4gib():
+    """Dense: the request's pages scattered over a 125000-page pool (page 64), most of them past
+    byte offset 2^32, against the same pages in a compact pool."""
+    rng = np.random.default_rng(1701)
+    page = 64
+    x = wl.dense_case(2, 2, 32, [3000, 700], page_size=page, seed=1701, extra_pages=4)
+    n_pages = x.kv.shape[0] // page
+    big_pages = BIG_ROWS // page
+    first_high_page = -(-FIRST_HIGH_ROW // page)
+    low = rng.choice(first_high_page, 3, replace=False)
+    high = rng.choice(np.arange(first_high_page, big_pages), n_pages - 3, replace=False)
+    where = np.concatenate([low, high]).astype(np.int64)       # compact page p -> pool page
+    big = _poisoned_pool()
+    big.view(big_pages, page, 576)[torch.from_numpy(where).to("cuda:0")] = \
+        torch.from_numpy(x.kv.reshape(n_pages, page, 576)).to("cuda:0")
+    table = x.block_table.copy()
+    used = table != wl.INT32_MAX
+    table[used] = where[table[used]]
+    assert table[used].max() >= first_high_page
+    for plan in ((1, 4), (3, 2), (7, 4, BALANCED)):
+        say("cache beyond 4 GiB, dense", plan)
+        small = run_gpu(x, upload(x), plan)
+        xb = wl.Inputs("dense", x.q_bits, x.kv[:1], x.k_scale, x.scale, page_size=page,
+                       block_table=table, seq_lens=x.seq_lens)
+        devb = upload(xb)
+        devb["kv"] = big
+        got = run_gpu(xb, devb, plan)
+        assert np.array_equal(bits(got[0]), bits(small[0])), plan
+        assert np.array_equal(got[1].cpu().numpy().view(np.uint32),
+                              small[1].cpu().numpy().view(np.uint32)), plan
+        o_ref, lse_ref, amb = run_oracle(x, plan)
+        assert_parity(got[0], got[1], o_ref, lse_ref, amb, what=f"dense beyond 4 GiB {plan}")
+    del big
+    torch.cuda.empty_cache()

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import BALANCED, as_f64, assert_parity, bits, run_gpu, run_oracle, say, upload
+from gpu_util import (BALANCED, as_f64, assert_parity, bits, run_gpu, run_oracle, sample_rows,
+                      say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,13 +94,13 @@ def test_closer_to_the_textbook_softmax_than_e4m3_p(seed):
     assert err[SPLIT] < 0.5 * err["e4m3"]
 
 
+@pytest.mark.timeout(900)   # the FP64 oracle over 256+ rows of 131072 keys takes about a minute
 @pytest.mark.parametrize("name", ["dense_paged", "topk_sparse", "long_dense"])
 def test_full_size_workloads_sampled(name):
     w = wl.WORKLOADS[name]
     x = w.make()
-    rng = np.random.default_rng(15)
-    n_rows = x.B * x.Q * x.H
-    sel = np.unique(np.concatenate([rng.choice(n_rows, 16, replace=False), [0, n_rows - 1]]))
+    sel = sample_rows(x, 256, seed=15)
+    assert len(sel) >= 256
     plan = tuple(w.plan)
     if plan[1] == 4:
         plan = (plan[0], 2) + plan[2:]

@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import BALANCED, assert_parity, bits, run_gpu, run_oracle, say, upload
+from gpu_util import (BALANCED, assert_parity, bits, run_gpu, run_oracle, sample_rows, say,
+                      upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,11 +96,11 @@ def test_grid_queries_give_the_default_precision_bits():
         assert np.array_equal(a[1].cpu().numpy(), b[1].cpu().numpy())
 
 
+@pytest.mark.timeout(900)   # the FP64 oracle over 256+ rows of 131072 keys takes about a minute
 @pytest.mark.parametrize("name", ["dense_paged", "topk_sparse", "long_dense"])
 def test_full_size_workloads_sampled(name):
     w = wl.WORKLOADS[name]
     x = w.make()
-    rng = np.random.default_rng(5)
-    n_rows = x.B * x.Q * x.H
-    sel = np.unique(np.concatenate([rng.choice(n_rows, 16, replace=False), [0, n_rows - 1]]))
+    sel = sample_rows(x, 256, seed=5)
+    assert len(sel) >= 256
     _parity(x, w.plan, f"{name} sampled", sel=sel)

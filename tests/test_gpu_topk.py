@@ -43,6 +43,12 @@ CASES = [
     (4, 32768, 2048, [32768, 32764, 2048, 20000], None, 0.01),
     (2, 32768, 2048, [32768, 32768], 1, 0.0),          # massive ties: values in {-3..3}
     (2, 512, 1000, [512, 300], None, 0.0),             # K > N
+    # rows longer than one 32768-column span: the keys are reloaded per span and the output runs
+    # carry over from span to span
+    (3, 40000, 2048, [32769, 40000, 35000], None, 0.0),   # ends just past, well past the first span
+    (2, 65536, 2048, [65536, 50000], 2, 0.05),             # ties at the threshold in both spans
+    (1, 131072, 2048, [131072], None, 0.01),               # four spans
+    (2, 65544, 4096, [65544, 40001], 8, 0.0),              # K above 2048, a ragged last span
 ]
 
 
@@ -101,3 +107,26 @@ def test_topk_then_sparse_decode_matches_the_oracle():
                                         cnt.reshape(B, Q), x.scale, mode=oracle.METHOD, chunk=128,
                                         allowance=True)
     assert_parity(o, lse, o_ref, lse_ref, amb, what="top-k -> sparse decode")
+
+
+def test_topk_rows_whose_first_span_holds_fewer_than_k_candidates():
+    """Spans of 32768 columns: the first span of row 0 holds only 1000 candidates (the rest NaN),
+    so the threshold and most of the list come from the second; row 1 has fewer than K candidates
+    in all (every one is taken, in column order, across spans); row 2 has exactly K."""
+    N, K = 40000, 3000
+    bits = _logits(3, N, seed=91, tie_levels=4)
+    rng = np.random.default_rng(92)
+    nan_cols = rng.permutation(32768)[:32768 - 1000]
+    bits[0, nan_cols] = 0x7FC0
+    bits[1, :] = 0x7FC0
+    keep = np.sort(rng.permutation(N)[:2500])
+    bits[1, keep] = _logits(1, N, seed=93)[0, keep]
+    bits[2, :] = 0x7FC0
+    keep2 = np.sort(rng.permutation(N)[:K])
+    bits[2, keep2] = _logits(1, N, seed=94, tie_levels=2)[0, keep2]
+    ends = [N, N, N]
+    rows, valid = _run(bits, ends, K)
+    ref, cnt = otopk.select(bits, np.asarray(ends), K)
+    assert list(cnt) == [K, 2500, K]
+    assert np.array_equal(valid, cnt)
+    assert np.array_equal(rows, ref)

@@ -100,3 +100,46 @@ def test_remap_follows_the_page_table():
                 assert out[r, t] == -1
             else:
                 assert out[r, t] == table[b, j // page] * page + j % page
+
+
+def test_remap_through_an_identity_table_is_the_closed_form():
+    """table[b, p] = b * P + p lays request b's positions out contiguously from row b * P * page:
+    position j must become row b * P * page + j, whatever the page size."""
+    for page, P, Q in ((1, 40, 1), (16, 5, 3), (64, 3, 2), (7, 11, 4)):
+        B = 3
+        table = (np.arange(B)[:, None] * P + np.arange(P)[None, :]).astype(np.int32)
+        cols = np.stack([np.arange(P * page) for _ in range(B * Q)]).astype(np.int32)
+        out = topk.remap(cols, table, page, Q, B * P * page)
+        b = np.arange(B * Q)[:, None] // Q
+        assert np.array_equal(out, b * P * page + cols), (page, P, Q)
+        # past the table (page index P) and past the cache: -1
+        assert np.all(topk.remap(np.full((B * Q, 1), P * page), table, page, Q, B * P * page) == -1)
+        assert np.all(topk.remap(cols, table, page, Q, B * P * page - 1)[-Q:, -1] == -1)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_sparse_decode_over_remapped_positions_equals_the_dense_decode(seed):
+    """The remap is the dense decode's key -> row rule: a sparse list of positions 0 .. n_i - 1
+    (n_i = seq_len - Q + i + 1, the causal bound of row i) remapped through the page table gives,
+    in the oracle's sparse front end, bit for bit what its dense front end computes from the table
+    itself (one split, 128-key chunks, so both walk the same keys in the same chunks)."""
+    import oracle
+    import workloads as wl
+    rng = np.random.default_rng(seed)
+    B, Q, H, page = 3, 3, 2, int(rng.choice([1, 16, 64]))
+    seq = rng.integers(1, 300, size=B)
+    seq[0] = 1                                    # row 0 before its causal bound: no key
+    x = wl.dense_case(B, Q, H, seq, page_size=page, seed=40 + seed, extra_pages=5)
+    n_i = np.clip(x.seq_lens[:, None] - Q + np.arange(Q)[None, :] + 1, 0, None)   # [B, Q]
+    K = int(x.seq_lens.max())
+    cols = np.full((B * Q, K), -1, np.int32)
+    for r in range(B * Q):
+        cols[r, :n_i.reshape(-1)[r]] = np.arange(n_i.reshape(-1)[r])
+    rows = topk.remap(cols, x.block_table, page, Q, x.kv.shape[0]).reshape(B, Q, K)
+    for mode in (oracle.EXACT, oracle.METHOD):
+        od, ld = oracle.dense(x.q_bits, x.kv, page, x.k_scale, x.block_table, x.seq_lens, x.scale,
+                              mode=mode, splits=1, chunk=128)
+        os_, ls = oracle.sparse(x.q_bits, x.kv, x.k_scale, rows, n_i.astype(np.int32), x.scale,
+                                mode=mode, splits=1, chunk=128)
+        assert np.array_equal(od, os_) and np.array_equal(ld, ls), mode
+    assert np.all(np.isneginf(ld[0, :Q - 1]))
