@@ -12,9 +12,9 @@ HIP events on the stream the kernel runs on bracket the timed calls. The reporte
 measured on a HIP graph that holds one call per KV copy, replayed back to back (the GPU time per
 call, with no host launch work in between); the time of K eager launches from Python is reported
 beside it (us_per_call_eager), and for the large workloads the two agree. Also reported per
-workload: the spread of the time per call over individually timed graph replays (p10 / p50 / p90,
-each replay being one call per KV copy) and the hot time per call (every call on one KV copy, so
-whatever of it fits stays in the caches).
+workload: the spread of the time per call over the timed graph replays (p10 / p50 / p90, each
+replay being one call per KV copy; an event is recorded between every two replays) and the hot
+time per call (every call on one KV copy, so whatever of it fits stays in the caches).
 
 Prints ONE JSON line.
 """
@@ -45,11 +45,19 @@ METRIC = ("µs/call and KV HBM GB/s (fraction of 8 TB/s peak), dense + top-k spa
 KERNEL_SRC = os.path.join(ROOT, "paged_mla_decode_fp8_amd", "csrc", "mla_decode.hip")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel source with its // comments and blank lines removed, so that counter
-    summaries stay valid across comment edits and go stale on any code change."""
-    with open(KERNEL_SRC) as f:
-        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in f]
+def kernel_source_hash(text: str | None = None) -> str:
+    """Hash of the decode kernel's device code (the source up to its host-side section) with //
+    comments, blank lines and #include lines removed, so that counter summaries stay valid across
+    comment edits and host-side changes and go stale on any change of the kernel's code."""
+    if text is None:
+        with open(KERNEL_SRC) as f:
+            text = f.read()
+    lines = []
+    for ln in text.splitlines():
+        if "---- host side" in ln:
+            break
+        if not ln.startswith("#include"):
+            lines.append(re.sub(r"//.*", "", ln).rstrip())
     code = "\n".join(ln for ln in lines if ln)
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
@@ -145,23 +153,19 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
     torch.cuda.synchronize()
     if not torch.equal(o.view(torch.int16), o_eager.view(torch.int16)):
         raise RuntimeError(f"{name}: graph replay output differs from the eager call")
+    # the timed calls: reps replays back to back, an event between every two (the spread of the
+    # time per call comes from the same replays as its mean)
     reps = max(1, steps // copies)
     stream = torch.cuda.current_stream(dev)
-    start.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    end.record(stream)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / (reps * copies)
-    # the spread: each replay timed on its own (events between replays, recorded back to back)
-    n_dist = max(16, reps)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
     marks[0].record(stream)
-    for r in range(n_dist):
+    for r in range(reps):
         graph.replay()
         marks[r + 1].record(stream)
     torch.cuda.synchronize()
-    per_call = np.array([marks[r].elapsed_time(marks[r + 1]) / copies for r in range(n_dist)])
+    ms = marks[0].elapsed_time(marks[reps]) / (reps * copies)
+    per_call = np.array([marks[r].elapsed_time(marks[r + 1]) / copies for r in range(reps)])
     del graph
     # hot: the same number of calls, all on KV copy 0
     hot = torch.cuda.CUDAGraph()
@@ -187,7 +191,7 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
         "us_per_call_eager": round(ms_eager * 1e3, 3),
         "us_per_call_hot": round(ms_hot * 1e3, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per_call, q)) * 1e3, 3) for q in (10, 50, 90)],
-        "spread_samples": f"{n_dist} graph replays of {copies} call(s) each (one per KV copy)",
+        "spread_samples": f"{reps} graph replays of {copies} call(s) each (one per KV copy)",
         "kv_bytes": alg["kv_bytes"],
         "alg_bytes": alg["bytes"],
         "alg_flops": alg["flops"],

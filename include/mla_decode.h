@@ -225,6 +225,55 @@ mla_status_t mla_topk_rows(const void* logits, const int32_t* row_ends, int R, i
                            const int32_t* block_table, int max_pages, int page_size, int Q,
                            int64_t num_rows, int32_t* rows_out, int32_t* valid_out, void* stream);
 
+/*
+ * The indexer's candidate blocks -> sparse block ids and valid column counts
+ * (vllm.model_executor.kernels.attention.dsa.sparse_mqa_logits, candidate_blocks_to_sparse_indices
+ * and _expand_candidates_kernel). ratio = candidate_block_size / sparse_block_kv must be 1 or 2.
+ * For row r with K range [ks, ke) = [row_ks[r], row_ke[r]) (kv_len = max(ke - ks, 0)):
+ *   - candidate c (request-local, in units of candidate_block_size positions; -1 padding) stands
+ *     for sparse blocks c (ratio 1) or 2c, 2c + 1 (ratio 2); a block b is valid when
+ *     0 <= b < ceil(kv_len / sparse_block_kv);
+ *   - sparse_indices[r, 0 .. n) = the n valid blocks in ascending order plus floor(ks /
+ *     sparse_block_kv) (repeats kept, each counting), sparse_indices[r, n .. K * ratio) = the last
+ *     of them (the anchor floor(ks / sparse_block_kv) alone when n = 0);
+ *   - end[r] = (n - 1) * sparse_block_kv + min(max(ke - (last * sparse_block_kv + ks), 1),
+ *     sparse_block_kv) with last the largest valid block (0 when n = 0): the valid sparse-token
+ *     columns, which form a prefix of the row.
+ *   candidate_blocks  device int32 [rows, K]; row_ks, row_ke device int32 [rows];
+ *   sparse_indices    device int32 [rows, K * ratio]; end device int32 [rows].
+ * Errors: MLA_ERR_SHAPE (rows < 0, K < 1, a ratio other than 1 or 2, K * ratio > 16384),
+ * MLA_ERR_NULL, MLA_ERR_ALIGN, MLA_ERR_LAUNCH. rows = 0 launches nothing. Asynchronous on `stream`.
+ */
+mla_status_t mla_expand_candidates(const int32_t* candidate_blocks, int rows, int K,
+                                   const int32_t* row_ks, const int32_t* row_ke,
+                                   int candidate_block_size, int sparse_block_kv,
+                                   int32_t* sparse_indices, int32_t* end, void* stream);
+
+/* The sparse logit columns of mla_topk_sparse_rows: column j * sparse_block_kv + o of logits row r
+ * scores request-local position (sparse_indices[r, j] - floor(row_ks[r] / sparse_block_kv)) *
+ * sparse_block_kv + o. S * sparse_block_kv must cover the logits' N columns. */
+typedef struct {
+    const int32_t* sparse_indices;   /* device int32 [R, S] (mla_expand_candidates' output) */
+    int32_t S;
+    int32_t sparse_block_kv;
+    const int32_t* row_ks;           /* device int32 [R]: the K range starts */
+} mla_sparse_cols_t;
+
+/*
+ * Top-k over sparse logits, remapped to positions, then (with a block table) to cache rows
+ * (vllm.model_executor.kernels.attention.dsa.sparse_mqa_logits, sparse_topk_remap and
+ * _sparse_topk_remap_kernel): the select of mla_topk_rows over columns [0, min(end[r], N)) of
+ * logits row r, then every selected column becomes its position by `cols` (-1 for a position
+ * outside [0, 2^31)), then, when block_table is not NULL, the cache row of that position as in
+ * mla_topk_rows. cols NULL: the columns are the positions (mla_topk_rows is this with cols NULL).
+ * Arguments and errors otherwise as for mla_topk_rows; MLA_ERR_SHAPE also for S < 1,
+ * sparse_block_kv < 1 or S * sparse_block_kv < N.
+ */
+mla_status_t mla_topk_sparse_rows(const void* logits, const int32_t* end, int R, int N, int K,
+                                  const mla_sparse_cols_t* cols, const int32_t* block_table,
+                                  int max_pages, int page_size, int Q, int64_t num_rows,
+                                  int32_t* rows_out, int32_t* valid_out, void* stream);
+
 /* A static, human-readable name of a status. */
 const char* mla_status_string(mla_status_t status);
 

@@ -97,3 +97,76 @@ def remap(cols: np.ndarray, block_table: np.ndarray, page_size: int, q_per_reque
             if page >= 0 and 0 <= row < num_rows:
                 out[r, t] = row
     return out
+
+
+# ---- candidate blocks -> sparse block ids, and sparse logit columns -> positions --------------------
+#
+# vllm.model_executor.kernels.attention.dsa.sparse_mqa_logits: the indexer names candidate blocks of
+# a row's context; they are expanded into sparse blocks (candidate_blocks_to_sparse_indices and
+# _expand_candidates_kernel), the logits are scored over the sparse blocks' columns, the top-k runs
+# over those columns (bounded by the row's valid column count), and the chosen columns are mapped
+# back to request-local positions (sparse_topk_remap and _sparse_topk_remap_kernel).
+
+def expand_candidates(candidate_blocks, row_ks, row_ke, candidate_block_size: int,
+                      sparse_block_kv: int):
+    """Candidate blocks -> (sparse block ids [rows, K * ratio], valid column counts [rows]).
+
+    ratio = candidate_block_size / sparse_block_kv (1 or 2); with ratio 2 candidate c stands for
+    sparse blocks 2c and 2c + 1, in that order. A row's K range is [ks, ke) (kv_len = max(ke - ks,
+    0) positions); a sparse block b is valid when 0 <= b < ceil(kv_len / sparse_block_kv). The
+    valid blocks come out in ascending order, offset by ks // sparse_block_kv (the row's anchor),
+    and the rest of the row repeats the last (largest) valid one, or holds the anchor when none is
+    valid. The count of valid sparse-token columns: every valid block is full except the last,
+    which holds the positions from its start to kv_len (at least one, at most a block)."""
+    cand = np.asarray(candidate_blocks, np.int64)
+    ks = np.asarray(row_ks, np.int64).reshape(-1)
+    ke = np.asarray(row_ke, np.int64).reshape(-1)
+    sbk = int(sparse_block_kv)
+    ratio = int(candidate_block_size) // sbk
+    assert ratio * sbk == candidate_block_size and ratio in (1, 2)
+    rows, K = cand.shape
+    S = K * ratio
+    si = np.zeros((rows, S), np.int32)
+    end = np.zeros(rows, np.int32)
+    for r in range(rows):
+        blocks = []
+        for c in cand[r].tolist():
+            blocks += [c] if ratio == 1 else [2 * c, 2 * c + 1]
+        kv_len = max(int(ke[r] - ks[r]), 0)
+        max_block = -(-kv_len // sbk)
+        valid = sorted(b for b in blocks if 0 <= b < max_block)
+        base = int(ks[r]) // sbk
+        pad = valid[-1] + base if valid else base
+        si[r] = [b + base for b in valid] + [pad] * (S - len(valid))
+        if valid:
+            last_start = valid[-1] * sbk + int(ks[r])
+            end[r] = (len(valid) - 1) * sbk + min(max(int(ke[r]) - last_start, 1), sbk)
+    return si, end
+
+
+def sparse_cols_to_positions(cols, sparse_indices, row_ks, sparse_block_kv: int, width: int):
+    """Selected sparse logit columns [rows, k] -> request-local positions: column j * sbk + o of a
+    row scores position (sparse_indices[row, j] - ks // sbk) * sbk + o; a column outside
+    [0, width) (an unfilled place, -1) becomes -1, and so does a position outside [0, 2^31) (only
+    sparse ids below the row's anchor give one: read as an absent key, like the -1 places)."""
+    cols = np.asarray(cols, np.int64)
+    si = np.asarray(sparse_indices, np.int64)
+    ks = np.asarray(row_ks, np.int64).reshape(-1)
+    sbk = int(sparse_block_kv)
+    out = np.full(cols.shape, -1, np.int32)
+    for r in range(cols.shape[0]):
+        for t in range(cols.shape[1]):
+            c = int(cols[r, t])
+            if 0 <= c < width:
+                pos = (si[r, c // sbk] - int(ks[r]) // sbk) * sbk + c % sbk
+                out[r, t] = pos if 0 <= pos < 2**31 else -1
+    return out
+
+
+def sparse_topk(logits_bits, end, k: int, sparse_indices, row_ks, sparse_block_kv: int):
+    """The top-k over sparse logits [rows, width] bounded by each row's valid column count
+    ``end``, remapped to request-local positions: (positions [rows, k], -1 padded; counts)."""
+    bits = np.asarray(logits_bits, np.uint16)
+    cols, cnt = select(bits, np.asarray(end), k)
+    return sparse_cols_to_positions(cols, sparse_indices, row_ks, sparse_block_kv,
+                                    bits.shape[1]), cnt

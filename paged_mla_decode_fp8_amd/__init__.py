@@ -16,7 +16,8 @@ import torch
 
 from ._build import LIB
 
-__all__ = ["MlaError", "Plan", "dense", "sparse", "plan_dense", "plan_sparse", "workspace_bytes",
+__all__ = ["MlaError", "Plan", "dense", "sparse", "combine", "topk_rows",
+           "expand_candidates", "topk_sparse_rows", "plan_dense", "plan_sparse", "workspace_bytes",
            "workspace_zero_bytes", "library_path", "UNIFORM", "BALANCED"]
 
 MLA_OK = 0
@@ -42,6 +43,11 @@ class _KV(ctypes.Structure):
 
 class _Plan(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int32), ("tiles", ctypes.c_int32), ("mode", ctypes.c_int32)]
+
+
+class _SparseCols(ctypes.Structure):
+    _fields_ = [("sparse_indices", ctypes.c_void_p), ("S", ctypes.c_int32),
+                ("sparse_block_kv", ctypes.c_int32), ("row_ks", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,6 +91,11 @@ def _load():
         lib.mla_topk_rows.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, ctypes.c_int64, P, P,
                                       P]
         lib.mla_topk_rows.restype = i32
+        lib.mla_topk_sparse_rows.argtypes = [P, P, i32, i32, i32, ctypes.POINTER(_SparseCols), P,
+                                             i32, i32, i32, ctypes.c_int64, P, P, P]
+        lib.mla_topk_sparse_rows.restype = i32
+        lib.mla_expand_candidates.argtypes = [P, i32, i32, P, P, i32, i32, P, P, P]
+        lib.mla_expand_candidates.restype = i32
         _lib = lib
     return _lib
 
@@ -338,4 +349,67 @@ def topk_rows(logits: torch.Tensor, row_ends: torch.Tensor, k: int, *, block_tab
     _check(_load().mla_topk_rows(_ptr(logits), _ptr(row_ends), R, N, int(k), _ptr(block_table),
                                  max_pages, int(page_size), int(q_per_request), int(num_rows),
                                  _ptr(rows), _ptr(valid), ctypes.c_void_p(stream)))
+    return rows, valid
+
+
+def expand_candidates(candidate_blocks: torch.Tensor, row_ks: torch.Tensor, row_ke: torch.Tensor,
+                      candidate_block_size: int, sparse_block_kv: int, *, sparse_indices=None,
+                      end=None):
+    """Candidate blocks [rows, K] (request-local ids, -1 padded) -> (sparse block ids [rows, K *
+    ratio], valid sparse-token column counts [rows]) (C ABI mla_expand_candidates), on the current
+    stream."""
+    dev = candidate_blocks.device
+    _check_tensor("candidate_blocks", candidate_blocks, torch.int32, dev)
+    _check_tensor("row_ks", row_ks, torch.int32, dev)
+    _check_tensor("row_ke", row_ke, torch.int32, dev)
+    if candidate_blocks.dim() != 2:
+        raise ValueError("candidate_blocks must be [rows, K]")
+    rows, K = candidate_blocks.shape
+    if tuple(row_ks.shape) != (rows,) or tuple(row_ke.shape) != (rows,):
+        raise ValueError("row_ks and row_ke must be [rows]")
+    ratio = candidate_block_size // sparse_block_kv if sparse_block_kv > 0 else 0
+    sparse_indices = _out_tensor("sparse_indices", sparse_indices, (rows, K * max(ratio, 1)),
+                                 torch.int32, dev)
+    end = _out_tensor("end", end, (rows,), torch.int32, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(_load().mla_expand_candidates(_ptr(candidate_blocks), rows, K, _ptr(row_ks),
+                                         _ptr(row_ke), int(candidate_block_size),
+                                         int(sparse_block_kv), _ptr(sparse_indices), _ptr(end),
+                                         ctypes.c_void_p(stream)))
+    return sparse_indices, end
+
+
+def topk_sparse_rows(logits: torch.Tensor, end: torch.Tensor, k: int, sparse_indices: torch.Tensor,
+                     row_ks: torch.Tensor, sparse_block_kv: int, *, block_table=None,
+                     page_size: int = 1, q_per_request: int = 1, num_rows: int = 0, rows=None,
+                     valid=None):
+    """Top-k over sparse logits [R, N] bounded by ``end`` [R], the chosen columns remapped to
+    request-local positions through ``sparse_indices`` [R, S] and ``row_ks`` [R] (C ABI
+    mla_topk_sparse_rows), then to cache rows through ``block_table`` when given. Returns
+    (rows int32 [R, k], -1 padded; valid int32 [R]) on the current stream."""
+    dev = logits.device
+    _check_tensor("logits", logits, torch.bfloat16, dev)
+    _check_tensor("end", end, torch.int32, dev)
+    _check_tensor("sparse_indices", sparse_indices, torch.int32, dev)
+    _check_tensor("row_ks", row_ks, torch.int32, dev)
+    R, N = logits.shape
+    if tuple(end.shape) != (R,) or tuple(row_ks.shape) != (R,):
+        raise ValueError("end and row_ks must be [R]")
+    if sparse_indices.dim() != 2 or sparse_indices.shape[0] != R:
+        raise ValueError("sparse_indices must be [R, S]")
+    max_pages = 0
+    if block_table is not None:
+        _check_tensor("block_table", block_table, torch.int32, dev)
+        max_pages = block_table.shape[1]
+        if block_table.shape[0] * q_per_request < R:
+            raise ValueError("block_table needs a row per request")
+    rows = _out_tensor("rows", rows, (R, k), torch.int32, dev)
+    valid = _out_tensor("valid", valid, (R,), torch.int32, dev)
+    cols = _SparseCols(sparse_indices.data_ptr(), sparse_indices.shape[1], int(sparse_block_kv),
+                       row_ks.data_ptr())
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(_load().mla_topk_sparse_rows(_ptr(logits), _ptr(end), R, N, int(k), ctypes.byref(cols),
+                                        _ptr(block_table), max_pages, int(page_size),
+                                        int(q_per_request), int(num_rows), _ptr(rows), _ptr(valid),
+                                        ctypes.c_void_p(stream)))
     return rows, valid

@@ -142,10 +142,43 @@ __device__ inline void tk_pick_bin(TkShared& sh, int nbins, int need, int slot)
     __syncthreads();
 }
 
+// What the selected columns become: with `si` set, sparse logit columns -> request-local
+// positions (column j * sbk + o of row r scores position (si[r, j] - floor(ks[r] / sbk)) * sbk + o);
+// then, with `table` set, positions -> cache rows through request r / Q's page table.
+struct TkRemap {
+    const int32_t* si;      // [R, S] sparse block ids backing the logit columns, or null
+    int S, sbk;
+    const int32_t* ks;      // [R] K range starts (the sparse ids' anchor)
+    const int32_t* table;   // [R / Q, max_pages] page ids, or null
+    int max_pages, page_size, Q;
+    int64_t num_rows;
+};
+
+__device__ inline int64_t tk_floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// One selected column -> the list entry (-1 where the position or its page or row is invalid).
+__device__ inline int32_t tk_remap(const TkRemap& m, int r, int col)
+{
+    int64_t j = col;
+    if (m.si) {
+        const int64_t blk = m.si[(int64_t)r * m.S + col / m.sbk];
+        j = (blk - tk_floor_div(m.ks[r], m.sbk)) * m.sbk + col % m.sbk;
+        if (j < 0 || j > 0x7FFFFFFF)
+            return -1;
+    }
+    if (!m.table)
+        return (int32_t)j;
+    const int64_t pgi = j / m.page_size;
+    if (pgi >= m.max_pages)
+        return -1;
+    const int64_t page = m.table[(int64_t)(r / m.Q) * m.max_pages + pgi];
+    const int64_t cr = page * m.page_size + j % m.page_size;
+    return (page >= 0 && cr < m.num_rows) ? (int32_t)cr : -1;
+}
+
 __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     const uint16_t* __restrict__ logits, const int32_t* __restrict__ row_ends, int N, int K,
-    const int32_t* __restrict__ table, int max_pages, int page_size, int Q, int64_t num_rows,
-    int32_t* __restrict__ rows_out, int32_t* __restrict__ valid_out)
+    const TkRemap remap, int32_t* __restrict__ rows_out, int32_t* __restrict__ valid_out)
 {
     __shared__ TkShared sh;
     const int r = blockIdx.x;
@@ -154,7 +187,6 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     int n = row_ends[r];
     n = n < 0 ? 0 : (n > N ? N : n);
     int32_t* out = rows_out + (int64_t)r * K;
-    const int b = r / Q;
     // a row of one span stays in registers for all three passes
     const bool resident = n <= TK_SPAN;
     uint32_t kw[TK_KW];
@@ -230,29 +262,90 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
         eq_run += tot_eq;
     }
     const int count = b1 >= 0 ? K : gt_run;
-    // the columns -> cache rows, each thread a strided share of the list (its writes are the
-    // workgroup's, visible after the barrier)
+    // the columns -> positions -> cache rows, each thread a strided share of the list (its writes
+    // are the workgroup's, visible after the barrier)
     __syncthreads();
-    for (int i = t; i < K; i += TK_THREADS) {
-        int32_t rr = -1;
-        if (i < count) {
-            const int j = out[i];
-            rr = j;
-            if (table) {
-                const int pgi = j / page_size;
-                rr = -1;
-                if (pgi < max_pages) {
-                    const int64_t page = table[(int64_t)b * max_pages + pgi];
-                    const int64_t cr = page * page_size + j % page_size;
-                    if (page >= 0 && cr < num_rows)
-                        rr = (int32_t)cr;
+    for (int i = t; i < K; i += TK_THREADS)
+        out[i] = i < count ? tk_remap(remap, r, out[i]) : -1;
+    if (t == 0)
+        valid_out[r] = count;
+}
+
+// ---- candidate blocks -> sparse block ids --------------------------------------------------------
+// vllm.model_executor.kernels.attention.dsa.sparse_mqa_logits, _expand_candidates_kernel and
+// candidate_blocks_to_sparse_indices: per row, candidate c (in units of candidate_block_size
+// positions) stands for sparse blocks c (ratio 1) or 2c, 2c + 1 (ratio 2, in that order); the blocks
+// inside the row's K range [ks, ke) (0 <= b < ceil(max(ke - ks, 0) / sbk)) come out ascending and
+// anchored at floor(ks / sbk), the rest of the row repeats the last one (or holds the anchor when
+// none is valid); end = the valid sparse-token columns, every valid block full but the last, which
+// holds min(max(ke - (last * sbk + ks), 1), sbk).
+//
+// One workgroup per row: the row's K * ratio block ids, invalid ones as INT32_MAX, sorted
+// ascending by a bitonic sort in LDS (padded to a power of two, at most EX_MAX), then written out.
+constexpr int EX_THREADS = 256;
+constexpr int EX_MAX = 16384;   // 64 KB of LDS
+
+__global__ __launch_bounds__(EX_THREADS) void mla_expand_kernel(
+    const int32_t* __restrict__ cand, int K, int ratio, const int32_t* __restrict__ row_ks,
+    const int32_t* __restrict__ row_ke, int sbk, int npad, int32_t* __restrict__ si,
+    int32_t* __restrict__ end)
+{
+    extern __shared__ int32_t ex_v[];
+    __shared__ int ex_valid;
+    const int r = blockIdx.x, t = threadIdx.x;
+    const int64_t ks = row_ks[r], ke = row_ke[r];
+    const int64_t kv_len = ke - ks > 0 ? ke - ks : 0;
+    const int64_t max_block = (kv_len + sbk - 1) / sbk;
+    const int S = K * ratio;
+    if (t == 0)
+        ex_valid = 0;
+    __syncthreads();
+    int nv = 0;
+    for (int i = t; i < npad; i += EX_THREADS) {
+        int32_t v = 0x7FFFFFFF;
+        if (i < S) {
+            const int64_t c = cand[(int64_t)r * K + i / ratio];
+            const int64_t b = ratio == 2 ? 2 * c + (i & 1) : c;
+            if (b >= 0 && b < max_block) {
+                v = (int32_t)b;
+                nv++;
+            }
+        }
+        ex_v[i] = v;
+    }
+    atomicAdd(&ex_valid, nv);
+    // bitonic sort, ascending: stage (k, j) compares element i with i ^ j
+    for (int k = 2; k <= npad; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            __syncthreads();
+            for (int i = t; i < npad; i += EX_THREADS) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const int32_t a = ex_v[i], b = ex_v[p];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) {
+                        ex_v[i] = b;
+                        ex_v[p] = a;
+                    }
                 }
             }
         }
-        out[i] = rr;
     }
-    if (t == 0)
-        valid_out[r] = count;
+    __syncthreads();
+    const int n = ex_valid;
+    const int64_t base = tk_floor_div(ks, sbk);
+    const int64_t last = n > 0 ? ex_v[n - 1] : -1;
+    const int32_t pad = (int32_t)(n > 0 ? last + base : base);
+    for (int i = t; i < S; i += EX_THREADS)
+        si[(int64_t)r * S + i] = i < n ? (int32_t)(ex_v[i] + base) : pad;
+    if (t == 0) {
+        int64_t e = 0;
+        if (n > 0) {
+            const int64_t fill = ke - (last * sbk + ks);
+            e = (int64_t)(n - 1) * sbk + (fill < 1 ? 1 : (fill > sbk ? sbk : fill));
+        }
+        end[r] = (int32_t)e;
+    }
 }
 
 bool tk_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -265,21 +358,73 @@ mla_status_t mla_topk_rows(const void* logits, const int32_t* row_ends, int R, i
                            const int32_t* block_table, int max_pages, int page_size, int Q,
                            int64_t num_rows, int32_t* rows_out, int32_t* valid_out, void* stream)
 {
+    return mla_topk_sparse_rows(logits, row_ends, R, N, K, nullptr, block_table, max_pages,
+                                page_size, Q, num_rows, rows_out, valid_out, stream);
+}
+
+mla_status_t mla_topk_sparse_rows(const void* logits, const int32_t* end, int R, int N, int K,
+                                  const mla_sparse_cols_t* cols, const int32_t* block_table,
+                                  int max_pages, int page_size, int Q, int64_t num_rows,
+                                  int32_t* rows_out, int32_t* valid_out, void* stream)
+{
     if (R < 0 || N < 8 || N % 8 != 0 || K < 1 || Q < 1 || R > 0x7FFFFFFF)
         return MLA_ERR_SHAPE;
     if (block_table && (max_pages < 1 || page_size < 1 || num_rows < 0 ||
                         (int64_t)max_pages * page_size > 0x7FFFFFFF))
         return MLA_ERR_SHAPE;
+    if (cols && (cols->sparse_block_kv < 1 || cols->S < 1 ||
+                 (int64_t)cols->S * cols->sparse_block_kv < N))
+        return MLA_ERR_SHAPE;
     if (R == 0)
         return MLA_OK;
-    if (!logits || !row_ends || !rows_out || !valid_out)
+    if (!logits || !end || !rows_out || !valid_out || (cols && (!cols->sparse_indices || !cols->row_ks)))
         return MLA_ERR_NULL;
-    if (!tk_aligned(logits, 16) || !tk_aligned(row_ends, 4) || !tk_aligned(rows_out, 4) ||
-        !tk_aligned(valid_out, 4) || !tk_aligned(block_table, 4))
+    if (!tk_aligned(logits, 16) || !tk_aligned(end, 4) || !tk_aligned(rows_out, 4) ||
+        !tk_aligned(valid_out, 4) || !tk_aligned(block_table, 4) ||
+        (cols && (!tk_aligned(cols->sparse_indices, 4) || !tk_aligned(cols->row_ks, 4))))
         return MLA_ERR_ALIGN;
+    TkRemap m{};
+    if (cols) {
+        m.si = cols->sparse_indices;
+        m.S = cols->S;
+        m.sbk = cols->sparse_block_kv;
+        m.ks = cols->row_ks;
+    }
+    m.table = block_table;
+    m.max_pages = max_pages;
+    m.page_size = page_size;
+    m.Q = Q;
+    m.num_rows = num_rows;
     hipLaunchKernelGGL(mla_topk_kernel, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
-                       (const uint16_t*)logits, row_ends, N, K, block_table, max_pages, page_size, Q,
-                       num_rows, rows_out, valid_out);
+                       (const uint16_t*)logits, end, N, K, m, rows_out, valid_out);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status_t mla_expand_candidates(const int32_t* candidate_blocks, int rows, int K,
+                                   const int32_t* row_ks, const int32_t* row_ke,
+                                   int candidate_block_size, int sparse_block_kv,
+                                   int32_t* sparse_indices, int32_t* end, void* stream)
+{
+    if (rows < 0 || K < 1 || sparse_block_kv < 1 || candidate_block_size < 1)
+        return MLA_ERR_SHAPE;
+    const int ratio = candidate_block_size / sparse_block_kv;
+    if ((ratio != 1 && ratio != 2) || ratio * sparse_block_kv != candidate_block_size ||
+        (int64_t)K * ratio > EX_MAX)
+        return MLA_ERR_SHAPE;
+    if (rows == 0)
+        return MLA_OK;
+    if (!candidate_blocks || !row_ks || !row_ke || !sparse_indices || !end)
+        return MLA_ERR_NULL;
+    if (!tk_aligned(candidate_blocks, 4) || !tk_aligned(row_ks, 4) || !tk_aligned(row_ke, 4) ||
+        !tk_aligned(sparse_indices, 4) || !tk_aligned(end, 4))
+        return MLA_ERR_ALIGN;
+    const int S = K * ratio;
+    int npad = 64;
+    while (npad < S)
+        npad *= 2;
+    hipLaunchKernelGGL(mla_expand_kernel, dim3((unsigned)rows), dim3(EX_THREADS),
+                       (size_t)npad * sizeof(int32_t), (hipStream_t)stream, candidate_blocks, K,
+                       ratio, row_ks, row_ke, sparse_block_kv, npad, sparse_indices, end);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

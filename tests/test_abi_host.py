@@ -243,3 +243,31 @@ def test_binding_rejects_index_tensors_of_the_wrong_shape():
         sparse(i32(B, Q, 8), i32(B, Q), q=torch.zeros(B, Q, H, 512, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="kv"):
         sparse(i32(B, Q, 8), i32(B, Q), kv=torch.zeros(64, 512, dtype=torch.uint8))
+
+
+def test_candidate_expansion_and_sparse_topk_check_arguments_without_launching():
+    lib = mla._load()
+    ex = lambda cb=0x1000, rows=4, K=8, ks=0x2000, ke=0x3000, cbs=16, sbk=16, si=0x4000, end=0x5000: \
+        lib.mla_expand_candidates(cb, rows, K, ks, ke, cbs, sbk, si, end, None)  # noqa: E731
+    assert ex(rows=-1) == SHAPE
+    assert ex(K=0) == SHAPE
+    assert ex(sbk=0) == SHAPE
+    assert ex(cbs=48) == SHAPE                 # ratio 3
+    assert ex(cbs=24) == SHAPE                 # not a multiple
+    assert ex(cbs=8) == SHAPE                  # ratio 0
+    assert ex(K=16385) == SHAPE                # beyond the in-LDS sort
+    assert ex(K=8193, cbs=32) == SHAPE         # K * ratio beyond it
+    assert ex(rows=0, cb=None) == OK
+    assert ex(cb=None) == NULL
+    assert ex(end=None) == NULL
+    assert ex(si=0x4002) == ALIGN
+    cols = lambda S=4, sbk=8, si=0x6000, ks=0x7000: ctypes.byref(mla._SparseCols(si, S, sbk, ks))  # noqa: E731
+    tk = lambda c, N=32, R=2: lib.mla_topk_sparse_rows(0x1000, 0x2000, R, N, 8, c, None, 0, 1, 1, 0,  # noqa: E731
+                                                       0x3000, 0x4000, None)
+    assert tk(cols(S=3)) == SHAPE               # 3 blocks of 8 do not cover 32 columns
+    assert tk(cols(sbk=0)) == SHAPE
+    assert tk(cols(S=0)) == SHAPE
+    assert tk(cols(si=None)) == NULL
+    assert tk(cols(ks=None)) == NULL
+    assert tk(cols(ks=0x7002)) == ALIGN
+    assert tk(cols(), R=0) == OK

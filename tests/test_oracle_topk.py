@@ -143,3 +143,66 @@ def test_sparse_decode_over_remapped_positions_equals_the_dense_decode(seed):
                                 mode=mode, splits=1, chunk=128)
         assert np.array_equal(od, os_) and np.array_equal(ld, ls), mode
     assert np.all(np.isneginf(ld[0, :Q - 1]))
+
+
+# ---- candidate blocks -> sparse blocks -> positions -------------------------------------------------
+
+def _brute_positions(cands, ks, ke, cbs):
+    """Plain sets: the request-local positions the valid candidate blocks cover inside the row's
+    K range, ascending (candidate c covers positions [c * cbs, (c + 1) * cbs))."""
+    kv_len = max(ke - ks, 0)
+    cover = set()
+    for c in cands:
+        if c >= 0:
+            cover.update(p for p in range(c * cbs, (c + 1) * cbs) if p < kv_len)
+    return sorted(cover)
+
+
+@pytest.mark.parametrize("cbs,sbk", [(16, 16), (8, 8), (32, 16), (16, 8)])
+def test_expanded_columns_map_back_to_the_candidates_positions(cbs, sbk):
+    """For unique candidates, the sparse columns [0, end) map back (through the sparse block ids)
+    to exactly the positions the valid candidate blocks cover below kv_len, ascending -- whatever
+    the K range's start ks (the ids are anchored at ks // sbk, positions are request-local)."""
+    rng = np.random.default_rng(cbs * 100 + sbk)
+    rows, K = 40, 16
+    cand = np.full((rows, K), -1, np.int64)
+    ks = rng.integers(0, 500, rows)
+    ke = ks + rng.integers(0, 400, rows)
+    ke[3] = ks[3] - 5                          # an empty range
+    for r in range(rows):
+        n = int(rng.integers(0, K + 1))
+        cand[r, :n] = rng.permutation(40)[:n]  # unique, some past the range
+    si, end = topk.expand_candidates(cand.astype(np.int32), ks, ke, cbs, sbk)
+    width = si.shape[1] * sbk
+    assert si.shape == (rows, K * cbs // sbk)
+    for r in range(rows):
+        want = _brute_positions(cand[r].tolist(), int(ks[r]), int(ke[r]), cbs)
+        assert end[r] == len(want), r
+        got = topk.sparse_cols_to_positions(np.arange(end[r])[None, :], si[r:r + 1], ks[r:r + 1],
+                                            sbk, width)[0]
+        assert got.tolist() == want, r
+    assert end[3] == 0 and np.all(si[3] == ks[3] // sbk)
+
+
+def test_expanded_blocks_are_sorted_then_padded_with_the_last():
+    """The docstring's layout: the valid blocks ascending (anchored at ks // sbk), then the last
+    valid block repeated; ratio 2 makes candidate c into sparse blocks 2c and 2c + 1; candidates
+    outside the range (or -1) are dropped; repeats are kept (each copy counts)."""
+    cand = np.array([[5, 1, -1, 3], [2, 2, 0, -1], [9, -1, -1, -1]], np.int32)
+    si, end = topk.expand_candidates(cand, [0, 0, 0], [64, 64, 64], 8, 8)
+    # row 0: blocks 5, 1, 3 valid (max_block 8): 1 3 5 then 5
+    assert si[0].tolist() == [1, 3, 5, 5] and end[0] == 24
+    assert si[1].tolist() == [0, 2, 2, 2] and end[1] == 24      # the repeat counts
+    assert si[2].tolist() == [0, 0, 0, 0] and end[2] == 0       # 9 >= 8: nothing valid
+    si, end = topk.expand_candidates(cand[:1], [17], [17 + 40], 16, 8)
+    # ratio 2: 10, 11, 2, 3, 6, 7 (max_block 5, anchor 17 // 8 = 2): 2 3 then 4 4 ... anchored
+    assert si[0].tolist() == [4, 5, 5, 5, 5, 5, 5, 5]
+    assert end[0] == 8 + 8                                        # block 3 holds positions 24..31 < 40
+
+
+def test_sparse_columns_outside_the_logits_width_become_minus_one():
+    si = np.array([[4, 9, 2]], np.int32)
+    cols = np.array([[0, 7, 8, 23, 24, -1, 100]])
+    pos = topk.sparse_cols_to_positions(cols, si, [16], 8, width=24)
+    # ks // 8 = 2: block 4 -> positions 16..23, block 9 -> 56..63, block 2 -> 0..7
+    assert pos[0].tolist() == [16, 23, 56, 7, -1, -1, -1]
