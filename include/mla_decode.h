@@ -180,6 +180,28 @@ mla_status_t mla_decode_sparse_q(const void* q, const mla_kv_t* kv, const int32_
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_dense_q for callers that cannot allocate device memory or own a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same decode, with
+ * the split partials and arrival counters in a file-scope device array of
+ * MLA_NOALLOC_SCRATCH_BYTES held by each GPU the library runs on until the process ends (a fixed
+ * 64 KiB counter region, then the partials). The call allocates nothing. Arguments, plan, results
+ * and errors as for mla_decode_dense_q without the workspace; a plan whose workspace would exceed
+ * the array (more than 262144 query rows, or partials beyond MLA_NOALLOC_SCRATCH_BYTES - 64 KiB)
+ * returns MLA_ERR_WORKSPACE before anything is launched. Results are bit-identical to
+ * mla_decode_dense_q with the same plan. The first call on a device looks up the array's address
+ * (hipGetSymbolAddress, so make it outside graph capture) and zeroes the counter region with a
+ * fill kernel on `stream`; calls leave the counters zero again. Every call on a GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other threads) race and must
+ * be ordered by the caller.
+ */
+enum { MLA_NOALLOC_SCRATCH_BYTES = 80 << 20 };
+mla_status_t mla_decode_dense_q_noalloc(const void* q, const mla_kv_t* kv,
+                                        const int32_t* block_table, int max_pages,
+                                        const int32_t* seq_lens, float scale, int B, int Q, int H,
+                                        const mla_plan_t* plan, int precision, void* o, float* lse,
+                                        void* stream);
+
+/*
  * Combine of R partial decodes of the same query rows over disjoint parts of their keys: the
  * decode-context-parallel merge at a row's owner (vllm.models.kimi_k3.nvidia.specialized_decode.
  * cutedsl.dsa.attn_sparse, module docstring and "push": each rank decodes its share of the keys and

@@ -16,7 +16,7 @@ import torch
 
 from ._build import LIB
 
-__all__ = ["MlaError", "Plan", "dense", "sparse", "combine", "topk_rows",
+__all__ = ["MlaError", "Plan", "dense", "dense_noalloc", "sparse", "combine", "topk_rows",
            "expand_candidates", "topk_sparse_rows", "plan_dense", "plan_sparse", "workspace_bytes",
            "workspace_zero_bytes", "library_path", "UNIFORM", "BALANCED"]
 
@@ -86,6 +86,9 @@ def _load():
         lib.mla_decode_sparse_q.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32, i32,
                                             ctypes.POINTER(_Plan), i32, P, P, P, sz, P]
         lib.mla_decode_sparse_q.restype = i32
+        lib.mla_decode_dense_q_noalloc.argtypes = [P, ctypes.POINTER(_KV), P, i32, P, f32, i32, i32,
+                                                   i32, ctypes.POINTER(_Plan), i32, P, P, P]
+        lib.mla_decode_dense_q_noalloc.restype = i32
         lib.mla_combine.argtypes = [P, P, i32, ctypes.c_int64, P, P, P]
         lib.mla_combine.restype = i32
         lib.mla_topk_rows.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, ctypes.c_int64, P, P,
@@ -272,6 +275,31 @@ def dense(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens
         _ptr(q), ctypes.byref(kvs), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
         float(scale), B, Q, H, _plan_arg(pl), qp, _ptr(o), _ptr(lse), _ptr(workspace),
         0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream)))
+    return o, lse
+
+
+def dense_noalloc(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor,
+                  seq_lens: torch.Tensor, scale: float, k_scale: float, page_size: int, *,
+                  plan=None, o=None, lse=None, q_precision: str = "split",
+                  p_precision: str = "e4m3"):
+    """``dense`` through the C ABI's mla_decode_dense_q_noalloc: no workspace; the split partials
+    live in the library's per-device scratch array (for callers that cannot allocate; calls that
+    overlap on one GPU race). Same results as ``dense`` with the same plan."""
+    qp = _precision(q_precision, p_precision)
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, dev)
+    _check_tensor("kv", kv, torch.uint8, dev)
+    _check_tensor("block_table", block_table, torch.int32, dev)
+    _check_tensor("seq_lens", seq_lens, torch.int32, dev)
+    B, Q, H = _query_shape(q)
+    _dense_index_shapes(B, kv, block_table, seq_lens)
+    o, lse = _outputs(q, o, lse)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pl = None if plan is None else cap_plan(plan, p_precision)
+    kvs = _KV(kv.data_ptr(), kv.numel() // 576, int(page_size), float(k_scale))
+    _check(_load().mla_decode_dense_q_noalloc(
+        _ptr(q), ctypes.byref(kvs), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        float(scale), B, Q, H, _plan_arg(pl), qp, _ptr(o), _ptr(lse), ctypes.c_void_p(stream)))
     return o, lse
 
 

@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mla_decode.h"
 
 namespace {
@@ -1633,9 +1635,9 @@ mla_status_t common_checks(const void* q, const mla_kv_t* kv, int B, int Q, int 
     return MLA_OK;
 }
 
-mla_status_t finish_plan(const mla_plan_t* in, mla_plan_t chosen, int dense, int groups,
-                         int tiles_per_group, int64_t max_keys, int B, int Q, int H, void* ws,
-                         size_t ws_bytes, mla_plan_t* out)
+// The plan a call runs (the caller's, or the chooser's) if the kernels implement it.
+mla_status_t check_plan(const mla_plan_t* in, mla_plan_t chosen, int groups, int tiles_per_group,
+                        int64_t max_keys, mla_plan_t* out)
 {
     mla_plan_t pl = in ? *in : chosen;
     if (pl.splits < 1 || pl.splits > 4096)
@@ -1648,6 +1650,18 @@ mla_status_t finish_plan(const mla_plan_t* in, mla_plan_t chosen, int dense, int
         (groups > MAX_BALANCED_GROUPS ||
          (int64_t)groups * ((max_keys + BLK - 1) / BLK + ITEM_BLOCKS) >= INT32_MAX))
         return MLA_ERR_UNSUPPORTED;
+    *out = pl;
+    return MLA_OK;
+}
+
+mla_status_t finish_plan(const mla_plan_t* in, mla_plan_t chosen, int dense, int groups,
+                         int tiles_per_group, int64_t max_keys, int B, int Q, int H, void* ws,
+                         size_t ws_bytes, mla_plan_t* out)
+{
+    mla_plan_t pl;
+    const mla_status_t st = check_plan(in, chosen, groups, tiles_per_group, max_keys, &pl);
+    if (st != MLA_OK)
+        return st;
     if (pl.splits > 1) {
         const WsLayout w = ws_layout(dense, B, Q, H, pl);
         if (!ws || ws_bytes < w.total)
@@ -1666,6 +1680,120 @@ void fill_workspace(Params& p, int dense, int B, int Q, int H, const mla_plan_t&
     p.ws_cnt = p.S > 1 ? (uint32_t*)base : nullptr;
     p.ws_ml = p.S > 1 ? (float*)(base + w.cnt_bytes) : nullptr;
     p.ws_o = p.S > 1 ? (float*)(base + w.cnt_bytes + w.ml_bytes) : nullptr;
+}
+
+// The checks, plan and kernel parameters of a dense call (the workspace pointers stay null). A call
+// with B == 0 returns MLA_OK after the argument checks; there is nothing to launch.
+mla_status_t dense_setup(const void* q, const mla_kv_t* kv, const int32_t* block_table, int max_pages,
+                         const int32_t* seq_lens, float scale, int B, int Q, int H,
+                         const mla_plan_t* plan, int precision, void* o, float* lse, Params& p,
+                         mla_plan_t& pl)
+{
+    if (!precision_ok(precision) || ((precision & MLA_P_SPLIT) && plan && plan->tiles == 4))
+        return MLA_ERR_UNSUPPORTED;
+    mla_status_t st = common_checks(q, kv, B, Q, H, o, lse);
+    if (st != MLA_OK || B == 0)
+        return st;
+    if (max_pages < 1 || kv->page_size < 1 || (int64_t)max_pages * kv->page_size > INT32_MAX)
+        return MLA_ERR_SHAPE;
+    if (!block_table || !seq_lens)
+        return MLA_ERR_NULL;
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+        return MLA_ERR_ALIGN;
+    mla_plan_t chosen;
+    mla_plan_dense(B, Q, H, max_pages, kv->page_size, &chosen);
+    if ((precision & MLA_P_SPLIT) && chosen.tiles == 4)
+        chosen.tiles = 2;
+    st = check_plan(plan, chosen, B, Q * H / 16, (int64_t)max_pages * kv->page_size, &pl);
+    if (st != MLA_OK)
+        return st;
+    p.q = (const uint16_t*)q;
+    p.kv = (const uint8_t*)kv->data;
+    p.num_rows = kv->num_rows;
+    p.page_size = kv->page_size;
+    set_page_division(p, kv->page_size);
+    p.table = block_table;
+    p.max_pages = max_pages;
+    p.seq_lens = seq_lens;
+    p.scale_log2 = (float)((double)scale * (double)kv->k_scale * 1.4426950408889634);
+    p.k_scale = kv->k_scale;
+    p.Q = Q;
+    p.H = H;
+    p.S = pl.splits;
+    p.balanced = pl.mode == MLA_SPLIT_BALANCED;
+    p.groups = B;
+    p.rows_per_group = Q * H;
+    p.tilesets = Q * H / 16 / pl.tiles;
+    p.units = p.balanced ? pl.splits : B * pl.splits;
+    p.o = (uint16_t*)o;
+    p.lse = lse;
+    return MLA_OK;
+}
+
+// ---- the scratch of mla_decode_dense_q_noalloc -------------------------------------------------
+// One array per device, held until the process ends: the arrival counters in a fixed leading
+// region (no call's partials ever land there, and every call leaves its counters zero: the last
+// arriving workgroup of each tile resets its counter), then the FP32 partials of the call.
+constexpr size_t STATIC_BYTES = MLA_NOALLOC_SCRATCH_BYTES;
+constexpr size_t STATIC_CNT_BYTES = 64 << 10;   // 16384 counters: calls of up to 262144 query rows
+static_assert(STATIC_CNT_BYTES % ALIGN_WS == 0, "partials stay 256-byte aligned");
+
+static __device__ __align__(256) uint8_t scratch[STATIC_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+
+struct StaticScratch {
+    std::mutex mu;
+    uint8_t* ptr[MAX_DEVICES] = {};    // the array's device address, per device
+    bool cleared[MAX_DEVICES] = {};    // its counter region zeroed by a completed launch order
+};
+StaticScratch g_static;
+
+__global__ void zero_words(uint32_t* __restrict__ p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+// This device's scratch address (looked up once per device, with that device current) and, until
+// a launch outside graph capture has done it, a fill kernel that zeroes the counter region, on the
+// caller's stream ahead of the decode (a fill kernel rather than hipMemsetAsync, so that a
+// captured graph replays it correctly).
+mla_status_t static_scratch(hipStream_t stream, uint8_t** out)
+{
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return MLA_ERR_LAUNCH;
+    int dev = cur;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess)
+        return MLA_ERR_LAUNCH;
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return MLA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_static.mu);
+    if (!g_static.ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess)
+            return MLA_ERR_LAUNCH;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess)
+            return MLA_ERR_LAUNCH;
+        if (e != hipSuccess || !ptr)
+            return MLA_ERR_LAUNCH;
+        g_static.ptr[dev] = (uint8_t*)ptr;
+    }
+    if (!g_static.cleared[dev]) {
+        constexpr int words = (int)(STATIC_CNT_BYTES / 4);
+        hipLaunchKernelGGL(zero_words, dim3(words / 256), dim3(256), 0, stream,
+                           (uint32_t*)g_static.ptr[dev], words);
+        if (hipGetLastError() != hipSuccess)
+            return MLA_ERR_LAUNCH;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+            g_static.cleared[dev] = true;
+    }
+    *out = g_static.ptr[dev];
+    return MLA_OK;
 }
 
 }  // namespace
@@ -1726,48 +1854,50 @@ mla_status_t mla_decode_dense_q(const void* q, const mla_kv_t* kv, const int32_t
                                 int H, const mla_plan_t* plan, int precision, void* o, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (!precision_ok(precision) || ((precision & MLA_P_SPLIT) && plan && plan->tiles == 4))
-        return MLA_ERR_UNSUPPORTED;
-    mla_status_t st = common_checks(q, kv, B, Q, H, o, lse);
+    Params p{};
+    mla_plan_t pl;
+    mla_status_t st = dense_setup(q, kv, block_table, max_pages, seq_lens, scale, B, Q, H, plan,
+                                  precision, o, lse, p, pl);
     if (st != MLA_OK || B == 0)
         return st;
-    if (max_pages < 1 || kv->page_size < 1 || (int64_t)max_pages * kv->page_size > INT32_MAX)
-        return MLA_ERR_SHAPE;
-    if (!block_table || !seq_lens)
-        return MLA_ERR_NULL;
-    if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
-        return MLA_ERR_ALIGN;
-    mla_plan_t chosen;
-    mla_plan_dense(B, Q, H, max_pages, kv->page_size, &chosen);
-    if ((precision & MLA_P_SPLIT) && chosen.tiles == 4)
-        chosen.tiles = 2;
-    mla_plan_t pl;
-    st = finish_plan(plan, chosen, 1, B, Q * H / 16, (int64_t)max_pages * kv->page_size, B, Q, H,
-                     workspace, workspace_bytes, &pl);
-    if (st != MLA_OK)
-        return st;
-    Params p{};
-    p.q = (const uint16_t*)q;
-    p.kv = (const uint8_t*)kv->data;
-    p.num_rows = kv->num_rows;
-    p.page_size = kv->page_size;
-    set_page_division(p, kv->page_size);
-    p.table = block_table;
-    p.max_pages = max_pages;
-    p.seq_lens = seq_lens;
-    p.scale_log2 = (float)((double)scale * (double)kv->k_scale * 1.4426950408889634);
-    p.k_scale = kv->k_scale;
-    p.Q = Q;
-    p.H = H;
-    p.S = pl.splits;
-    p.balanced = pl.mode == MLA_SPLIT_BALANCED;
-    p.groups = B;
-    p.rows_per_group = Q * H;
-    p.tilesets = Q * H / 16 / pl.tiles;
-    p.units = p.balanced ? pl.splits : B * pl.splits;
-    p.o = (uint16_t*)o;
-    p.lse = lse;
+    if (pl.splits > 1) {
+        const WsLayout w = ws_layout(1, B, Q, H, pl);
+        if (!workspace || workspace_bytes < w.total)
+            return MLA_ERR_WORKSPACE;
+        if (!aligned(workspace, ALIGN_WS))
+            return MLA_ERR_ALIGN;
+    }
     fill_workspace(p, 1, B, Q, H, pl, workspace);
+    if (launch<true>(pl.tiles, precision, p, (hipStream_t)stream) != hipSuccess)
+        return MLA_ERR_LAUNCH;
+    return MLA_OK;
+}
+
+mla_status_t mla_decode_dense_q_noalloc(const void* q, const mla_kv_t* kv,
+                                        const int32_t* block_table, int max_pages,
+                                        const int32_t* seq_lens, float scale, int B, int Q, int H,
+                                        const mla_plan_t* plan, int precision, void* o, float* lse,
+                                        void* stream)
+{
+    Params p{};
+    mla_plan_t pl;
+    mla_status_t st = dense_setup(q, kv, block_table, max_pages, seq_lens, scale, B, Q, H, plan,
+                                  precision, o, lse, p, pl);
+    if (st != MLA_OK || B == 0)
+        return st;
+    if (pl.splits > 1) {
+        // the counters in the scratch's fixed counter region, the partials after it
+        const WsLayout w = ws_layout(1, B, Q, H, pl);
+        if (w.cnt_bytes > STATIC_CNT_BYTES || STATIC_CNT_BYTES + w.ml_bytes + w.o_bytes > STATIC_BYTES)
+            return MLA_ERR_WORKSPACE;
+        uint8_t* base = nullptr;
+        st = static_scratch((hipStream_t)stream, &base);
+        if (st != MLA_OK)
+            return st;
+        p.ws_cnt = (uint32_t*)base;
+        p.ws_ml = (float*)(base + STATIC_CNT_BYTES);
+        p.ws_o = (float*)(base + STATIC_CNT_BYTES + w.ml_bytes);
+    }
     if (launch<true>(pl.tiles, precision, p, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_LAUNCH;
     return MLA_OK;
