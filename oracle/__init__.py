@@ -14,8 +14,9 @@ With ``q_e4m3=True`` the logits use the E4M3 query (``q_e4m3_row``) in place of 
 With ``p_split=True`` (METHOD mode) each P meets V as E4M3 hi + lo (``p_used``) instead of E4M3.
 
 With ``allowance=True`` the front ends also return, per output element, how far o may move when a
-P that an FP32 implementation can only place to within 2^-13 (relative) of an E4M3 rounding
-midpoint is rounded the other way (METHOD mode; zeros otherwise).
+P that an FP8-MFMA / FP32 implementation can only place to within its per-key error bound (the
+derivation is at ``logit_error_bound`` in mla_oracle.c; ``logit_bound`` exposes its sum part) of an
+E4M3 rounding midpoint is rounded the other way (METHOD mode; zeros otherwise).
 """
 from __future__ import annotations
 
@@ -61,6 +62,8 @@ def _load():
         lib.mo_bf16_decode.restype = ctypes.c_double
         lib.mo_q_e4m3_bits.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         lib.mo_q_e4m3_bits.restype = None
+        lib.mo_logit_bound.argtypes = [P, P, i32, ctypes.c_double, ctypes.c_double]
+        lib.mo_logit_bound.restype = ctypes.c_double
         lib.mo_p_used.argtypes = [ctypes.c_double, ctypes.c_int]
         lib.mo_p_used.restype = ctypes.c_double
         lib.mo_q_shift.argtypes = [ctypes.c_void_p]
@@ -95,6 +98,14 @@ def p_used(p: float, split: bool) -> float:
     """The P that meets V in METHOD mode for a P of ``p`` (rounded to FP32 first): E4M3(p), or with
     ``split`` hi + lo, hi = E4M3(p), lo = E4M3(p - hi)."""
     return _load().mo_p_used(float(p), int(bool(split)))
+
+
+def logit_bound(q_bits_row, k_row, scale, k_scale, q_e4m3=False) -> float:
+    """The sum's part of the per-key logit error bound, in log2 units: rs (T + gamma(n) sum|p| +
+    sum|r K|) for one query row (uint16 bf16 bits [576]) and one cache row (uint8 [576])."""
+    q = _as(q_bits_row, np.uint16).reshape(576)
+    k = _as(k_row, np.uint8).reshape(576)
+    return _load().mo_logit_bound(_ptr(q), _ptr(k), int(bool(q_e4m3)), float(scale), float(k_scale))
 
 
 def _flags(mode, q_e4m3, p_split):
