@@ -26,11 +26,13 @@
 //          against rope | rope), each K fragment streamed from LDS through a register ring and used
 //          for both tiles; then the softmax inside the wave: block maximum (exchanged with the
 //          other key half through LDS), running max, P = 448 exp2(x - max) -> E4M3 into LDS, row
-//          sums of the unrounded P in a fixed order, rescale factor to LDS.
+//          sums of the unrounded P in a fixed order, rescale factor to LDS; then, in the time the
+//          PV waves still need before the next barrier, the row pointers and presence bits of
+//          block i + 2 for PV wave 4 + w (its 32 keys of the block), into that block's table.
 //   PV waves 4..7: wave 4 + c owns latent columns 128c..128c+127 of every tile. They run one block
 //          behind: after issuing the gather of block i + 1 (raw indices DMA'd into LDS three blocks
-//          ahead, row pointers one block ahead in a per-wave LDS table, 18 row DMAs per wave into
-//          the other LDS slot) they take O^T += V^T P^T of block i - 1, whose MFMAs share each SIMD's
+//          ahead, row pointers from the block's LDS table, 18 row DMAs per wave into the other LDS
+//          slot) they take O^T += V^T P^T of block i - 1, whose MFMAs share each SIMD's
 //          matrix pipe with the QK wave's MFMAs of block i; then they copy block i's V^T
 //          (ds_read_b64_tr_b8) into registers while its slot is valid, so two slots suffice.
 // Two barriers per block: B1 "block i landed; P and the rescale factors of block i - 1 published",
@@ -118,8 +120,8 @@ struct Smem {
     static constexpr int OFF_XMAX = OFF_FL + 4 * T * 16 * 4;   // float [4][T*16] block maxima per QK wave
     static constexpr int OFF_KMASK = OFF_XMAX + 4 * T * 16 * 4; // uint32 [4][4] key presence bits
     static constexpr int OFF_IDX = OFF_KMASK + 4 * 16;         // int32 [2][BLK] raw key indices
-    static constexpr int OFF_PTAB = OFF_IDX + 2 * BLK * 4;     // uint64 [4 waves][32] key pointers
-    static constexpr int OFF_MISC = OFF_PTAB + 4 * 32 * 8;     // int [4]
+    static constexpr int OFF_PTAB = OFF_IDX + 2 * BLK * 4;     // uint64 [2 block parities][4 waves][32] key pointers
+    static constexpr int OFF_MISC = OFF_PTAB + 2 * 4 * 32 * 8; // int [4]
     // E4M3 P lo [T][16][PPITCH] when P goes to PV as hi + lo (after everything else, so that the
     // other offsets do not depend on it)
     static constexpr int OFF_PLO = (OFF_MISC + 16 + 15) / 16 * 16;
@@ -806,6 +808,31 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     }
     float* xalpha = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
     float* xmax = reinterpret_cast<float*>(smem + L::OFF_XMAX);   // [4 waves][T * 16] block maxima
+    // The gather's pointer table of PV wave qw (keys 32 qw .. 32 qw + 31 of every block), built here
+    // two blocks ahead: the row pointer of each key (the zero row when absent) and the presence word.
+    const int32_t* idx_lds = reinterpret_cast<const int32_t*>(smem + L::OFF_IDX);
+    uint64_t* ptabs = reinterpret_cast<uint64_t*>(smem + L::OFF_PTAB) + 32 * qw;   // block parity b: + 128 b
+    uint64_t kv_base = (uint64_t)(uintptr_t)p.kv, zero_row = (uint64_t)(uintptr_t)g_zero_row;
+    uint64_t ibase = (uint64_t)(uintptr_t)(DENSE ? p.table + (int64_t)w.g * p.max_pages : p.rows + (int64_t)w.g * p.K);
+    int64_t nrows = p.num_rows;
+    uint32_t psz = (uint32_t)p.page_size, pmag = p.pg_magic;
+    int ps1 = p.pg_s1, ps2 = p.pg_s2;
+    asm volatile("" : "+s"(kv_base), "+s"(zero_row), "+s"(ibase), "+s"(nrows), "+s"(psz), "+s"(pmag), "+s"(ps1), "+s"(ps2));
+    auto pdiv = [&](uint32_t n) {
+        const uint32_t t = __umulhi(n, pmag);
+        return (t + ((n - t) >> ps1)) >> ps2;
+    };
+    auto key_ptrs_all = [&](int blk, int32_t idx) {
+        const int ln = lane_now();
+        const int kk = 32 * qw + (ln & 31);
+        const int64_t left = w.mine - (int64_t)blk * BLK;
+        const int64_t j = w.first + (int64_t)blk * BLK + kk;
+        const int64_t rd = DENSE ? (int64_t)idx * psz + (int64_t)((uint32_t)j - pdiv((uint32_t)j) * psz) : (int64_t)idx;
+        const bool ok = kk < left && idx >= 0 && rd < nrows;
+        const uint32_t word = (uint32_t)__ballot(ok);
+        *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 3) * 16 + 4 * qw) = word;
+        ptabs[128 * (blk & 1) + 16 * (ln & 1) + 8 * ((ln >> 4) & 1) + ((ln & 15) >> 1)] = ok ? kv_base + (uint64_t)rd * ROW : zero_row;
+    };
 
     // iteration i: QK and softmax of block i (the PV waves work on block i - 1)
     for (int i = 0; i <= w.nblk; i++) {
@@ -967,6 +994,9 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
                     xalpha[(qt0 + j) * 16 + (lo & 15)] = alpha[j];
             }
         }
+        // the pointers and presence word of block i + 2 (its indices landed before B1; the PV wave
+        // reads the other parity's table, block i + 1's, in this iteration)
+        key_ptrs_all(i + 2, idx_lds[(i & 1) * BLK + 32 * qw + (lane_now() & 31)]);
     }
 
     // ---- epilogue: m and the parts' sums to LDS; the row sum is ((p0 + p1) + p2) + p3 ----
@@ -1023,11 +1053,11 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
 
     // Gather: this wave moves keys 32 pw .. 32 pw + 31 (subtiles 2 pw, 2 pw + 1) of every block.
     // The raw indices (page ids or row ids) of block b arrive in LDS slot b % 2 by DMA three blocks
-    // ahead; two blocks ahead they become row pointers (the zero row when absent), which go to the
-    // wave's pointer table, and a presence word; one block ahead the wave issues the block's 18 row
-    // DMAs with each lane's source read from the table.
-    int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + L::OFF_IDX);
-    uint64_t* ptab = reinterpret_cast<uint64_t*>(smem + L::OFF_PTAB) + 32 * pw;   // the wave's pointer table
+    // ahead; two blocks ahead QK wave pw turns them into row pointers (the zero row when absent),
+    // which go to this wave's pointer table of block parity b % 2, and a presence word (this wave
+    // does it itself for blocks 0 and 1); one block ahead the wave issues the block's 18 row DMAs
+    // with each lane's source read from the table.
+    uint64_t* ptabs = reinterpret_cast<uint64_t*>(smem + L::OFF_PTAB) + 32 * pw;   // the wave's tables (+ 128 per block parity)
     // The gather's scalars (the same arithmetic as index_ptr and key_row), made opaque so that the
     // loop keeps them in scalar registers instead of reloading them from the kernel arguments
     uint64_t kv_base = (uint64_t)(uintptr_t)p.kv, zero_row = (uint64_t)(uintptr_t)g_zero_row;
@@ -1075,30 +1105,16 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
             *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 3) * 16 + 4 * pw) = word;
         const uint64_t ptr = row >= 0 ? kv_base + (uint64_t)row * ROW : zero_row;
         if (ln < 32)
-            ptab[16 * (ln & 1) + 8 * (ln >> 4) + ((ln & 15) >> 1)] = ptr;
+            ptabs[128 * (blk & 1) + 16 * (ln & 1) + 8 * (ln >> 4) + ((ln & 15) >> 1)] = ptr;
     };
-    // The same without branches, for the loop: lane l handles key 32 pw + l % 32 (idx: the raw
-    // index of that key in both halves), so lanes l and l + 32 store the same pointer to the same
-    // entry and every lane stores the presence word; for a block past the item every key is absent.
-    auto key_ptrs_all = [&](int blk, int32_t idx) {
-        const int ln = lane_now();
-        const int kk = 32 * pw + (ln & 31);
-        const int64_t left = w.mine - (int64_t)blk * BLK;
-        const int64_t j = w.first + (int64_t)blk * BLK + kk;
-        const int64_t rd = DENSE ? (int64_t)idx * psz + (int64_t)((uint32_t)j - pdiv((uint32_t)j) * psz) : (int64_t)idx;
-        const bool ok = kk < left && idx >= 0 && rd < nrows;
-        const uint32_t word = (uint32_t)__ballot(ok);
-        *reinterpret_cast<uint32_t*>(smem + L::OFF_KMASK + (blk & 3) * 16 + 4 * pw) = word;
-        ptab[16 * (ln & 1) + 8 * ((ln >> 4) & 1) + ((ln & 15) >> 1)] = ok ? kv_base + (uint64_t)rd * ROW : zero_row;
+    auto issue_half = [&](int blk, int h) {   // one subtile's 9 row DMAs, pointers from the table
+        const uint8_t* src[9];
+        subtile_sources(ptabs + 128 * (blk & 1), h, src);
+        issue_subtile(smem, src, blk, pw, h);
     };
-    auto issue_block = [&](int blk) {   // the block's 18 row DMAs, pointers from the table
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const uint8_t* src[9];
-            subtile_sources(ptab, h, src);
-            issue_subtile(smem, src, blk, pw, h);
-        }
-    };
+    // Sparse lists with four tiles issue a block's second subtile after B2 (the scattered rows'
+    // DMAs then spread over both phases; measured faster there, slower for paged KV)
+    constexpr bool SPLIT_ISSUE = !DENSE && T == 4;
     if (w.nblk > 0) {
         const int kk = 32 * pw + lane;
         int32_t idx0 = fi.i0, idx1 = fi.i1;
@@ -1111,7 +1127,8 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         if (w.nblk > 2)
             dma_indices(2);
         key_ptrs(0, idx0);
-        issue_block(0);
+        issue_half(0, 0);
+        issue_half(0, 1);
         if (w.nblk > 1)
             key_ptrs(1, idx1);   // the table's reads for block 0 precede these writes (one wave)
     }
@@ -1140,10 +1157,10 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
     // iteration i, before B2: P and the rescale factors of block i - 1 (published before B1) and
     // the row DMAs of block i + 1 (its slot's last readers finished before B1); after B2, in one
     // stretch of code: the PV of block i - 1 (its V^T is in registers), each V^T chunk replaced by
-    // block i's once its MFMAs are issued (the slot is refilled only after the next B1), and the
-    // pointers and presence word of block i + 2; then the indices of block i + 3. The table is read
-    // before B2 and rewritten after it; presence words and index slots alternate by block, away
-    // from the QK waves' reads. With four tiles every iteration runs the whole stretch (the first
+    // block i's once its MFMAs are issued (the slot is refilled only after the next B1); then the
+    // indices of block i + 3. Meanwhile the QK waves write the pointers and presence words of block
+    // i + 2 (the other parity's table; presence words and index slots alternate by block, away from
+    // the readers of the current ones). With four tiles every iteration runs the whole stretch (the first
     // multiplies zeros, the last reads an unused slot: registers are too few for a second copy of
     // the code); otherwise the first and last iterations take the same steps one by one.
     if (T == 4) {
@@ -1155,7 +1172,6 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         lds_sync();   // B1: block i landed; P of block i - 1 published
         // block i + 2's indices (landed with this iteration's vmcnt wait; any block's slot is
         // readable)
-        const int32_t idx2 = idx_lds[(i & 1) * BLK + 32 * pw + (lane_now() & 31)];
         float alpha[T];
         v8i pb[T];
         v8i pl[T];   // with PS: P lo
@@ -1176,8 +1192,11 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                 }
             }
         }
-        if (i + 1 < w.nblk)
-            issue_block(i + 1);
+        if (i + 1 < w.nblk) {
+            issue_half(i + 1, 0);
+            if (!SPLIT_ISSUE)
+                issue_half(i + 1, 1);
+        }
         if (i >= 1) {
 #pragma unroll
             for (int t = 0; t < T; t++) {
@@ -1191,8 +1210,9 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
         lds_sync();   // B2: the PV waves hold P of block i - 1; the QK waves' maxima are published
         // the lane's V^T base for block i's slot (recomputed here, not held across the loop)
         const int b = (i & 1) * SLOT + vbase(lane_now());
+        if (SPLIT_ISSUE && i + 1 < w.nblk)
+            issue_half(i + 1, 1);
         if (T == 4 || (i >= 1 && i < w.nblk)) {
-            key_ptrs_all(i + 2, idx2);
 #pragma unroll
             for (int c = 0; c < 8; c++) {
 #pragma unroll
@@ -1204,8 +1224,6 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
                 vt[c] = load_vt(i & 1, c, b + 128 * pw, b + 128 * (pw ^ 1));
             }
         } else {
-            if (i + 2 < w.nblk)
-                key_ptrs_all(i + 2, idx2);
             if (i >= 1) {
 #pragma unroll
                 for (int c = 0; c < 8; c++)
