@@ -94,7 +94,7 @@ def algorithmic(x, q_precision="split", p_precision="e4m3"):
 
 
 def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precision="split", x=None,
-                   p_precision="e4m3"):
+                   p_precision="e4m3", plan=None):
     import torch
 
     import paged_mla_decode_fp8_amd as mla
@@ -105,7 +105,7 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
         x = w.make()
     alg = algorithmic(x, q_precision, p_precision)
     dev = torch.device("cuda:0")
-    plan = mla.cap_plan(w.plan, p_precision)
+    plan = mla.cap_plan(w.plan if plan is None else plan, p_precision)
     kv_host = torch.from_numpy(x.kv)
     copies = max(1, min(8, math.ceil(min_rotation_bytes / max(1, x.kv.nbytes))))
     kvs = [kv_host.to(dev) for _ in range(copies)]
@@ -431,6 +431,9 @@ def main():
                     help="skip the E4M3-query and P hi + lo precision runs of every workload")
     ap.add_argument("--no-combine", action="store_true",
                     help="skip the decode-context-parallel combine and top-k producer runs")
+    ap.add_argument("--plan", default=None,
+                    help="splits,tiles,mode: run the named workloads with this launch plan instead of "
+                         "the chooser's (for counter runs; mode 0 uniform, 1 balanced)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (a known-size reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -461,8 +464,10 @@ def main():
     variants = {}
     p_variants = {}
     head_x = None
+    plan_override = tuple(int(v) for v in args.plan.split(",")) if args.plan else None
     for name in names:
-        res, x = bench_workload(name, args.steps, args.warmup)
+        res, x = bench_workload(name, args.steps, args.warmup,
+                                plan=plan_override if name in args.workloads.split(",") else None)
         results[name] = res
         print(f"[bench] {name}: {res['us_per_call']} us/call, {res['kv_GBps']} KV GB/s, "
               f"hbm {res['hbm_frac']:.3f}, mfma {res['mfma_frac']:.3f}", file=sys.stderr,
