@@ -33,11 +33,15 @@ typedef int v4i_c __attribute__((ext_vector_type(4)));
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ inline uint32_t to_bf16_rne(float f)
+typedef float v2f_c __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_c __attribute__((ext_vector_type(2)));
+
+// Two floats -> two BF16 codes (a in the low half), round to nearest even, with gfx950's packed
+// conversion (identical to (u + 0x7FFF + lsb) >> 16 on every non-NaN FP32 bit pattern, as checked
+// on MI355X).
+__device__ inline uint32_t pack_bf16_c(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_c{a, b}, v2bf_c));
 }
 
 __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(const uint16_t* __restrict__ o_parts,
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(const uint16_t*
     uint32_t outw[4];
 #pragma unroll
     for (int k = 0; k < 4; k++)
-        outw[k] = to_bf16_rne(acc[2 * k] / L) | (to_bf16_rne(acc[2 * k + 1] / L) << 16);
+        outw[k] = pack_bf16_c(acc[2 * k] / L, acc[2 * k + 1] / L);
     *reinterpret_cast<v4i_c*>(orow) = v4i_c{(int)outw[0], (int)outw[1], (int)outw[2], (int)outw[3]};
     if (lane == 0)
         lse[row] = M + logf(L);
