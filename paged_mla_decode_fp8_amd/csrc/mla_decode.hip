@@ -414,7 +414,7 @@ __device__ inline FirstIdx first_indices(const Params& p, int unit, int pw)
 // (and tile set). A group's real blocks go to the pieces their virtual positions fall in, so a
 // group is split where piece boundaries fall among its blocks; a piece walks the groups it
 // overlaps in order. An empty group belongs to the piece holding the start of its run.
-constexpr int ITEM_BLOCKS = 4;
+constexpr int ITEM_BLOCKS = 6;
 
 struct Span {
     int g_lo, g_hi;   // the piece's groups
@@ -1450,11 +1450,15 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    // a unit's tile sets share one XCD (blockIdx % 8)
+    // a unit's tile sets share one XCD (blockIdx % 8). With at most two tile sets, consecutive
+    // units do too (XCD x runs units x ceil(units / 8) ..): the pieces a split group spans mostly
+    // share one L2, which then holds the partials their merge reads (measured faster there, and
+    // no better with more tile sets, where the units go round the XCDs)
     const int bid = blockIdx.x;
     const int slotid = bid >> 3;
     const int ts = slotid % p.tilesets;
-    const int unit = (slotid / p.tilesets) * 8 + (bid & 7);
+    const int unit = p.tilesets <= 2 ? (bid & 7) * (int)(((int64_t)p.units + 7) / 8) + slotid / p.tilesets
+                                     : (slotid / p.tilesets) * 8 + (bid & 7);
     if (unit >= p.units)
         return;
     // uniform plan: the one item (group unit % groups); balanced plan: the piece's groups in order

@@ -78,7 +78,7 @@ def sample_rows(x, n_min=256, seed=0):
     return np.unique(np.concatenate(sel)).astype(np.int64)
 
 
-ITEM_BLOCKS = 4   # virtual blocks a key group's run starts with under the balanced plan
+ITEM_BLOCKS = 6   # virtual blocks a key group's run starts with under the balanced plan
 
 
 def balanced_cuts(x, pieces: int):
