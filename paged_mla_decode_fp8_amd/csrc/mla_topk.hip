@@ -23,8 +23,9 @@
 // fraction bits, so the LDS atomics of clustered values spread over many bins), then its low 4
 // bits among the keys in the chosen bin. The ordered output: per thread two 64-bit masks (columns
 // above / equal to the threshold), one workgroup prefix sum per span of their popcounts (wave
-// prefix by lane shuffles, then the 16 wave totals through LDS) and the set bits in ascending
-// order: thread order is column order, so the lists come out in column order without a sort.
+// prefix by DPP row shifts and the rows' totals, then the 16 wave totals through LDS) and the set
+// bits in ascending order: thread order is column order, so the lists come out in column order
+// without a sort. Lists of up to 8192 entries are built in LDS and remapped from there.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -46,10 +47,17 @@ constexpr int TK_LO_BITS = 16 - TK_HI_BITS;       // second digit: key bits 3..0
 constexpr int TK_BINS = 1 << TK_HI_BITS;
 constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the threshold search (4)
 
+constexpr int TK_LDS_K = 8192;   // lists of up to this many entries are built in LDS
+
 struct TkShared {
     uint32_t hist[TK_BINS + 1];   // the last counter takes the NaN / past-the-end columns (unused)
     int wave_tot[TK_WAVES];
     int sel[4];   // first-digit bin, keys above it, second-digit bin, keys above the threshold
+};
+
+template <bool STAGE>
+struct TkList {   // the selected columns: in LDS (K <= TK_LDS_K), else in the output row itself
+    int32_t col[STAGE ? TK_LDS_K : 1];
 };
 
 // the order key of a bf16 pattern (16 bits), or 0 for NaN (no valid key is 0: -inf maps to 0x7F)
@@ -60,17 +68,26 @@ __device__ inline uint32_t tk_key(uint32_t b)
     return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
 }
 
+// Inclusive prefix sum over the wave's lanes: within each row of 16 lanes by DPP row shifts of 1,
+// 2, 4 and 8 (a lane whose source lies before its row adds 0), then the rows' totals (lanes 15, 31
+// and 47, read into scalars) added to the rows after them. No LDS round trips.
+__device__ inline int tk_wave_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // Exclusive prefix sum over the workgroup's threads in thread order (and the total).
 __device__ inline int tk_scan(int x, TkShared& sh, int& total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int v = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(v, d, 64);
-        if (lane >= d)
-            v += y;
-    }
+    const int v = tk_wave_scan(x);
     if (lane == 63)
         sh.wave_tot[wave] = v;
     __syncthreads();
@@ -176,17 +193,20 @@ __device__ inline int32_t tk_remap(const TkRemap& m, int r, int col)
     return (page >= 0 && cr < m.num_rows) ? (int32_t)cr : -1;
 }
 
+template <bool STAGE>
 __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     const uint16_t* __restrict__ logits, const int32_t* __restrict__ row_ends, int N, int K,
     const TkRemap remap, int32_t* __restrict__ rows_out, int32_t* __restrict__ valid_out)
 {
     __shared__ TkShared sh;
+    __shared__ TkList<STAGE> lst;
     const int r = blockIdx.x;
     const int t = threadIdx.x;
     const uint16_t* row = logits + (int64_t)r * N;
     int n = row_ends[r];
     n = n < 0 ? 0 : (n > N ? N : n);
     int32_t* out = rows_out + (int64_t)r * K;
+    int32_t* list = STAGE ? lst.col : out;   // the ordered columns before the remap
     // a row of one span stays in registers for all three passes
     const bool resident = n <= TK_SPAN;
     uint32_t kw[TK_KW];
@@ -255,9 +275,9 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
         int pe = eq_run + tk_scan(__builtin_popcountll(eqm), sh, tot_eq);
         const int cbase = s0 + TK_OWN * t;
         for (; gtm; gtm &= gtm - 1)   // in column order
-            out[pg++] = cbase + __builtin_ctzll(gtm);
+            list[pg++] = cbase + __builtin_ctzll(gtm);
         for (; eqm && pe < eq_room; eqm &= eqm - 1)
-            out[c_gt + pe++] = cbase + __builtin_ctzll(eqm);
+            list[c_gt + pe++] = cbase + __builtin_ctzll(eqm);
         gt_run += tot_gt;
         eq_run += tot_eq;
     }
@@ -266,7 +286,7 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     // are the workgroup's, visible after the barrier)
     __syncthreads();
     for (int i = t; i < K; i += TK_THREADS)
-        out[i] = i < count ? tk_remap(remap, r, out[i]) : -1;
+        out[i] = i < count ? tk_remap(remap, r, list[i]) : -1;
     if (t == 0)
         valid_out[r] = count;
 }
@@ -395,8 +415,12 @@ mla_status_t mla_topk_sparse_rows(const void* logits, const int32_t* end, int R,
     m.page_size = page_size;
     m.Q = Q;
     m.num_rows = num_rows;
-    hipLaunchKernelGGL(mla_topk_kernel, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
-                       (const uint16_t*)logits, end, N, K, m, rows_out, valid_out);
+    if (K <= TK_LDS_K)
+        hipLaunchKernelGGL(mla_topk_kernel<true>, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
+                           (const uint16_t*)logits, end, N, K, m, rows_out, valid_out);
+    else
+        hipLaunchKernelGGL(mla_topk_kernel<false>, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
+                           (const uint16_t*)logits, end, N, K, m, rows_out, valid_out);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

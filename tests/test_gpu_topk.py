@@ -49,6 +49,8 @@ CASES = [
     (2, 65536, 2048, [65536, 50000], 2, 0.05),             # ties at the threshold in both spans
     (1, 131072, 2048, [131072], None, 0.01),               # four spans
     (2, 65544, 4096, [65544, 40001], 8, 0.0),              # K above 2048, a ragged last span
+    # K above the 8192 entries the kernel lists in LDS: the list is built in the output row
+    (3, 40000, 9000, [40000, 9000, 5000], 4, 0.02),
 ]
 
 
