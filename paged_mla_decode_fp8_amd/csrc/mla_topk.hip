@@ -50,7 +50,7 @@ constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the thre
 constexpr int TK_LDS_K = 8192;   // lists of up to this many entries are built in LDS
 
 struct TkShared {
-    uint32_t hist[TK_BINS + 1];   // the last counter takes the NaN / past-the-end columns (unused)
+    uint32_t hist[TK_BINS];
     int wave_tot[TK_WAVES];
     int sel[4];   // first-digit bin, keys above it, second-digit bin, keys above the threshold
 };
@@ -60,12 +60,12 @@ struct TkList {   // the selected columns: in LDS (K <= TK_LDS_K), else in the o
     int32_t col[STAGE ? TK_LDS_K : 1];
 };
 
-// the order key of a bf16 pattern (16 bits), or 0 for NaN (no valid key is 0: -inf maps to 0x7F)
+// the order key of a bf16 pattern (16 bits), or 0 for NaN (no valid key is 0: -inf maps to 0x7F);
+// branch-free: b ^ 0xFFFF (= ~b) for a set sign bit, b ^ 0x8000 (= b | 0x8000) for a clear one
 __device__ inline uint32_t tk_key(uint32_t b)
 {
-    if ((b & 0x7FFFu) > 0x7F80u)
-        return 0u;
-    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+    const uint32_t k = b ^ (0x8000u | (0x7FFFu * (b >> 15)));
+    return (b & 0x7FFFu) > 0x7F80u ? 0u : k;
 }
 
 // Inclusive prefix sum over the wave's lanes: within each row of 16 lanes by DPP row shifts of 1,
@@ -105,26 +105,43 @@ __device__ inline int tk_scan(int x, TkShared& sh, int& total)
 
 constexpr int TK_KW = TK_OWN / 2;                 // key registers per thread (two keys each)
 
-// The order keys of this thread's 32 columns of the span starting at s0: kw[i] holds column 2 i in
-// its low half and column 2 i + 1 in its high half (0 past the row end).
-__device__ inline void tk_keys(const uint16_t* row, int n, int s0, uint32_t (&kw)[TK_KW])
+// This thread's 32 columns of the span starting at s0 as raw bf16 vectors (1 <= lim <= N and
+// N % 8 == 0: a 16-byte vector that starts before lim lies wholly in the row). A vector starting
+// at or past column lim is read from the last vector that starts before lim instead (its keys are
+// masked later as past the row end), so that all four loads go out together without branches.
+__device__ inline void tk_load(const uint16_t* row, int lim, int s0, v4i_t (&raw)[TK_VEC])
 {
     const int c = s0 + TK_OWN * (int)threadIdx.x;
-    v4i_t raw[TK_VEC];
+    const int last = (lim - 1) & ~7;
 #pragma unroll
     for (int m = 0; m < TK_VEC; m++) {
-        raw[m] = v4i_t{0, 0, 0, 0};
-        if (c + 8 * m < n)   // n <= N and N % 8 == 0: the whole 16-byte vector lies in the row
-            raw[m] = *reinterpret_cast<const v4i_t*>(row + c + 8 * m);
+        const int cm = c + 8 * m < lim ? c + 8 * m : last;
+        raw[m] = *reinterpret_cast<const v4i_t*>(row + cm);
     }
+}
+
+// Their order keys: kw[i] holds column 2 i in its low half and column 2 i + 1 in its high half
+// (0 at and past the row end n).
+__device__ inline void tk_form(const v4i_t (&raw)[TK_VEC], int n, int s0, uint32_t (&kw)[TK_KW])
+{
+    const int c = s0 + TK_OWN * (int)threadIdx.x;
 #pragma unroll
     for (int i = 0; i < TK_KW; i++) {
         const uint32_t w = (uint32_t)raw[i >> 2][i & 3];
         const int col = c + 2 * i;
-        const uint32_t lo = col < n ? tk_key(w & 0xFFFFu) : 0u;
-        const uint32_t hi = col + 1 < n ? tk_key(w >> 16) : 0u;
-        kw[i] = lo | (hi << 16);
+        // 0xFFFF where the column lies before n (the sign of col - n), else 0: no branch
+        const uint32_t mlo = ((uint32_t)(col - n) >> 31) * 0xFFFFu;
+        const uint32_t mhi = ((uint32_t)(col + 1 - n) >> 31) * 0xFFFFu;
+        kw[i] = (tk_key(w & 0xFFFFu) & mlo) | ((tk_key(w >> 16) & mhi) << 16);
     }
+}
+
+// The order keys of this thread's 32 columns of the span starting at s0 (0 past the row end n).
+__device__ inline void tk_keys(const uint16_t* row, int n, int s0, uint32_t (&kw)[TK_KW])
+{
+    v4i_t raw[TK_VEC];
+    tk_load(row, n, s0, raw);
+    tk_form(raw, n, s0, kw);
 }
 
 // Of the nbins bins (counts in sh.hist), the highest bin b whose count together with the bins
@@ -193,7 +210,9 @@ __device__ inline int32_t tk_remap(const TkRemap& m, int r, int col)
     return (page >= 0 && cr < m.num_rows) ? (int32_t)cr : -1;
 }
 
-template <bool STAGE>
+// ONE: every row fits one span (N <= 32768), so the keys stay in registers for all three passes
+// and the span loops run once (a separate instantiation keeps the other case's code out).
+template <bool STAGE, bool ONE>
 __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     const uint16_t* __restrict__ logits, const int32_t* __restrict__ row_ends, int N, int K,
     const TkRemap remap, int32_t* __restrict__ rows_out, int32_t* __restrict__ valid_out)
@@ -203,27 +222,33 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     const int r = blockIdx.x;
     const int t = threadIdx.x;
     const uint16_t* row = logits + (int64_t)r * N;
+    // the first span's columns are requested together with the row end (bounded by the row's
+    // width, not its end), so the two loads share one round trip
+    v4i_t raw0[TK_VEC];
+    tk_load(row, N < TK_SPAN ? N : TK_SPAN, 0, raw0);
     int n = row_ends[r];
     n = n < 0 ? 0 : (n > N ? N : n);
     int32_t* out = rows_out + (int64_t)r * K;
     int32_t* list = STAGE ? lst.col : out;   // the ordered columns before the remap
     // a row of one span stays in registers for all three passes
-    const bool resident = n <= TK_SPAN;
+    const bool resident = ONE || n <= TK_SPAN;
+    const int s_end = ONE ? (n > 0 ? 1 : 0) : n;   // the span loops: s0 < s_end
     uint32_t kw[TK_KW];
     if (resident)
-        tk_keys(row, n, 0, kw);
+        tk_form(raw0, n, 0, kw);
 
     // pass 1: histogram of the candidates' first digits (NaN and columns past the end skipped)
-    for (int i = t; i <= TK_BINS; i += TK_THREADS)
+    for (int i = t; i < TK_BINS; i += TK_THREADS)
         sh.hist[i] = 0u;
     __syncthreads();
-    for (int s0 = 0; s0 < n; s0 += TK_SPAN) {
+    for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
         if (!resident)
             tk_keys(row, n, s0, kw);
 #pragma unroll
         for (int e = 0; e < TK_OWN; e++) {
             const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            atomicAdd(&sh.hist[k != 0u ? k >> TK_LO_BITS : TK_BINS], 1u);   // no branch
+            if (k != 0u)   // NaN and past the end: no atomic (one shared counter for them all
+                atomicAdd(&sh.hist[k >> TK_LO_BITS], 1u);   // would serialize short rows)
         }
     }
     __syncthreads();
@@ -238,7 +263,7 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
         if (t < (1 << TK_LO_BITS))
             sh.hist[t] = 0u;
         __syncthreads();
-        for (int s0 = 0; s0 < n; s0 += TK_SPAN) {
+        for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
             if (!resident)
                 tk_keys(row, n, s0, kw);
 #pragma unroll
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     // pass 3: the selected columns in order, remapped to cache rows
     int gt_run = 0, eq_run = 0;
     const int eq_room = K - c_gt;
-    for (int s0 = 0; s0 < n; s0 += TK_SPAN) {
+    for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
         if (!resident)
             tk_keys(row, n, s0, kw);
         // bit e of the masks: column e of this thread's part is above / equal to the threshold
@@ -285,8 +310,16 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     // the columns -> positions -> cache rows, each thread a strided share of the list (its writes
     // are the workgroup's, visible after the barrier)
     __syncthreads();
-    for (int i = t; i < K; i += TK_THREADS)
-        out[i] = i < count ? tk_remap(remap, r, list[i]) : -1;
+    // two entries per thread and round, both looked up before either is stored (the stores could
+    // alias the tables for all the compiler knows, which would serialize the lookups)
+    for (int i = t; i < K; i += 2 * TK_THREADS) {
+        const int i2 = i + TK_THREADS;
+        const int32_t a = i < count ? tk_remap(remap, r, list[i]) : -1;
+        const int32_t b = i2 < count ? tk_remap(remap, r, list[i2]) : -1;
+        out[i] = a;
+        if (i2 < K)
+            out[i2] = b;
+    }
     if (t == 0)
         valid_out[r] = count;
 }
@@ -415,12 +448,10 @@ mla_status_t mla_topk_sparse_rows(const void* logits, const int32_t* end, int R,
     m.page_size = page_size;
     m.Q = Q;
     m.num_rows = num_rows;
-    if (K <= TK_LDS_K)
-        hipLaunchKernelGGL(mla_topk_kernel<true>, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
-                           (const uint16_t*)logits, end, N, K, m, rows_out, valid_out);
-    else
-        hipLaunchKernelGGL(mla_topk_kernel<false>, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
-                           (const uint16_t*)logits, end, N, K, m, rows_out, valid_out);
+    auto kern = K <= TK_LDS_K ? (N <= TK_SPAN ? mla_topk_kernel<true, true> : mla_topk_kernel<true, false>)
+                              : (N <= TK_SPAN ? mla_topk_kernel<false, true> : mla_topk_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)R), dim3(TK_THREADS), 0, (hipStream_t)stream,
+                       (const uint16_t*)logits, end, N, K, m, rows_out, valid_out);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
