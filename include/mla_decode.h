@@ -60,11 +60,11 @@ typedef struct {
  * ceil(n / 128) blocks of 128.
  *   MLA_SPLIT_UNIFORM   the pages' rule: every group in `splits` = S parts, part s holding keys
  *                       [s*per, min(n, (s+1)*per)), per = ceil(n / S).
- *   MLA_SPLIT_BALANCED  every group counts as a run of 4 + (its blocks) virtual blocks, the 4
+ *   MLA_SPLIT_BALANCED  every group counts as a run of 6 + (its blocks) virtual blocks, the 6
  *                       standing for the fixed cost of one work item; the runs, concatenated in
  *                       group order (V virtual blocks), are cut into `splits` = P pieces of equal
  *                       size: piece p holds virtual blocks [floor(p*V/P), floor((p+1)*V/P)), and
- *                       block j of a group whose run starts at virtual block r sits at r + 4 + j.
+ *                       block j of a group whose run starts at virtual block r sits at r + 6 + j.
  *                       A group is split where a piece boundary falls among its blocks (so split
  *                       boundaries are multiples of 128 keys) and each piece goes to one
  *                       workgroup per tile set, which evens out ragged key counts. A group's
