@@ -266,6 +266,10 @@ def bench_combine(R, rows, steps, warmup, min_rotation_bytes=768 << 20, seed=0):
 TOPK_CASE = {"B": 32, "Q": 5, "N": 32768, "K": 2048, "page": 64}
 
 
+# Plans timed beside the chooser's: the latency checkpoint's configuration names the many-split
+# path and its FP32 LSE combine, which the chooser does not pick there (one split measures faster).
+SPLIT_PLANS = {"latency_sparse": [(2, 1, 0), (4, 1, 0)]}
+
 TOPK_CALLS_PER_GRAPH = 16
 
 
@@ -471,6 +475,7 @@ def main():
     results = {}
     variants = {}
     p_variants = {}
+    split_plans = {}
     head_x = None
     plan_override = tuple(int(v) for v in args.plan.split(",")) if args.plan else None
     for name in names:
@@ -493,6 +498,13 @@ def main():
             print(f"[bench] {name} (P hi + lo): {v['us_per_call']} us/call, {v['kv_GBps']} KV "
                   f"GB/s, hbm {v['hbm_frac']:.3f}, mfma {v['mfma_frac']:.3f}", file=sys.stderr,
                   flush=True)
+        for sp in SPLIT_PLANS.get(name, ()) if not args.no_variants else ():
+            v, _ = bench_workload(name, args.steps, args.warmup, x=x, plan=sp)
+            key = f"{sp[0]},{sp[1]},{'balanced' if sp[2] else 'uniform'}"
+            split_plans.setdefault(name, {})[key] = {k: v[k] for k in ("us_per_call", "kv_GBps", "hbm_frac",
+                                                                        "us_p10_p50_p90")}
+            print(f"[bench] {name} (plan {key}): {v['us_per_call']} us/call, {v['kv_GBps']} KV GB/s",
+                  file=sys.stderr, flush=True)
         if name == HEADLINE:
             head_x = x
         else:
@@ -553,6 +565,7 @@ def main():
         "workloads": results,
         "q_e4m3": variants or None,
         "p_split": p_variants or None,
+        "split_plans": split_plans or None,
         "dcp_combine": combine or None,
         "topk_producer": topk_res,
     }
