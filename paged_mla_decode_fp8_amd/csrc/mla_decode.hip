@@ -412,13 +412,16 @@ __device__ inline FirstIdx first_indices(const Params& p, int unit, int pw)
 // pipeline fill, output); the runs, concatenated in group order (V virtual blocks), are cut into
 // S pieces of equal size (piece q = [floor(q V / S), floor((q + 1) V / S))), one per workgroup
 // (and tile set). A group's real blocks go to the pieces their virtual positions fall in, so a
-// group is split where piece boundaries fall among its blocks; a piece walks the groups it
-// overlaps in order. An empty group belongs to the piece holding the start of its run.
+// group is split where piece boundaries fall among its blocks. A piece walks the groups it overlaps
+// from the last to the first: its part of the group it starts then comes in early, and the last
+// part of a split group to finish more often finds every other part counted in before its epilogue
+// (it then merges from LDS without storing its own partial). An empty group belongs to the piece
+// holding the start of its run.
 constexpr int ITEM_BLOCKS = 6;
 
 struct Span {
     int g_lo, g_hi;   // the piece's groups
-    int64_t pre_lo;   // virtual blocks before group g_lo
+    int64_t pre_hi;   // virtual blocks before group g_hi (0 when the piece holds no group)
     int64_t V;        // virtual blocks of all groups
 };
 
@@ -505,7 +508,7 @@ __device__ Span piece_span(const Params& p, uint8_t* smem, int piece, int tid, i
     Span sp;
     sp.g_lo = __builtin_amdgcn_readfirstlane(red[8]);
     sp.g_hi = __builtin_amdgcn_readfirstlane(red[9]) - 1;
-    sp.pre_lo = __builtin_amdgcn_readfirstlane(pre[sp.g_lo]);
+    sp.pre_hi = sp.g_hi >= sp.g_lo ? __builtin_amdgcn_readfirstlane(pre[sp.g_hi]) : 0;
     sp.V = V;
     __syncthreads();   // every wave has read the span before the slots fill
     return sp;
@@ -1419,8 +1422,10 @@ __device__ __forceinline__ void finish_item(const Params& p, uint8_t* smem, cons
     if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        misc[0] = (old == (uint32_t)(w.count - 1)) ? 1 : 0;
+        const bool last = old == (uint32_t)(w.count - 1);
+        if (last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the others' released partials
+        misc[0] = last ? 1 : 0;
     }
     __syncthreads();   // E3
     if (misc[0] == 0)
@@ -1461,7 +1466,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
                                      : (slotid / p.tilesets) * 8 + (bid & 7);
     if (unit >= p.units)
         return;
-    // uniform plan: the one item (group unit % groups); balanced plan: the piece's groups in order
+    // uniform plan: the one item (group unit % groups); balanced plan: the piece's groups, last first
     Span sp{unit % p.groups, unit % p.groups, 0, 0};
     if (p.balanced)
         sp = piece_span<DENSE>(p, smem, unit, tid, lane);
@@ -1475,8 +1480,8 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
     // on SIMD i % 4, so each SIMD pairs one QK wave with one PV wave. Each role walks the items
     // itself (same items, same barriers), so neither keeps the other's values live.
     if (wave < 4) {
-        int64_t pre = sp.pre_lo;
-        for (int g = sp.g_lo; g <= sp.g_hi; g++) {
+        int64_t pre = sp.pre_hi;
+        for (int g = sp.g_hi; g >= sp.g_lo; g--) {
             const Params& pi = fresh_params();
             int li = lane;   // lane-derived offsets are recomputed per item, not kept live
             asm volatile("" : "+v"(li));
@@ -1484,19 +1489,21 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             stage_q<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
             Work w;
             item(pi, g, pre, w);
-            pre += ITEM_BLOCKS + nblocks(w.n_grp);
+            if (g > sp.g_lo)
+                pre -= ITEM_BLOCKS + nblocks(group_keys<DENSE>(pi, g - 1));
             qk_role<T, DENSE, QE, PS>(pi, smem, w, wave, li);
             finish_item<T>(pi, smem, w, tid);
             __syncthreads();   // the next item reuses every LDS area
         }
     } else {
-        int64_t pre = sp.pre_lo;
-        for (int g = sp.g_lo; g <= sp.g_hi; g++) {
+        int64_t pre = sp.pre_hi;
+        for (int g = sp.g_hi; g >= sp.g_lo; g--) {
             const Params& pi = fresh_params();
             const FirstIdx fi = first_indices<DENSE>(pi, unit, wave - 4);
             Work w;
             item(pi, g, pre, w);
-            pre += ITEM_BLOCKS + nblocks(w.n_grp);
+            if (g > sp.g_lo)
+                pre -= ITEM_BLOCKS + nblocks(group_keys<DENSE>(pi, g - 1));
             v4f O[T][8];
 #pragma unroll
             for (int t = 0; t < T; t++)
