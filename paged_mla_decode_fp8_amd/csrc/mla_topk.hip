@@ -176,37 +176,89 @@ __device__ inline void tk_pick_bin(TkShared& sh, int nbins, int need, int slot)
     __syncthreads();
 }
 
+// Division of a 32-bit unsigned n by an invariant d (1 <= d < 2^31): with l = ceil(log2 d),
+// magic = floor(2^32 (2^l - d) / d) + 1, t = umulhi(n, magic), n / d = (t + ((n - t) >> s1)) >> s2,
+// s1 = min(l, 1), s2 = max(l - 1, 0) (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994, Figure 4.1). A few instructions instead of a division routine.
+struct TkDiv {
+    uint32_t magic;
+    int s1, s2;
+};
+
+TkDiv tk_division(int d)
+{
+    int l = 0;
+    while ((1ll << l) < d)
+        l++;
+    TkDiv v;
+    v.magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - (uint64_t)d)) / (uint64_t)d + 1);
+    v.s1 = l < 1 ? l : 1;
+    v.s2 = l - 1 > 0 ? l - 1 : 0;
+    return v;
+}
+
+__device__ inline uint32_t tk_div(const TkDiv& v, uint32_t n)
+{
+    const uint32_t t = __umulhi(n, v.magic);
+    return (t + ((n - t) >> v.s1)) >> v.s2;
+}
+
 // What the selected columns become: with `si` set, sparse logit columns -> request-local
 // positions (column j * sbk + o of row r scores position (si[r, j] - floor(ks[r] / sbk)) * sbk + o);
 // then, with `table` set, positions -> cache rows through request r / Q's page table.
 struct TkRemap {
     const int32_t* si;      // [R, S] sparse block ids backing the logit columns, or null
     int S, sbk;
+    TkDiv sdiv;             // division by sbk
     const int32_t* ks;      // [R] K range starts (the sparse ids' anchor)
     const int32_t* table;   // [R / Q, max_pages] page ids, or null
     int max_pages, page_size, Q;
+    TkDiv pdiv;             // division by page_size
     int64_t num_rows;
 };
 
 __device__ inline int64_t tk_floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
+// A row's share of the remap, looked up once per row: its sparse block ids and their anchor
+// floor(ks[r] / sbk), and its request's page table row.
+struct TkRowMap {
+    const int32_t* si_row;
+    int64_t anchor;
+    const int32_t* table_row;
+};
+
+__device__ inline TkRowMap tk_row_map(const TkRemap& m, int r)
+{
+    TkRowMap rm{nullptr, 0, nullptr};
+    if (m.si) {
+        rm.si_row = m.si + (int64_t)r * m.S;
+        rm.anchor = tk_floor_div(m.ks[r], m.sbk);
+    }
+    if (m.table)
+        rm.table_row = m.table + (int64_t)(r / m.Q) * m.max_pages;
+    return rm;
+}
+
 // One selected column -> the list entry (-1 where the position or its page or row is invalid).
-__device__ inline int32_t tk_remap(const TkRemap& m, int r, int col)
+// The column (in [0, N), N < 2^31) and the position (checked to lie in [0, 2^31)) divide as 32-bit
+// unsigned values.
+__device__ inline int32_t tk_remap(const TkRemap& m, const TkRowMap& rm, int col)
 {
     int64_t j = col;
     if (m.si) {
-        const int64_t blk = m.si[(int64_t)r * m.S + col / m.sbk];
-        j = (blk - tk_floor_div(m.ks[r], m.sbk)) * m.sbk + col % m.sbk;
+        const uint32_t q = tk_div(m.sdiv, (uint32_t)col);
+        const int64_t blk = rm.si_row[q];
+        j = (blk - rm.anchor) * m.sbk + (int64_t)((uint32_t)col - q * (uint32_t)m.sbk);
         if (j < 0 || j > 0x7FFFFFFF)
             return -1;
     }
     if (!m.table)
         return (int32_t)j;
-    const int64_t pgi = j / m.page_size;
-    if (pgi >= m.max_pages)
+    const uint32_t pgi = tk_div(m.pdiv, (uint32_t)j);
+    if ((int64_t)pgi >= m.max_pages)
         return -1;
-    const int64_t page = m.table[(int64_t)(r / m.Q) * m.max_pages + pgi];
-    const int64_t cr = page * m.page_size + j % m.page_size;
+    const int64_t page = rm.table_row[pgi];
+    const int64_t cr = page * m.page_size + (int64_t)((uint32_t)j - pgi * (uint32_t)m.page_size);
     return (page >= 0 && cr < m.num_rows) ? (int32_t)cr : -1;
 }
 
@@ -312,10 +364,11 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     __syncthreads();
     // two entries per thread and round, both looked up before either is stored (the stores could
     // alias the tables for all the compiler knows, which would serialize the lookups)
+    const TkRowMap rm = tk_row_map(remap, r);
     for (int i = t; i < K; i += 2 * TK_THREADS) {
         const int i2 = i + TK_THREADS;
-        const int32_t a = i < count ? tk_remap(remap, r, list[i]) : -1;
-        const int32_t b = i2 < count ? tk_remap(remap, r, list[i2]) : -1;
+        const int32_t a = i < count ? tk_remap(remap, rm, list[i]) : -1;
+        const int32_t b = i2 < count ? tk_remap(remap, rm, list[i2]) : -1;
         out[i] = a;
         if (i2 < K)
             out[i2] = b;
@@ -441,11 +494,14 @@ mla_status_t mla_topk_sparse_rows(const void* logits, const int32_t* end, int R,
         m.si = cols->sparse_indices;
         m.S = cols->S;
         m.sbk = cols->sparse_block_kv;
+        m.sdiv = tk_division(m.sbk);
         m.ks = cols->row_ks;
     }
     m.table = block_table;
     m.max_pages = max_pages;
     m.page_size = page_size;
+    if (block_table)
+        m.pdiv = tk_division(page_size);
     m.Q = Q;
     m.num_rows = num_rows;
     auto kern = K <= TK_LDS_K ? (N <= TK_SPAN ? mla_topk_kernel<true, true> : mla_topk_kernel<true, false>)

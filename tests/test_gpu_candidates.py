@@ -71,10 +71,12 @@ def _bits(R, N, seed, ties=None, nan=0.0):
     return b
 
 
-@pytest.mark.parametrize("sbk,K,ties", [(16, 64, None), (8, 300, 4), (16, 2048, 2)])
-def test_topk_over_sparse_columns_is_bit_exact(sbk, K, ties):
+@pytest.mark.parametrize("sbk,K,ties,page", [(16, 64, None, 64), (8, 300, 4, 64), (16, 2048, 2, 64),
+                                             (12, 500, 3, 48), (7, 1024, None, 37)])
+def test_topk_over_sparse_columns_is_bit_exact(sbk, K, ties, page):
     """Expanded candidates -> synthetic sparse logits (columns past each row's valid count poisoned
     with +inf) -> the top-k remapped to positions, then through a page table to cache rows."""
+    say("sparse topk", sbk, K, page)
     rng = np.random.default_rng(sbk * 1000 + K)
     R, Kc, cbs = 6, 512, 2 * sbk
     cand = _cands(R, Kc, 4000, rng, fill=int(Kc * 0.8))
@@ -91,8 +93,9 @@ def test_topk_over_sparse_columns_is_bit_exact(sbk, K, ties):
     ref, ref_cnt = otopk.sparse_topk(bits, end, K, si, ks, sbk)
     assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
     assert np.array_equal(pos.cpu().numpy(), ref)
-    # through a page table (two query rows per request, page 64)
-    Q, page = 2, 64
+    # through a page table (two query rows per request); block and page sizes that are not powers
+    # of two divide by their precomputed reciprocals
+    Q = 2
     pages = int(ke.max()) // page + 1
     table = rng.permutation((R // Q) * pages).astype(np.int32).reshape(R // Q, pages)
     table[0, 5] = -1

@@ -69,9 +69,13 @@ def test_topk_select_is_bit_exact(case):
     assert np.array_equal(rows, ref)
 
 
-def test_topk_remap_through_a_page_table_is_bit_exact():
-    B, Q, N, K, page = 3, 2, 2048, 128, 64
-    rng = np.random.default_rng(5)
+@pytest.mark.parametrize("page", [64, 48, 37, 1])
+def test_topk_remap_through_a_page_table_is_bit_exact(page):
+    """Page sizes that are not powers of two divide by their precomputed reciprocal; with 48 and
+    37 the table's pages end before N, so the last positions fall past max_pages (-1)."""
+    B, Q, N, K = 3, 2, 2048, 128
+    say("topk remap", page)
+    rng = np.random.default_rng(5 + page)
     pages = N // page
     table = rng.permutation(B * pages).astype(np.int32).reshape(B, pages)
     table[2, -3:] = 2 ** 31 - 1
