@@ -94,7 +94,7 @@ def algorithmic(x, q_precision="split", p_precision="e4m3"):
 
 
 def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precision="split", x=None,
-                   p_precision="e4m3", plan=None):
+                   p_precision="e4m3", plan=None, min_timed_ms=0.0):
     import torch
 
     import paged_mla_decode_fp8_amd as mla
@@ -154,8 +154,11 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
     if not torch.equal(o.view(torch.int16), o_eager.view(torch.int16)):
         raise RuntimeError(f"{name}: graph replay output differs from the eager call")
     # the timed calls: reps replays back to back, an event between every two (the spread of the
-    # time per call comes from the same replays as its mean)
+    # time per call comes from the same replays as its mean); with min_timed_ms, at least that long
+    # a timed region by the eager estimate (short workloads: enough replays for a steady figure)
     reps = max(1, steps // copies)
+    if min_timed_ms > 0.0:
+        reps = max(reps, math.ceil(min_timed_ms / max(ms_eager * copies, 1e-3)))
     stream = torch.cuda.current_stream(dev)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
@@ -192,6 +195,7 @@ def bench_workload(name, steps, warmup, min_rotation_bytes=768 << 20, q_precisio
         "us_per_call_hot": round(ms_hot * 1e3, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per_call, q)) * 1e3, 3) for q in (10, 50, 90)],
         "spread_samples": f"{reps} graph replays of {copies} call(s) each (one per KV copy)",
+        "timed_calls": reps * copies,
         "kv_bytes": alg["kv_bytes"],
         "alg_bytes": alg["bytes"],
         "alg_flops": alg["flops"],
@@ -269,6 +273,10 @@ TOPK_CASE = {"B": 32, "Q": 5, "N": 32768, "K": 2048, "page": 64}
 # Plans timed beside the chooser's: the latency checkpoint's configuration names the many-split
 # path and its FP32 LSE combine, which the chooser does not pick there (one split measures faster).
 SPLIT_PLANS = {"latency_sparse": [(2, 1, 0), (4, 1, 0)]}
+
+# The headline times exactly --steps calls; the other workloads time at least this long (by the
+# eager estimate), so that the short ones average over enough replays for a steady figure.
+MIN_TIMED_MS = 10.0
 
 TOPK_CALLS_PER_GRAPH = 16
 
@@ -479,30 +487,31 @@ def main():
     head_x = None
     plan_override = tuple(int(v) for v in args.plan.split(",")) if args.plan else None
     for name in names:
-        res, x = bench_workload(name, args.steps, args.warmup,
+        mt = 0.0 if name == HEADLINE else MIN_TIMED_MS
+        res, x = bench_workload(name, args.steps, args.warmup, min_timed_ms=mt,
                                 plan=plan_override if name in args.workloads.split(",") else None)
         results[name] = res
         print(f"[bench] {name}: {res['us_per_call']} us/call, {res['kv_GBps']} KV GB/s, "
               f"hbm {res['hbm_frac']:.3f}, mfma {res['mfma_frac']:.3f}", file=sys.stderr,
               flush=True)
         if not args.no_variants:
-            v, _ = bench_workload(name, args.steps, args.warmup, q_precision="e4m3", x=x)
+            v, _ = bench_workload(name, args.steps, args.warmup, q_precision="e4m3", x=x, min_timed_ms=mt)
             variants[name] = {k: v[k] for k in ("us_per_call", "kv_GBps", "hbm_frac", "mfma_frac",
-                                                "alg_flops", "mfma_floor_us")}
+                                                "alg_flops", "mfma_floor_us", "timed_calls")}
             print(f"[bench] {name} (E4M3 query): {v['us_per_call']} us/call, {v['kv_GBps']} KV "
                   f"GB/s, hbm {v['hbm_frac']:.3f}, mfma {v['mfma_frac']:.3f}", file=sys.stderr,
                   flush=True)
-            v, _ = bench_workload(name, args.steps, args.warmup, p_precision="split", x=x)
+            v, _ = bench_workload(name, args.steps, args.warmup, p_precision="split", x=x, min_timed_ms=mt)
             p_variants[name] = {k: v[k] for k in ("us_per_call", "kv_GBps", "hbm_frac", "mfma_frac",
-                                                  "alg_flops", "mfma_floor_us", "plan")}
+                                                  "alg_flops", "mfma_floor_us", "plan", "timed_calls")}
             print(f"[bench] {name} (P hi + lo): {v['us_per_call']} us/call, {v['kv_GBps']} KV "
                   f"GB/s, hbm {v['hbm_frac']:.3f}, mfma {v['mfma_frac']:.3f}", file=sys.stderr,
                   flush=True)
         for sp in SPLIT_PLANS.get(name, ()) if not args.no_variants else ():
-            v, _ = bench_workload(name, args.steps, args.warmup, x=x, plan=sp)
+            v, _ = bench_workload(name, args.steps, args.warmup, x=x, plan=sp, min_timed_ms=mt)
             key = f"{sp[0]},{sp[1]},{'balanced' if sp[2] else 'uniform'}"
             split_plans.setdefault(name, {})[key] = {k: v[k] for k in ("us_per_call", "kv_GBps", "hbm_frac",
-                                                                        "us_p10_p50_p90")}
+                                                                        "us_p10_p50_p90", "timed_calls")}
             print(f"[bench] {name} (plan {key}): {v['us_per_call']} us/call, {v['kv_GBps']} KV GB/s",
                   file=sys.stderr, flush=True)
         if name == HEADLINE:
