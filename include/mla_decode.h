@@ -115,7 +115,7 @@ size_t mla_workspace_zero_bytes(int dense, int B, int Q, int H, const mla_plan_t
  *   seq_lens     device int32 [B]: keys of request b, clamped to [0, max_pages * page_size].
  *   scale        softmax scale multiplying q . K (k_scale is applied on top).
  *   plan         NULL for mla_plan_dense()'s choice.
- *   o            device bf16 [B, Q, H, 512] (8-byte aligned): softmax-weighted latent, RNE.
+ *   o            device bf16 [B, Q, H, 512] (16-byte aligned): softmax-weighted latent, RNE.
  *   lse          device float [B, Q, H]: natural-log sum of exp(scale * q . K) over the row's keys.
  *   Position i sees keys j < seq_len - Q + i + 1; a row with none gets o = +0 and lse = -inf.
  *   workspace    device, >= mla_workspace_bytes(1, B, Q, H, plan) bytes, 256-byte aligned (may

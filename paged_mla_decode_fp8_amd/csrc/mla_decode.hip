@@ -363,14 +363,15 @@ __device__ inline int64_t group_keys(const Params& p, int g)
 __device__ inline int64_t nblocks(int64_t n) { return (n + BLK - 1) / BLK; }
 
 // Uniform plan (the pages' rule): unit = (split s, group g); the split holds keys
-// [s per, min(n, (s + 1) per)) with per = ceil(n / S).
+// [s per, min(n, (s + 1) per)) with per = ceil(n / S). n_known: the group's key count when the
+// caller has already loaded it (else -1).
 template <bool DENSE>
-__device__ inline void decode_uniform(const Params& p, int unit, int ts, Work& w)
+__device__ inline void decode_uniform(const Params& p, int unit, int ts, Work& w, int64_t n_known = -1)
 {
     const int s = unit / p.groups;
     w.g = unit % p.groups;
     w.ts = ts;
-    w.n_grp = group_keys<DENSE>(p, w.g);
+    w.n_grp = n_known >= 0 ? n_known : group_keys<DENSE>(p, w.g);
     const int64_t per = (w.n_grp + p.S - 1) / p.S;
     w.first = (int64_t)s * per < w.n_grp ? (int64_t)s * per : w.n_grp;
     w.mine = (w.n_grp - w.first) < per ? (w.n_grp - w.first) : per;
@@ -381,29 +382,39 @@ __device__ inline void decode_uniform(const Params& p, int unit, int ts, Work& w
     w.row_base = (int64_t)w.g * p.rows_per_group;
 }
 
-// Raw indices of the first two blocks, requested before the key count is known: for split 0 of
-// a uniform plan the keys start at 0, so lanes 0..31 of PV wave pw load those of keys 32 pw + lane
-// and 128 + 32 pw + lane that lie within the list's capacity (their count mask comes later).
+// Raw indices of the first two blocks and the group's key count, requested together: for split 0
+// of a uniform plan the keys start at 0, so lanes 0..31 of PV wave pw load those of keys 32 pw + lane
+// and 128 + 32 pw + lane that lie within the list's capacity (their count mask comes later). The
+// parameters these loads need (and the first parameter line, which the gather reads next) are read
+// in one batch, so that the loads wait for one round trip to the parameters instead of several.
 struct FirstIdx {
     int32_t i0, i1;
     bool ok;
+    int64_t n;   // the group's key count (clamped as group_keys does), or -1
 };
 
 template <bool DENSE>
 __device__ inline FirstIdx first_indices(const Params& p, int unit, int pw)
 {
-    FirstIdx f{-1, -1, false};
-    if (p.balanced || unit >= p.groups)
+    FirstIdx f{-1, -1, false, -1};
+    const int bal = p.balanced, groups = p.groups;
+    const int64_t cap = DENSE ? (int64_t)p.max_pages * p.page_size : (int64_t)p.K;
+    const int32_t* cnt = DENSE ? p.seq_lens : p.valid;
+    const int32_t* ibase = DENSE ? p.table : p.rows;
+    const uint8_t* kv = p.kv;
+    asm volatile("" ::"s"(bal), "s"(groups), "s"(cap), "s"(cnt), "s"(ibase), "s"(kv));
+    if (bal || unit >= groups)
         return f;
     f.ok = true;
+    const int g = unit;
     const int ln = lane_now();
     const int kk = 32 * pw + ln;
-    const int g = unit;
-    const int64_t cap = DENSE ? (int64_t)p.max_pages * p.page_size : (int64_t)p.K;
     if (ln < 32 && kk < cap)
         f.i0 = *index_ptr<DENSE>(p, g, kk);
     if (ln < 32 && BLK + kk < cap)
         f.i1 = *index_ptr<DENSE>(p, g, BLK + kk);
+    const int64_t n = cnt[g];   // after the index loads, so that its wait covers them too
+    f.n = n < 0 ? 0 : (n > cap ? cap : n);
     return f;
 }
 
@@ -1258,15 +1269,25 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
             const float lt = ((fl[r] + fl[T * 16 + r]) + fl[2 * T * 16 + r]) + fl[3 * T * 16 + r];
             const float rl = 1.f / lt;   // one division per row
             const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
+            // Column blocks c and c + 1 in pairs: lane (n16, grp) holds columns 4 grp .. 4 grp + 3 of
+            // both. One 16-lane row swap (odd rows of the first operand with even rows of the
+            // second) leaves an even-grp lane with columns 8 (grp / 2) .. + 7 of block c (its own
+            // four, then its neighbour's) and an odd-grp lane with the same columns of block c + 1,
+            // so that every lane writes 16 contiguous bytes: half the store instructions.
 #pragma unroll
-            for (int c = 0; c < 8; c++) {
-                const int col = 128 * pw + 16 * c + 4 * grp;
-                uint32_t w01 = 0, w23 = 0;
+            for (int c = 0; c < 8; c += 2) {
+                uint32_t a01 = 0, a23 = 0, b01 = 0, b23 = 0;
                 if (lt > 0.f) {
-                    w01 = pack_bf16(div_by(O[t][c][0], lt, rl) * p.k_scale, div_by(O[t][c][1], lt, rl) * p.k_scale);
-                    w23 = pack_bf16(div_by(O[t][c][2], lt, rl) * p.k_scale, div_by(O[t][c][3], lt, rl) * p.k_scale);
+                    a01 = pack_bf16(div_by(O[t][c][0], lt, rl) * p.k_scale, div_by(O[t][c][1], lt, rl) * p.k_scale);
+                    a23 = pack_bf16(div_by(O[t][c][2], lt, rl) * p.k_scale, div_by(O[t][c][3], lt, rl) * p.k_scale);
+                    b01 = pack_bf16(div_by(O[t][c + 1][0], lt, rl) * p.k_scale, div_by(O[t][c + 1][1], lt, rl) * p.k_scale);
+                    b23 = pack_bf16(div_by(O[t][c + 1][2], lt, rl) * p.k_scale, div_by(O[t][c + 1][3], lt, rl) * p.k_scale);
                 }
-                *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) = v2i{(int)w01, (int)w23};
+                const auto x01 = __builtin_amdgcn_permlane16_swap(a01, b01, false, false);
+                const auto x23 = __builtin_amdgcn_permlane16_swap(a23, b23, false, false);
+                const int col = 128 * pw + 16 * (c + (grp & 1)) + 8 * (grp >> 1);
+                *reinterpret_cast<v4i*>(p.o + orow * LATENT + col) =
+                    v4i{(int)x01[0], (int)x23[0], (int)x01[1], (int)x23[1]};
             }
         }
         return;
@@ -1286,8 +1307,9 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
 }
 
 // The last arriving item of a (group, tile set) merges the group's FP32 partials in split order.
-// Thread (wave c, lane) owns column block c of every column quarter and tile for rows
-// 16 t + lane % 16: per contributor it weighs T rows and issues 4 T contiguous loads at once.
+// Thread (wave c, lane) owns the four adjacent column blocks 4 (c % 2) .. + 3 of column quarter
+// c / 2 of every tile, for rows 16 t + lane % 16: per contributor it weighs T rows and issues 4 T
+// contiguous loads at once; adjacent blocks pair up for 16-byte output stores.
 // own_lds: this item's own partial is in LDS, in the workspace's layout at the start of the KV
 // slots (O, then (m, l) at own_ml_offset<T>()), rather than in the workspace; the loads go through
 // generic pointers so that one code path reads both.
@@ -1318,10 +1340,10 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid, const uint
         for (int t = 0; t < T; t++)
             pt.ml[t] = *reinterpret_cast<const v2f*>(mlb + (16 * t + n16) * 2);
 #pragma unroll
-        for (int pw = 0; pw < 4; pw++)
+        for (int k = 0; k < 4; k++)
 #pragma unroll
             for (int t = 0; t < T; t++)
-                pt.x[pw][t] = *reinterpret_cast<const v4f*>(ob + partial_o_offset<T>(0, pw, t, c, lane));
+                pt.x[k][t] = *reinterpret_cast<const v4f*>(ob + partial_o_offset<T>(0, c >> 1, t, 4 * (c & 1) + k, lane));
     };
     // One round trip for the common case: the first two contributors' partials and every
     // contributor's maximum are requested before any of them is used.
@@ -1378,19 +1400,26 @@ __device__ void merge_splits(const Params& p, const Work& w, int tid, const uint
 #pragma unroll
     for (int t = 0; t < T; t++) {
         const int64_t orow = w.row_base + 16 * (w.ts * T + t) + n16;
+        // blocks k and k + 1: the same 16-lane row swap as the single-split epilogue leaves each lane
+        // 8 contiguous columns (even grp: block k, odd grp: block k + 1)
 #pragma unroll
-        for (int pw = 0; pw < 4; pw++) {
-            uint32_t w01 = 0, w23 = 0;
+        for (int k = 0; k < 4; k += 2) {
+            uint32_t w[2][2] = {{0, 0}, {0, 0}};
             if (total[t] > 0.f) {
                 const float rt = 1.f / total[t];
-                float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; e++) v[e] = div_by(acc[pw][t][e], total[t], rt) * p.k_scale;
-                w01 = pack_bf16(v[0], v[1]);
-                w23 = pack_bf16(v[2], v[3]);
+                for (int h = 0; h < 2; h++) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v[e] = div_by(acc[k + h][t][e], total[t], rt) * p.k_scale;
+                    w[h][0] = pack_bf16(v[0], v[1]);
+                    w[h][1] = pack_bf16(v[2], v[3]);
+                }
             }
-            const int col = 128 * pw + 16 * c + 4 * grp;
-            *reinterpret_cast<v2i*>(p.o + orow * LATENT + col) = v2i{(int)w01, (int)w23};
+            const auto x01 = __builtin_amdgcn_permlane16_swap(w[0][0], w[1][0], false, false);
+            const auto x23 = __builtin_amdgcn_permlane16_swap(w[0][1], w[1][1], false, false);
+            const int col = 128 * (c >> 1) + 16 * (4 * (c & 1) + k + (grp & 1)) + 8 * (grp >> 1);
+            *reinterpret_cast<v4i*>(p.o + orow * LATENT + col) = v4i{(int)x01[0], (int)x23[0], (int)x01[1], (int)x23[1]};
         }
         if (c == 0 && grp == 0)
             p.lse[orow] = total[t] > 0.f ? (top[t] - LOG2_ANCHOR + log2f(total[t])) * LN2 : neg_inf;
@@ -1461,6 +1490,12 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
     // no better with more tile sets, where the units go round the XCDs)
     const int bid = blockIdx.x;
     const int slotid = bid >> 3;
+    {
+        // both 64-byte lines of parameters the first steps read, fetched in one round trip
+        const void* line0 = p.kv;
+        const int line1 = p.tilesets;
+        asm volatile("" ::"s"(line0), "s"(line1));
+    }
     const int ts = slotid % p.tilesets;
     const int unit = p.tilesets <= 2 ? (bid & 7) * (int)(((int64_t)p.units + 7) / 8) + slotid / p.tilesets
                                      : (slotid / p.tilesets) * 8 + (bid & 7);
@@ -1470,11 +1505,11 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
     Span sp{unit % p.groups, unit % p.groups, 0, 0};
     if (p.balanced)
         sp = piece_span<DENSE>(p, smem, unit, tid, lane);
-    auto item = [&](const Params& pi, int g, int64_t pre, Work& w) {
+    auto item = [&](const Params& pi, int g, int64_t pre, Work& w, int64_t n_known = -1) {
         if (pi.balanced)
             balanced_item<DENSE>(pi, unit, ts, g, pre, sp, w);
         else
-            decode_uniform<DENSE>(pi, unit, ts, w);
+            decode_uniform<DENSE>(pi, unit, ts, w, n_known);
     };
     // waves 0..3: QK (tile = wave); waves 4..7: gather + PV (columns 128 (wave - 4) ..); wave i runs
     // on SIMD i % 4, so each SIMD pairs one QK wave with one PV wave. Each role walks the items
@@ -1501,7 +1536,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             const Params& pi = fresh_params();
             const FirstIdx fi = first_indices<DENSE>(pi, unit, wave - 4);
             Work w;
-            item(pi, g, pre, w);
+            item(pi, g, pre, w, fi.n);
             if (g > sp.g_lo)
                 pre -= ITEM_BLOCKS + nblocks(group_keys<DENSE>(pi, g - 1));
             v4f O[T][8];
@@ -1659,7 +1694,7 @@ mla_status_t common_checks(const void* q, const mla_kv_t* kv, int B, int Q, int 
         return MLA_ERR_NULL;
     if (kv->num_rows < 0)
         return MLA_ERR_SHAPE;
-    if (!aligned(q, 16) || !aligned(kv->data, 16) || !aligned(o, 8) || !aligned(lse, 4))
+    if (!aligned(q, 16) || !aligned(kv->data, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return MLA_ERR_ALIGN;
     return MLA_OK;
 }

@@ -70,6 +70,7 @@ def test_bad_arguments_return_status_without_launching():
     assert _dense(q=0x1008) == ALIGN
     assert _dense(kv=_kv(ptr=0x1004)) == ALIGN
     assert _dense(o=0x4002) == ALIGN
+    assert _dense(o=0x4008) == ALIGN   # 16-byte output stores
     assert _dense(plan=P(0, 1)) == UNSUPPORTED
     assert _dense(plan=P(1, 3)) == UNSUPPORTED
     assert _dense(plan=P(1, 2)) == UNSUPPORTED       # 1 row tile per group: tiles must divide it
