@@ -12,8 +12,9 @@
 // a row that no rank holds a key of gets o = +0 and lse = -inf.
 //
 // One wave per row: lane l owns latent columns 8 l .. 8 l + 7 (16 bytes of bf16 per rank). The
-// row's R LSEs are wave-uniform loads; the o rows of the first eight ranks are requested together
-// with them (one memory round trip for R <= 8), later ranks eight at a time. HBM-bound for large
+// row's R LSEs are wave-uniform loads; the o rows and LSEs of the first eight ranks are all
+// requested before any is waited for (one memory round trip for R <= 8), later ranks eight at a
+// time. HBM-bound for large
 // row counts (each partial byte is read once), latency-bound for the small ones.
 #include <hip/hip_runtime.h>
 
@@ -55,18 +56,23 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(const uint16_t*
     const int64_t row = (int64_t)blockIdx.x * CB_ROWS + wave;
     if (row >= rows)
         return;
-    // the first eight ranks' o rows, requested before the LSEs arrive (rows of ranks without keys
-    // are read but never used)
+    // the first eight ranks' o rows and LSEs, all requested before any of them is waited for: the
+    // rank index is clamped to R - 1 so that every load is in bounds and none sits behind a branch
+    // (ranks >= R are masked afterwards; rows of ranks without keys are read but never used)
     v4i_c part[CB_UNROLL];
+    float lv[CB_UNROLL];
 #pragma unroll
     for (int u = 0; u < CB_UNROLL; u++) {
-        part[u] = v4i_c{0, 0, 0, 0};
-        if (u < R)
-            part[u] = *reinterpret_cast<const v4i_c*>(o_parts + ((int64_t)u * rows + row) * 512 + 8 * lane);
+        const int64_t r = u < R ? u : R - 1;
+        part[u] = *reinterpret_cast<const v4i_c*>(o_parts + (r * rows + row) * 512 + 8 * lane);
+        lv[u] = lse_parts[r * rows + row];
     }
     // the largest LSE of the row (wave-uniform)
     float M = -INFINITY;
-    for (int r = 0; r < R; r++)
+#pragma unroll
+    for (int u = 0; u < CB_UNROLL; u++)
+        M = u < R ? fmaxf(M, lv[u]) : M;
+    for (int r = CB_UNROLL; r < R; r++)
         M = fmaxf(M, lse_parts[(int64_t)r * rows + row]);
     uint16_t* orow = o + row * 512 + 8 * lane;
     if (M == -INFINITY) {
@@ -82,13 +88,13 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(const uint16_t*
 #pragma unroll
         for (int u = 0; u < CB_UNROLL; u++) {
             const int r = r0 + u;
-            const float l = r < R ? lse_parts[(int64_t)r * rows + row] : -INFINITY;
-            w[u] = l == -INFINITY ? 0.f : expf(l - M);
             if (r0 > 0) {
-                part[u] = v4i_c{0, 0, 0, 0};
-                if (r < R)
-                    part[u] = *reinterpret_cast<const v4i_c*>(o_parts + ((int64_t)r * rows + row) * 512 + 8 * lane);
+                const int64_t rr = r < R ? r : R - 1;
+                part[u] = *reinterpret_cast<const v4i_c*>(o_parts + (rr * rows + row) * 512 + 8 * lane);
+                lv[u] = lse_parts[rr * rows + row];
             }
+            const float l = r < R ? lv[u] : -INFINITY;
+            w[u] = l == -INFINITY ? 0.f : expf(l - M);
         }
 #pragma unroll
         for (int u = 0; u < CB_UNROLL; u++) {
