@@ -50,10 +50,14 @@ constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the thre
 constexpr int TK_LDS_K = 8192;   // lists of up to this many entries are built in LDS
 
 struct TkShared {
-    uint32_t hist[TK_BINS];
+    alignas(16) uint32_t hist[TK_BINS];   // read and cleared 16 bytes at a time
+    alignas(16) uint32_t hist2[1 << TK_LO_BITS];   // second digits (cleared with the first histogram)
+    uint32_t wave_min[TK_WAVES];
     int wave_tot[TK_WAVES];
-    int sel[4];   // first-digit bin, keys above it, second-digit bin, keys above the threshold
+    int sel[2];   // first-digit bin, keys above it
 };
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 template <bool STAGE>
 struct TkList {   // the selected columns: in LDS (K <= TK_LDS_K), else in the output row itself
@@ -83,7 +87,21 @@ __device__ inline int tk_wave_scan(int v)
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// Exclusive prefix sum over the workgroup's threads in thread order (and the total).
+// Minimum over the wave's lanes (the same in every lane): within each row of 16 lanes by quad swaps
+// and the half-row and row mirrors, then across the four rows by readlane.
+__device__ inline uint32_t tk_wave_min(uint32_t v)
+{
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return min(min(a, b), min(c, d));
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order (and the total). One barrier:
+// the caller puts another between this scan's reads of wave_tot and the next scan's writes.
 __device__ inline int tk_scan(int x, TkShared& sh, int& total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -99,7 +117,6 @@ __device__ inline int tk_scan(int x, TkShared& sh, int& total)
         off += w < wave ? t : 0;
         total += t;
     }
-    __syncthreads();   // wave_tot is reused by the next scan
     return off + v - x;
 }
 
@@ -144,34 +161,25 @@ __device__ inline void tk_keys(const uint16_t* row, int n, int s0, uint32_t (&kw
     tk_form(raw, n, s0, kw);
 }
 
-// Of the nbins bins (counts in sh.hist), the highest bin b whose count together with the bins
-// above it reaches need; sh.sel[slot] = b (-1 if none), sh.sel[slot + 1] = the count above b.
-// Thread t looks at bins nbins - 1 - TK_BPT t - i, i = 0 .. TK_BPT - 1 (from the top).
-__device__ inline void tk_pick_bin(TkShared& sh, int nbins, int need, int slot)
+// Of the TK_BINS first-digit bins (counts in sh.hist), the highest bin b whose count together with
+// the bins above it reaches need: sh.sel[0] = b, sh.sel[1] = the count above b (left at -1 and 0,
+// as cleared, if there is none). Thread t looks at the four bins 4 (1023 - t) + 3 .. 4 (1023 - t),
+// from the top; the bin is found by the one thread whose share crosses need.
+__device__ inline void tk_pick_bin(TkShared& sh, int need)
 {
     const int t = threadIdx.x;
-    int c[TK_BPT];
-    int mine = 0;
-#pragma unroll
-    for (int i = 0; i < TK_BPT; i++) {
-        const int bin = nbins - 1 - TK_BPT * t - i;
-        c[i] = bin >= 0 ? (int)sh.hist[bin] : 0;
-        mine += c[i];
-    }
+    const int b0 = TK_BINS - TK_BPT * (t + 1);
+    static_assert(TK_BPT == 4, "one 16-byte LDS read per thread");
+    const v4i_t h = *reinterpret_cast<const v4i_t*>(&sh.hist[b0]);
     int total;
-    int excl = tk_scan(mine, sh, total);
-    if (t == 0) {
-        sh.sel[slot] = -1;
-        sh.sel[slot + 1] = 0;
-    }
-    __syncthreads();
+    int excl = tk_scan(h[0] + h[1] + h[2] + h[3], sh, total);
 #pragma unroll
-    for (int i = 0; i < TK_BPT; i++) {
-        if (c[i] > 0 && excl < need && excl + c[i] >= need) {
-            sh.sel[slot] = nbins - 1 - TK_BPT * t - i;
-            sh.sel[slot + 1] = excl;
+    for (int i = TK_BPT - 1; i >= 0; i--) {
+        if (h[i] > 0 && excl < need && excl + h[i] >= need) {
+            sh.sel[0] = b0 + i;
+            sh.sel[1] = excl;
         }
-        excl += c[i];
+        excl += h[i];
     }
     __syncthreads();
 }
@@ -286,20 +294,67 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     const bool resident = ONE || n <= TK_SPAN;
     const int s_end = ONE ? (n > 0 ? 1 : 0) : n;   // the span loops: s0 < s_end
     uint32_t kw[TK_KW];
-    if (resident)
+    // A lower bound on the threshold, from a row held in registers: with m = ceil(K / 1024) <= 2,
+    // every thread holding at least m candidates has m keys >= its m-th largest, so if these
+    // threads number F with m F >= K, at least K keys are >= the least of their m-th largest keys,
+    // L, and so is the K-th largest. The first-digit bins below L's bin can then hold neither the
+    // threshold nor a key above it, and pass 1 leaves those keys out (for N(0, 1) logits most of
+    // them, with their LDS atomics). Lb = the first key of L's bin (1: no bound, only NaN and the
+    // columns past the end left out).
+    uint32_t Lb = 1u;
+    const int m = (K + TK_THREADS - 1) / TK_THREADS;
+    if (resident) {
         tk_form(raw0, n, 0, kw);
+        // the largest and second-largest key of the even and the odd columns, two lanes at once
+        u16x2_t a1 = {0, 0}, a2 = {0, 0};
+#pragma unroll
+        for (int i = 0; i < TK_KW; i++) {
+            const u16x2_t k = __builtin_bit_cast(u16x2_t, kw[i]);
+            a2 = __builtin_elementwise_max(a2, __builtin_elementwise_min(a1, k));
+            a1 = __builtin_elementwise_max(a1, k);
+        }
+        const uint32_t m1 = a1[0] > a1[1] ? a1[0] : a1[1];
+        const uint32_t lo1 = a1[0] > a1[1] ? a1[1] : a1[0];
+        const uint32_t hi2 = a2[0] > a2[1] ? a2[0] : a2[1];
+        const uint32_t m2 = lo1 > hi2 ? lo1 : hi2;
+        const uint32_t mth = m == 1 ? m1 : m2;   // 0: fewer than m candidates
+        const bool full = m <= 2 && mth != 0u;
+        const uint32_t wmin = tk_wave_min(full ? mth : 0xFFFFu);
+        const int wfull = __builtin_popcountll(__ballot(full));
+        if ((t & 63) == 0) {
+            sh.wave_min[t >> 6] = wmin;
+            sh.wave_tot[t >> 6] = wfull;
+        }
+    }
 
-    // pass 1: histogram of the candidates' first digits (NaN and columns past the end skipped)
-    for (int i = t; i < TK_BINS; i += TK_THREADS)
-        sh.hist[i] = 0u;
+    // pass 1: histogram of the candidates' first digits (NaN, the columns past the end and, with a
+    // bound, the bins below it skipped)
+    *reinterpret_cast<v4i_t*>(&sh.hist[TK_BPT * t]) = v4i_t{0, 0, 0, 0};
+    if (t < (1 << TK_LO_BITS))
+        sh.hist2[t] = 0u;
+    if (t == 0) {
+        sh.sel[0] = -1;
+        sh.sel[1] = 0;
+    }
     __syncthreads();
+    if (resident) {
+        uint32_t L = 0xFFFFu;
+        int F = 0;
+#pragma unroll
+        for (int w = 0; w < TK_WAVES; w++) {
+            L = min(L, sh.wave_min[w]);
+            F += sh.wave_tot[w];
+        }
+        if (m * F >= K)
+            Lb = (L >> TK_LO_BITS) << TK_LO_BITS > 1u ? (L >> TK_LO_BITS) << TK_LO_BITS : 1u;
+    }
     for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
         if (!resident)
             tk_keys(row, n, s0, kw);
 #pragma unroll
         for (int e = 0; e < TK_OWN; e++) {
             const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            if (k != 0u)   // NaN and past the end: no atomic (one shared counter for them all
+            if (k >= Lb)   // no atomic for NaN and past the end (one shared counter for them all
                 atomicAdd(&sh.hist[k >> TK_LO_BITS], 1u);   // would serialize short rows)
         }
     }
@@ -307,14 +362,11 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     // the threshold: v = 0 selects every candidate (fewer than K of them)
     uint32_t v = 0u;
     int c_gt = 0;
-    tk_pick_bin(sh, TK_BINS, K, 0);
+    tk_pick_bin(sh, K);   // ends with a barrier: wave_tot is free again
     const int b1 = sh.sel[0];
     if (b1 >= 0) {
         const int above = sh.sel[1];
-        // pass 2: histogram of the second digits of the keys in bin b1
-        if (t < (1 << TK_LO_BITS))
-            sh.hist[t] = 0u;
-        __syncthreads();
+        // pass 2: histogram of the second digits of the keys in bin b1 (hist2 was cleared with hist)
         for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
             if (!resident)
                 tk_keys(row, n, s0, kw);
@@ -322,13 +374,28 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
             for (int e = 0; e < TK_OWN; e++) {
                 const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                 if (k != 0u && (int)(k >> TK_LO_BITS) == b1)
-                    atomicAdd(&sh.hist[k & ((1u << TK_LO_BITS) - 1u)], 1u);
+                    atomicAdd(&sh.hist2[k & ((1u << TK_LO_BITS) - 1u)], 1u);
             }
         }
         __syncthreads();
-        tk_pick_bin(sh, 1 << TK_LO_BITS, K - above, 2);
-        v = ((uint32_t)b1 << TK_LO_BITS) | (uint32_t)sh.sel[2];
-        c_gt = above + sh.sel[3];
+        // every thread finds the second digit itself from the 16 counts: the highest digit d whose
+        // count together with the digits above it reaches K - above (the counts of bin b1 reach it)
+        const int need = K - above;
+        int cum = 0, d = 0, cum_d = 0;
+#pragma unroll
+        for (int q = (1 << TK_LO_BITS) / 4 - 1; q >= 0; q--) {
+            const v4i_t h = *reinterpret_cast<const v4i_t*>(&sh.hist2[4 * q]);
+#pragma unroll
+            for (int i = 3; i >= 0; i--) {
+                if (cum < need && cum + h[i] >= need) {
+                    d = 4 * q + i;
+                    cum_d = cum;
+                }
+                cum += h[i];
+            }
+        }
+        v = ((uint32_t)b1 << TK_LO_BITS) | (uint32_t)d;
+        c_gt = above + cum_d;
     }
     // pass 3: the selected columns in order, remapped to cache rows
     int gt_run = 0, eq_run = 0;
@@ -347,16 +414,21 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
         }
         uint64_t gtm = ((uint64_t)gm[1] << 32) | gm[0];
         uint64_t eqm = ((uint64_t)em[1] << 32) | em[0];
-        int tot_gt, tot_eq;
-        int pg = gt_run + tk_scan(__builtin_popcountll(gtm), sh, tot_gt);
-        int pe = eq_run + tk_scan(__builtin_popcountll(eqm), sh, tot_eq);
+        // both prefix sums in one: the counts above the threshold in the low 16 bits, those equal
+        // to it in the high 16 (each at most 32768 per span, so neither carries into the other)
+        int tot;
+        const int pre = tk_scan(__builtin_popcountll(gtm) | (__builtin_popcountll(eqm) << 16), sh, tot);
+        int pg = gt_run + (pre & 0xFFFF);
+        int pe = eq_run + (pre >> 16);
         const int cbase = s0 + TK_OWN * t;
         for (; gtm; gtm &= gtm - 1)   // in column order
             list[pg++] = cbase + __builtin_ctzll(gtm);
         for (; eqm && pe < eq_room; eqm &= eqm - 1)
             list[c_gt + pe++] = cbase + __builtin_ctzll(eqm);
-        gt_run += tot_gt;
-        eq_run += tot_eq;
+        gt_run += tot & 0xFFFF;
+        eq_run += tot >> 16;
+        if (s0 + TK_SPAN < s_end)
+            __syncthreads();   // the next span's scan rewrites wave_tot
     }
     const int count = b1 >= 0 ? K : gt_run;
     // the columns -> positions -> cache rows, each thread a strided share of the list (its writes

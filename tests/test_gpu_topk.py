@@ -136,3 +136,33 @@ def test_topk_rows_whose_first_span_holds_fewer_than_k_candidates():
     assert list(cnt) == [K, 2500, K]
     assert np.array_equal(valid, cnt)
     assert np.array_equal(rows, ref)
+
+
+@pytest.mark.parametrize("K", [2048, 1024, 1500, 2049])
+def test_topk_rows_built_around_the_per_thread_bound(K):
+    """Rows of one 32768-column span whose structure sits on the lower bound the kernel derives
+    from each thread's 32 consecutive columns (the least of their m-th largest keys, m = ceil(K /
+    1024)): row 0 puts two high values (with ties) in every 32-column group and low ones elsewhere,
+    so the bound meets the threshold; row 1 ascends, so the first group's bound is far below it;
+    row 2 gives half the groups one candidate only (the rest NaN), so too few groups qualify for
+    a bound; row 3 is a plain N(0, 1) row ending mid-group."""
+    N = 32768
+    rng = np.random.default_rng(700 + K)
+    x = rng.standard_normal((4, N)).astype(np.float32) - 3.0
+    g = N // 32
+    hi_cols = (np.arange(g)[:, None] * 32 + np.stack([rng.choice(32, 2, replace=False)
+                                                     for _ in range(g)])).ravel()
+    x[0, hi_cols] = np.round((rng.standard_normal(hi_cols.size) + 3.0) * 2) / 2
+    x[1] = np.sort(rng.standard_normal(N)).astype(np.float32)
+    x[3] = rng.standard_normal(N).astype(np.float32)
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    lone = np.arange(0, g, 2) * 32 + rng.integers(0, 32, g // 2)
+    keep = np.zeros(N, bool)
+    keep[lone] = True
+    keep[(np.arange(g) % 2 == 1).repeat(32)] = True
+    bits[2, ~keep] = 0x7FC0
+    ends = [N, N, N, N - 17]
+    rows, valid = _run(bits, ends, K)
+    ref, cnt = otopk.select(bits, np.asarray(ends), K)
+    assert np.array_equal(valid, cnt)
+    assert np.array_equal(rows, ref)
