@@ -16,16 +16,20 @@
 // pattern to an unsigned integer: positive bits | 0x8000, negative ~bits.
 //
 // One 1024-thread workgroup per row. The row is taken in spans of 32768 columns; in a span thread
-// t owns the 32 consecutive columns 32 t .. 32 t + 31 (four 16-byte loads), whose order keys it
-// forms once and keeps packed two to a register (0 for NaN and past the row end), so a row of at
-// most 32768 columns is read from memory once for all three passes. The threshold comes
-// from two radix histograms in LDS: the key's top 12 bits (4096 bins: sign, exponent and three
-// fraction bits, so the LDS atomics of clustered values spread over many bins), then its low 4
-// bits among the keys in the chosen bin. The ordered output: per thread two 64-bit masks (columns
-// above / equal to the threshold), one workgroup prefix sum per span of their popcounts (wave
-// prefix by DPP row shifts and the rows' totals, then the 16 wave totals through LDS) and the set
-// bits in ascending order: thread order is column order, so the lists come out in column order
-// without a sort. Lists of up to 8192 entries are built in LDS and remapped from there.
+// t owns the 32 consecutive columns 32 t .. 32 t + 31 (four 16-byte loads), whose ranks (the order
+// key less 0x7E, 0 for NaN and past the row end, formed two at a time by packed 16-bit arithmetic)
+// it keeps packed two to a register, so a row of at most 32768 columns is read from memory once
+// for all three passes. The threshold comes from two radix histograms in LDS. The first covers the
+// ranks from a lower bound to the row's largest in 4096 bins of 2^sb ranks, sb as small as fits:
+// for a row held in registers the bound is the least m-th largest rank of the threads' 32
+// (m = ceil(K / 1024)), and for N(0, 1) logits every rank then gets a bin of its own (sb = 0),
+// which finds the threshold exactly and skips the second histogram; otherwise that one resolves
+// the chosen bin's 2^sb ranks. The ordered output: per thread two 32-bit masks (columns above /
+// equal to the threshold, one compare and one add-with-carry per bit), one workgroup prefix sum
+// per span of both popcounts packed in one word (wave prefix by DPP row shifts and the rows'
+// totals, then the 16 wave totals through LDS) and the set bits in ascending order: thread order
+// is column order, so the lists come out in column order without a sort. Lists of up to 8192
+// entries are built in LDS and remapped from there.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -50,9 +54,11 @@ constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the thre
 constexpr int TK_LDS_K = 8192;   // lists of up to this many entries are built in LDS
 
 struct TkShared {
-    alignas(16) uint32_t hist[TK_BINS];   // read and cleared 16 bytes at a time
-    alignas(16) uint32_t hist2[1 << TK_LO_BITS];   // second digits (cleared with the first histogram)
+    alignas(16) uint32_t hist[TK_BINS + 64];   // the bins (read and cleared 16 bytes at a time),
+                                               // then a spare counter per lane, never read
+    alignas(16) uint32_t hist2[1 << TK_LO_BITS];   // the second pass (cleared with the first)
     uint32_t wave_min[TK_WAVES];
+    uint32_t wave_max[TK_WAVES];
     int wave_tot[TK_WAVES];
     int sel[2];   // first-digit bin, keys above it
 };
@@ -64,12 +70,21 @@ struct TkList {   // the selected columns: in LDS (K <= TK_LDS_K), else in the o
     int32_t col[STAGE ? TK_LDS_K : 1];
 };
 
-// the order key of a bf16 pattern (16 bits), or 0 for NaN (no valid key is 0: -inf maps to 0x7F);
-// branch-free: b ^ 0xFFFF (= ~b) for a set sign bit, b ^ 0x8000 (= b | 0x8000) for a clear one
-__device__ inline uint32_t tk_key(uint32_t b)
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+
+// The ranks of two bf16 patterns (one per 16-bit half): the order key minus 0x7E, or 0 for NaN.
+// The order key is b ^ 0xFFFF (= ~b) for a set sign bit, b ^ 0x8000 (= b | 0x8000) for a clear
+// one: -inf maps to 0x7F, +inf to 0xFF80, the negative NaNs below 0x7F and the positive ones
+// above 0xFF80. Three packed 16-bit steps, two columns per instruction: + 0x7E saturating (the
+// positive NaNs, and only they, reach 0xFFFF), + 1 wrapping (they become 0), - 0xFD saturating
+// (the negative NaNs, at most 0xFC by then, become 0). Numbers come out at 1 .. 0xFF02 in the
+// keys' order, so every comparison of ranks is one of keys.
+__device__ inline uint32_t tk_rank2(uint32_t w)
 {
-    const uint32_t k = b ^ (0x8000u | (0x7FFFu * (b >> 15)));
-    return (b & 0x7FFFu) > 0x7F80u ? 0u : k;
+    const s16x2_t sgn = __builtin_bit_cast(s16x2_t, w) >> (s16x2_t){15, 15};   // 0xFFFF where negative
+    const u16x2_t key = __builtin_bit_cast(u16x2_t, w ^ (__builtin_bit_cast(uint32_t, sgn) | 0x80008000u));
+    const u16x2_t a = __builtin_elementwise_add_sat(key, (u16x2_t){0x7E, 0x7E}) + (u16x2_t){1, 1};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(a, (u16x2_t){0xFD, 0xFD}));
 }
 
 // Inclusive prefix sum over the wave's lanes: within each row of 16 lanes by DPP row shifts of 1,
@@ -137,20 +152,42 @@ __device__ inline void tk_load(const uint16_t* row, int lim, int s0, v4i_t (&raw
     }
 }
 
-// Their order keys: kw[i] holds column 2 i in its low half and column 2 i + 1 in its high half
-// (0 at and past the row end n).
+// Their ranks: kw[i] holds column 2 i in its low half and column 2 i + 1 in its high half (0 at
+// and past the row end n, which only the threads holding columns at or past n mask).
 __device__ inline void tk_form(const v4i_t (&raw)[TK_VEC], int n, int s0, uint32_t (&kw)[TK_KW])
 {
     const int c = s0 + TK_OWN * (int)threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < TK_KW; i++) {
-        const uint32_t w = (uint32_t)raw[i >> 2][i & 3];
-        const int col = c + 2 * i;
-        // 0xFFFF where the column lies before n (the sign of col - n), else 0: no branch
-        const uint32_t mlo = ((uint32_t)(col - n) >> 31) * 0xFFFFu;
-        const uint32_t mhi = ((uint32_t)(col + 1 - n) >> 31) * 0xFFFFu;
-        kw[i] = (tk_key(w & 0xFFFFu) & mlo) | ((tk_key(w >> 16) & mhi) << 16);
+    for (int i = 0; i < TK_KW; i++)
+        kw[i] = tk_rank2((uint32_t)raw[i >> 2][i & 3]);
+    if (c + TK_OWN > n) {
+#pragma unroll
+        for (int i = 0; i < TK_KW; i++) {
+            const int col = c + 2 * i;
+            // 0xFFFF where the column lies before n (the sign of col - n), else 0
+            const uint32_t mlo = ((uint32_t)(col - n) >> 31) * 0xFFFFu;
+            const uint32_t mhi = ((uint32_t)(col + 1 - n) >> 31) * 0xFFFF0000u;
+            kw[i] &= mlo | mhi;
+        }
     }
+}
+
+// Two more columns into the threshold masks: the key pair w (column 2 i in the low half, 2 i + 1 in
+// the high half), taken from the last column down, so that column e ends at bit e. Per column one
+// compare of the selected 16-bit half with v into VCC and one add-with-carry m = m + m + VCC.
+__device__ inline void tk_mask_step(uint32_t w, uint32_t v, uint32_t& gm, uint32_t& em)
+{
+    asm("v_cmp_gt_u32_sdwa vcc, %2, %3 src0_sel:WORD_1 src1_sel:DWORD\n\t"
+        "v_addc_co_u32 %0, vcc, %0, %0, vcc\n\t"
+        "v_cmp_eq_u32_sdwa vcc, %2, %3 src0_sel:WORD_1 src1_sel:DWORD\n\t"
+        "v_addc_co_u32 %1, vcc, %1, %1, vcc\n\t"
+        "v_cmp_gt_u32_sdwa vcc, %2, %3 src0_sel:WORD_0 src1_sel:DWORD\n\t"
+        "v_addc_co_u32 %0, vcc, %0, %0, vcc\n\t"
+        "v_cmp_eq_u32_sdwa vcc, %2, %3 src0_sel:WORD_0 src1_sel:DWORD\n\t"
+        "v_addc_co_u32 %1, vcc, %1, %1, vcc"
+        : "+v"(gm), "+v"(em)
+        : "v"(w), "v"(v)
+        : "vcc");
 }
 
 // The order keys of this thread's 32 columns of the span starting at s0 (0 past the row end n).
@@ -294,18 +331,23 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     const bool resident = ONE || n <= TK_SPAN;
     const int s_end = ONE ? (n > 0 ? 1 : 0) : n;   // the span loops: s0 < s_end
     uint32_t kw[TK_KW];
-    // A lower bound on the threshold, from a row held in registers: with m = ceil(K / 1024) <= 2,
-    // every thread holding at least m candidates has m keys >= its m-th largest, so if these
-    // threads number F with m F >= K, at least K keys are >= the least of their m-th largest keys,
-    // L, and so is the K-th largest. The first-digit bins below L's bin can then hold neither the
-    // threshold nor a key above it, and pass 1 leaves those keys out (for N(0, 1) logits most of
-    // them, with their LDS atomics). Lb = the first key of L's bin (1: no bound, only NaN and the
-    // columns past the end left out).
-    uint32_t Lb = 1u;
+    // The first histogram covers ranks base .. M in 4096 bins (k - base) >> sb, with the least sb
+    // (0 .. 4) that fits; ranks below base go to per-lane spare counters (no branch, no shared
+    // counter). Without more knowledge base = 1 (every candidate) and sb = 4. A row held in
+    // registers gives more: with m = ceil(K / 1024) <= 2, every thread holding at least m
+    // candidates has m ranks >= its m-th largest, so if these threads number F with m F >= K, at
+    // least K ranks are >= the least of their m-th largest, L, and so is the threshold: base = L.
+    // M = the row's largest rank. For N(0, 1) logits this leaves about a quarter of the ranks in
+    // range, and M - base < 4096: sb = 0, every rank has its own bin and the threshold is found
+    // without a second pass.
+    uint32_t base = 1u;
+    int sb = TK_LO_BITS;
     const int m = (K + TK_THREADS - 1) / TK_THREADS;
+    bool any = true;   // this lane holds a rank >= base (resident rows)
+    uint32_t m1 = 0u;
     if (resident) {
         tk_form(raw0, n, 0, kw);
-        // the largest and second-largest key of the even and the odd columns, two lanes at once
+        // the largest and second-largest rank of the even and the odd columns, two lanes at once
         u16x2_t a1 = {0, 0}, a2 = {0, 0};
 #pragma unroll
         for (int i = 0; i < TK_KW; i++) {
@@ -313,22 +355,23 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
             a2 = __builtin_elementwise_max(a2, __builtin_elementwise_min(a1, k));
             a1 = __builtin_elementwise_max(a1, k);
         }
-        const uint32_t m1 = a1[0] > a1[1] ? a1[0] : a1[1];
+        m1 = a1[0] > a1[1] ? a1[0] : a1[1];
         const uint32_t lo1 = a1[0] > a1[1] ? a1[1] : a1[0];
         const uint32_t hi2 = a2[0] > a2[1] ? a2[0] : a2[1];
         const uint32_t m2 = lo1 > hi2 ? lo1 : hi2;
         const uint32_t mth = m == 1 ? m1 : m2;   // 0: fewer than m candidates
         const bool full = m <= 2 && mth != 0u;
         const uint32_t wmin = tk_wave_min(full ? mth : 0xFFFFu);
+        const uint32_t wmax = 0xFFFFu - tk_wave_min(0xFFFFu - m1);
         const int wfull = __builtin_popcountll(__ballot(full));
         if ((t & 63) == 0) {
             sh.wave_min[t >> 6] = wmin;
+            sh.wave_max[t >> 6] = wmax;
             sh.wave_tot[t >> 6] = wfull;
         }
     }
 
-    // pass 1: histogram of the candidates' first digits (NaN, the columns past the end and, with a
-    // bound, the bins below it skipped)
+    // pass 1: the first histogram
     *reinterpret_cast<v4i_t*>(&sh.hist[TK_BPT * t]) = v4i_t{0, 0, 0, 0};
     if (t < (1 << TK_LO_BITS))
         sh.hist2[t] = 0u;
@@ -338,24 +381,31 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     }
     __syncthreads();
     if (resident) {
-        uint32_t L = 0xFFFFu;
+        uint32_t L = 0xFFFFu, M = 0u;
         int F = 0;
 #pragma unroll
         for (int w = 0; w < TK_WAVES; w++) {
             L = min(L, sh.wave_min[w]);
+            M = max(M, sh.wave_max[w]);
             F += sh.wave_tot[w];
         }
         if (m * F >= K)
-            Lb = (L >> TK_LO_BITS) << TK_LO_BITS > 1u ? (L >> TK_LO_BITS) << TK_LO_BITS : 1u;
+            base = L;   // >= 1: a qualifying thread's m-th largest rank is a candidate's
+        sb = 0;
+        while (M >= base && ((M - base) >> sb) >= (uint32_t)TK_BINS)
+            sb++;   // at most 4: ranks are below 2^16
+        any = m1 >= base;
     }
-    for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
-        if (!resident)
-            tk_keys(row, n, s0, kw);
+    const uint32_t spare = TK_BINS + (t & 63);
+    if (__ballot(any) != 0ull) {   // a wave with no rank in range has nothing to count
+        for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
+            if (!resident)
+                tk_keys(row, n, s0, kw);
 #pragma unroll
-        for (int e = 0; e < TK_OWN; e++) {
-            const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            if (k >= Lb)   // no atomic for NaN and past the end (one shared counter for them all
-                atomicAdd(&sh.hist[k >> TK_LO_BITS], 1u);   // would serialize short rows)
+            for (int e = 0; e < TK_OWN; e++) {
+                const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                atomicAdd(&sh.hist[k >= base ? (k - base) >> sb : spare], 1u);
+            }
         }
     }
     __syncthreads();
@@ -366,36 +416,44 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     const int b1 = sh.sel[0];
     if (b1 >= 0) {
         const int above = sh.sel[1];
-        // pass 2: histogram of the second digits of the keys in bin b1 (hist2 was cleared with hist)
-        for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
-            if (!resident)
-                tk_keys(row, n, s0, kw);
+        const uint32_t lo = base + ((uint32_t)b1 << sb);   // bin b1: ranks lo .. lo + 2^sb - 1
+        v = lo;
+        c_gt = above;
+        if (sb > 0) {
+            // pass 2: histogram of the ranks in bin b1 by their offset from lo (hist2 was
+            // cleared with hist; a rank below lo wraps to a large offset)
+            const uint32_t width = 1u << sb;
+            for (int s0 = 0; s0 < s_end; s0 += TK_SPAN) {
+                if (!resident)
+                    tk_keys(row, n, s0, kw);
 #pragma unroll
-            for (int e = 0; e < TK_OWN; e++) {
-                const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                if (k != 0u && (int)(k >> TK_LO_BITS) == b1)
-                    atomicAdd(&sh.hist2[k & ((1u << TK_LO_BITS) - 1u)], 1u);
-            }
-        }
-        __syncthreads();
-        // every thread finds the second digit itself from the 16 counts: the highest digit d whose
-        // count together with the digits above it reaches K - above (the counts of bin b1 reach it)
-        const int need = K - above;
-        int cum = 0, d = 0, cum_d = 0;
-#pragma unroll
-        for (int q = (1 << TK_LO_BITS) / 4 - 1; q >= 0; q--) {
-            const v4i_t h = *reinterpret_cast<const v4i_t*>(&sh.hist2[4 * q]);
-#pragma unroll
-            for (int i = 3; i >= 0; i--) {
-                if (cum < need && cum + h[i] >= need) {
-                    d = 4 * q + i;
-                    cum_d = cum;
+                for (int e = 0; e < TK_OWN; e++) {
+                    const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    if (k - lo < width)
+                        atomicAdd(&sh.hist2[k - lo], 1u);
                 }
-                cum += h[i];
             }
+            __syncthreads();
+            // every thread finds the offset itself from the counts: the highest offset d whose
+            // count together with those above it reaches K - above (bin b1's counts reach it)
+            const int need = K - above;
+            int cum = 0, d = 0, cum_d = 0;
+#pragma unroll
+            for (int q = (1 << TK_LO_BITS) / 4 - 1; q >= 0; q--) {
+                const v4i_t h = *reinterpret_cast<const v4i_t*>(&sh.hist2[4 * q]);
+#pragma unroll
+                for (int i = 3; i >= 0; i--) {
+                    const int c = __builtin_amdgcn_readfirstlane(h[i]);   // the same in every lane
+                    if (cum < need && cum + c >= need) {
+                        d = 4 * q + i;
+                        cum_d = cum;
+                    }
+                    cum += c;
+                }
+            }
+            v = lo + (uint32_t)d;
+            c_gt = above + cum_d;
         }
-        v = ((uint32_t)b1 << TK_LO_BITS) | (uint32_t)d;
-        c_gt = above + cum_d;
     }
     // pass 3: the selected columns in order, remapped to cache rows
     int gt_run = 0, eq_run = 0;
@@ -405,15 +463,14 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
             tk_keys(row, n, s0, kw);
         // bit e of the masks: column e of this thread's part is above / equal to the threshold
         // (a key equal to v is never 0: v = 0 only when every candidate is taken)
-        uint32_t gm[2] = {0u, 0u}, em[2] = {0u, 0u};
+        static_assert(TK_OWN == 32, "one 32-bit mask per thread");
+        uint32_t gm = 0u, em = 0u;
 #pragma unroll
-        for (int e = 0; e < TK_OWN; e++) {
-            const uint32_t k = (kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            gm[e >> 5] |= (k > v ? 1u : 0u) << (e & 31);
-            em[e >> 5] |= (k == v && v != 0u ? 1u : 0u) << (e & 31);
-        }
-        uint64_t gtm = ((uint64_t)gm[1] << 32) | gm[0];
-        uint64_t eqm = ((uint64_t)em[1] << 32) | em[0];
+        for (int i = TK_KW - 1; i >= 0; i--)
+            tk_mask_step(kw[i], v, gm, em);
+        em = v != 0u ? em : 0u;
+        uint64_t gtm = gm;
+        uint64_t eqm = em;
         // both prefix sums in one: the counts above the threshold in the low 16 bits, those equal
         // to it in the high 16 (each at most 32768 per span, so neither carries into the other)
         int tot;

@@ -166,3 +166,29 @@ def test_topk_rows_built_around_the_per_thread_bound(K):
     ref, cnt = otopk.select(bits, np.asarray(ends), K)
     assert np.array_equal(valid, cnt)
     assert np.array_equal(rows, ref)
+
+
+@pytest.mark.parametrize("K", [2048, 700, 3000])
+def test_topk_rows_of_wide_and_narrow_value_ranges(K):
+    """The first histogram spans the row's ranks from a lower bound to the largest, in bins of 1, 2,
+    4, 8 or 16 ranks as the span needs: rows of log-normal values over many binades (wide), of
+    values near 1e-30 (narrow, negative and positive), a row of +inf and NaN only, and a row where
+    a few huge values sit above a mass of ordinary ones; every row bit-exact against the oracle."""
+    N = 32768
+    rng = np.random.default_rng(900 + K)
+    x = np.empty((5, N), np.float32)
+    with np.errstate(over="ignore"):
+        x[0] = np.exp(rng.standard_normal(N) * 20.0).astype(np.float32)
+    x[1] = (rng.standard_normal(N) * 1e-30).astype(np.float32)
+    x[2] = np.inf
+    x[3] = rng.standard_normal(N).astype(np.float32)
+    x[3, rng.choice(N, 40, replace=False)] = 3e38
+    x[4] = -np.abs(rng.standard_normal(N)).astype(np.float32) * 1e20
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    bits[2, rng.random(N) < 0.5] = 0x7FC0
+    bits[2, rng.random(N) < 0.2] = 0xFFC1
+    ends = [N, N - 3, N, N, 31000]
+    rows, valid = _run(bits, ends, K)
+    ref, cnt = otopk.select(bits, np.asarray(ends), K)
+    assert np.array_equal(valid, cnt)
+    assert np.array_equal(rows, ref)
