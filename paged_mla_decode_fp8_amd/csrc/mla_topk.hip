@@ -119,19 +119,22 @@ __device__ inline uint32_t tk_wave_min(uint32_t v)
 // the caller puts another between this scan's reads of wave_tot and the next scan's writes.
 __device__ inline int tk_scan(int x, TkShared& sh, int& total)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int v = tk_wave_scan(x);
     if (lane == 63)
         sh.wave_tot[wave] = v;
     __syncthreads();
-    int off = 0;
-    total = 0;
-#pragma unroll
-    for (int w = 0; w < TK_WAVES; w++) {
-        const int t = sh.wave_tot[w];
-        off += w < wave ? t : 0;
-        total += t;
-    }
+    // the 16 wave totals in lanes 0..15 (each row of 16 lanes holds a copy), scanned inside the
+    // row by DPP shifts; this wave's offset and the total are read out as scalars
+    static_assert(TK_WAVES == 16, "one DPP row of wave totals");
+    int wt = sh.wave_tot[lane & 15];
+    wt += __builtin_amdgcn_update_dpp(0, wt, 0x111, 0xF, 0xF, true);   // row_shr:1
+    wt += __builtin_amdgcn_update_dpp(0, wt, 0x112, 0xF, 0xF, true);   // row_shr:2
+    wt += __builtin_amdgcn_update_dpp(0, wt, 0x114, 0xF, 0xF, true);   // row_shr:4
+    wt += __builtin_amdgcn_update_dpp(0, wt, 0x118, 0xF, 0xF, true);   // row_shr:8
+    total = __builtin_amdgcn_readlane(wt, TK_WAVES - 1);
+    const int off = wave > 0 ? __builtin_amdgcn_readlane(wt, wave > 0 ? wave - 1 : 0) : 0;
     return off + v - x;
 }
 
