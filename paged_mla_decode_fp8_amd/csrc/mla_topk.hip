@@ -472,19 +472,17 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
         for (int i = TK_KW - 1; i >= 0; i--)
             tk_mask_step(kw[i], v, gm, em);
         em = v != 0u ? em : 0u;
-        uint64_t gtm = gm;
-        uint64_t eqm = em;
         // both prefix sums in one: the counts above the threshold in the low 16 bits, those equal
         // to it in the high 16 (each at most 32768 per span, so neither carries into the other)
         int tot;
-        const int pre = tk_scan(__builtin_popcountll(gtm) | (__builtin_popcountll(eqm) << 16), sh, tot);
+        const int pre = tk_scan(__builtin_popcount(gm) | (__builtin_popcount(em) << 16), sh, tot);
         int pg = gt_run + (pre & 0xFFFF);
         int pe = eq_run + (pre >> 16);
         const int cbase = s0 + TK_OWN * t;
-        for (; gtm; gtm &= gtm - 1)   // in column order
-            list[pg++] = cbase + __builtin_ctzll(gtm);
-        for (; eqm && pe < eq_room; eqm &= eqm - 1)
-            list[c_gt + pe++] = cbase + __builtin_ctzll(eqm);
+        for (uint32_t g = gm; g; g &= g - 1)   // in column order
+            list[pg++] = cbase + __builtin_ctz(g);
+        for (uint32_t q = em; q && pe < eq_room; q &= q - 1)
+            list[c_gt + pe++] = cbase + __builtin_ctz(q);
         gt_run += tot & 0xFFFF;
         eq_run += tot >> 16;
         if (s0 + TK_SPAN < s_end)
