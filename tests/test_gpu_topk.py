@@ -192,3 +192,32 @@ def test_topk_rows_of_wide_and_narrow_value_ranges(K):
     ref, cnt = otopk.select(bits, np.asarray(ends), K)
     assert np.array_equal(valid, cnt)
     assert np.array_equal(rows, ref)
+
+
+@pytest.mark.parametrize("K", [1, 100, 2048, 30000])
+def test_topk_over_every_bf16_pattern(K):
+    """Rows that hold every 16-bit pattern once, shuffled (all NaNs of both signs, both zeros, both
+    infinities, the subnormals): row 0 all 65536 (two spans, reloaded per pass), rows 1 and 2 the
+    even and the odd patterns in one 32768-column span each (held in registers, with the lower
+    bound), row 3 the first 20000 of row 1 (a short row). Bit-exact against the oracle's select,
+    which ranks by its own order key: the kernel's ranks must order every pair of patterns the
+    same way and put every NaN out of the race."""
+    rng = np.random.default_rng(1234 + K)
+    allp = rng.permutation(65536).astype(np.uint16)
+    ev = rng.permutation(np.arange(0, 65536, 2)).astype(np.uint16)
+    od = rng.permutation(np.arange(1, 65536, 2)).astype(np.uint16)
+    bits = np.full((4, 65536), 0x7FC0, np.uint16)
+    bits[0] = allp
+    bits[1, :32768] = ev
+    bits[2, :32768] = od
+    bits[3, :32768] = ev
+    ends = [65536, 32768, 32768, 20000]
+    rows, valid = _run(bits, ends, K)
+    ref, cnt = otopk.select(bits, np.asarray(ends), K)
+    assert np.array_equal(valid, cnt)
+    assert np.array_equal(rows, ref)
+    # the same halves as rows of one 32768-column span (the one-span kernel)
+    rows2, valid2 = _run(bits[1:, :32768].copy(), [32768, 32768, 20000], K)
+    ref2, cnt2 = otopk.select(bits[1:, :32768].copy(), np.asarray([32768, 32768, 20000]), K)
+    assert np.array_equal(valid2, cnt2)
+    assert np.array_equal(rows2, ref2)
