@@ -461,8 +461,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU (the decode is measured on one GPU's "
-              "share; no multi-GPU path is built). Use --gpus 1.", file=sys.stderr)
+        print("bench.py: measures one GPU only (the decode of one GPU's share of the keys; the "
+              "library has no multi-GPU path). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
