@@ -46,8 +46,8 @@ constexpr int TK_SPAN = TK_THREADS * TK_OWN;      // 32768 columns
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-constexpr int TK_HI_BITS = 12;                    // first radix digit: key bits 15..4
-constexpr int TK_LO_BITS = 16 - TK_HI_BITS;       // second digit: key bits 3..0
+constexpr int TK_HI_BITS = 12;                    // the first histogram: 4096 bins
+constexpr int TK_LO_BITS = 16 - TK_HI_BITS;       // bins of at most 2^4 ranks, the second's 16 bins
 constexpr int TK_BINS = 1 << TK_HI_BITS;
 constexpr int TK_BPT = TK_BINS / TK_THREADS;      // bins per thread in the threshold search (4)
 
@@ -60,7 +60,7 @@ struct TkShared {
     uint32_t wave_min[TK_WAVES];
     uint32_t wave_max[TK_WAVES];
     int wave_tot[TK_WAVES];
-    int sel[2];   // first-digit bin, keys above it
+    int sel[2];   // the first histogram's chosen bin, ranks above it
 };
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
@@ -138,7 +138,7 @@ __device__ inline int tk_scan(int x, TkShared& sh, int& total)
     return off + v - x;
 }
 
-constexpr int TK_KW = TK_OWN / 2;                 // key registers per thread (two keys each)
+constexpr int TK_KW = TK_OWN / 2;                 // rank registers per thread (two ranks each)
 
 // This thread's 32 columns of the span starting at s0 as raw bf16 vectors (1 <= lim <= N and
 // N % 8 == 0: a 16-byte vector that starts before lim lies wholly in the row). A vector starting
@@ -175,8 +175,8 @@ __device__ inline void tk_form(const v4i_t (&raw)[TK_VEC], int n, int s0, uint32
     }
 }
 
-// Two more columns into the threshold masks: the key pair w (column 2 i in the low half, 2 i + 1 in
-// the high half), taken from the last column down, so that column e ends at bit e. Per column one
+// Two more columns into the threshold masks: the rank pair w (column 2 i in the low half, 2 i + 1
+// in the high half), taken from the last column down, so that column e ends at bit e. Per column one
 // compare of the selected 16-bit half with v into VCC and one add-with-carry m = m + m + VCC.
 __device__ inline void tk_mask_step(uint32_t w, uint32_t v, uint32_t& gm, uint32_t& em)
 {
@@ -193,7 +193,7 @@ __device__ inline void tk_mask_step(uint32_t w, uint32_t v, uint32_t& gm, uint32
         : "vcc");
 }
 
-// The order keys of this thread's 32 columns of the span starting at s0 (0 past the row end n).
+// The ranks of this thread's 32 columns of the span starting at s0 (0 past the row end n).
 __device__ inline void tk_keys(const uint16_t* row, int n, int s0, uint32_t (&kw)[TK_KW])
 {
     v4i_t raw[TK_VEC];
@@ -201,7 +201,7 @@ __device__ inline void tk_keys(const uint16_t* row, int n, int s0, uint32_t (&kw
     tk_form(raw, n, s0, kw);
 }
 
-// Of the TK_BINS first-digit bins (counts in sh.hist), the highest bin b whose count together with
+// Of the TK_BINS bins of the first histogram (counts in sh.hist), the highest bin b whose count together with
 // the bins above it reaches need: sh.sel[0] = b, sh.sel[1] = the count above b (left at -1 and 0,
 // as cleared, if there is none). Thread t looks at the four bins 4 (1023 - t) + 3 .. 4 (1023 - t),
 // from the top; the bin is found by the one thread whose share crosses need.
@@ -310,7 +310,7 @@ __device__ inline int32_t tk_remap(const TkRemap& m, const TkRowMap& rm, int col
     return (page >= 0 && cr < m.num_rows) ? (int32_t)cr : -1;
 }
 
-// ONE: every row fits one span (N <= 32768), so the keys stay in registers for all three passes
+// ONE: every row fits one span (N <= 32768), so the ranks stay in registers for all passes
 // and the span loops run once (a separate instantiation keeps the other case's code out).
 template <bool STAGE, bool ONE>
 __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
         if (!resident)
             tk_keys(row, n, s0, kw);
         // bit e of the masks: column e of this thread's part is above / equal to the threshold
-        // (a key equal to v is never 0: v = 0 only when every candidate is taken)
+        // (a rank equal to v is never 0: v = 0 only when every candidate is taken)
         static_assert(TK_OWN == 32, "one 32-bit mask per thread");
         uint32_t gm = 0u, em = 0u;
 #pragma unroll
