@@ -51,6 +51,8 @@ CASES = [
     (2, 65544, 4096, [65544, 40001], 8, 0.0),              # K above 2048, a ragged last span
     # K above the 8192 entries the kernel lists in LDS: the list is built in the output row
     (3, 40000, 9000, [40000, 9000, 5000], 4, 0.02),
+    (2, 16384, 10000, [16384, 12000], 2, 0.05),        # the same with the row in one span
+    (2, 32768, 8192, [32768, 30000], None, 0.0),       # the largest list built in LDS
 ]
 
 
