@@ -345,7 +345,7 @@ __global__ __launch_bounds__(TK_THREADS) void mla_topk_kernel(
     // without a second pass.
     uint32_t base = 1u;
     int sb = TK_LO_BITS;
-    const int m = (K + TK_THREADS - 1) / TK_THREADS;
+    const int m = K / TK_THREADS + (K % TK_THREADS != 0 ? 1 : 0);   // ceil, without overflow
     bool any = true;   // this lane holds a rank >= base (resident rows)
     uint32_t m1 = 0u;
     if (resident) {
