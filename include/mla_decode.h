@@ -239,8 +239,9 @@ mla_status_t mla_combine(const void* o_parts, const float* lse_parts, int R, int
  *   logits     device bf16 [R, N], 16-byte aligned; N a multiple of 8.
  *   row_ends   device int32 [R]; block_table device int32 [ceil(R / Q), max_pages] or NULL.
  *   rows_out   device int32 [R, K]; valid_out device int32 [R].
- * Errors: MLA_ERR_SHAPE (R < 0, N < 8 or not a multiple of 8, K < 1, Q < 1, or with a table
- * max_pages < 1, page_size < 1, num_rows < 0 or max_pages * page_size above 2^31 - 1),
+ * Errors: MLA_ERR_SHAPE (R < 0, N < 8, not a multiple of 8 or above 2^31 - 32769, K < 1, Q < 1,
+ * or with a table max_pages < 1, page_size < 1, num_rows < 0 or max_pages * page_size above
+ * 2^31 - 1),
  * MLA_ERR_NULL, MLA_ERR_ALIGN, MLA_ERR_LAUNCH. R = 0 launches nothing. Asynchronous on `stream`.
  */
 mla_status_t mla_topk_rows(const void* logits, const int32_t* row_ends, int R, int N, int K,

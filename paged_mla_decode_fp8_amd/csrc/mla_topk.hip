@@ -603,7 +603,8 @@ mla_status_t mla_topk_sparse_rows(const void* logits, const int32_t* end, int R,
                                   int max_pages, int page_size, int Q, int64_t num_rows,
                                   int32_t* rows_out, int32_t* valid_out, void* stream)
 {
-    if (R < 0 || N < 8 || N % 8 != 0 || K < 1 || Q < 1 || R > 0x7FFFFFFF)
+    // N below 2^31 - 32768: column arithmetic of the last span stays inside int
+    if (R < 0 || N < 8 || N % 8 != 0 || N > 0x7FFFFFFF - TK_SPAN || K < 1 || Q < 1)
         return MLA_ERR_SHAPE;
     if (block_table && (max_pages < 1 || page_size < 1 || num_rows < 0 ||
                         (int64_t)max_pages * page_size > 0x7FFFFFFF))

@@ -202,6 +202,9 @@ def test_topk_checks_arguments_without_launching():
     assert call(args(R=-1)) == SHAPE
     assert call(args(N=60)) == SHAPE           # not a multiple of 8
     assert call(args(N=0)) == SHAPE
+    assert call(args(N=0x7FFFFFF8)) == SHAPE   # the last span's columns would overflow int
+    assert call(args(N=0x7FFF8000)) == SHAPE
+    assert call(args(N=0x7FFF7FF8, R=0)) == OK   # the largest accepted N
     assert call(args(K=0)) == SHAPE
     assert call(args(Q=0)) == SHAPE
     assert call(args(tb=0x5000, mp=0)) == SHAPE
