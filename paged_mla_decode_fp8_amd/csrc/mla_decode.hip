@@ -626,6 +626,59 @@ __device__ inline float group_max(float v)
     return v;
 }
 
+// The exact E4M3 split of one 16-byte unit (8 bf16 query values) of a row whose power of two is
+// 2^k (sinv = 2^-k): hi = E4M3(q 2^k), lo = E4M3(q 2^k - hi) (|q 2^k| <= 448 and |q 2^k - hi| <=
+// 16, so neither rounding saturates), as {hi of values 0..3, hi of 4..7, lo of 0..3, lo of 4..7}.
+// gfx950's scaled conversions: bf16 / f32 -> E4M3 computes RNE(x / s) and E4M3 -> f32 computes
+// v * s (both exact for a power of two s; checked bit for bit against the plain conversions of
+// x / s and v * s on MI355X): hi, its value in q units hi 2^-k, the exact remainder
+// d = q - hi 2^-k and lo = E4M3(d 2^k). QE: the E4M3 query, lo = 0.
+template <bool QE>
+__device__ __forceinline__ v4i split_unit(const v4i raw, float sinv)
+{
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const uint32_t qa = (uint32_t)raw[2 * h], qb = (uint32_t)raw[2 * h + 1];   // q 4h .. 4h + 3
+        v2s hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2s{0, 0}, __builtin_bit_cast(v2bf, qa), sinv, false);
+        hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw, __builtin_bit_cast(v2bf, qb), sinv, true);
+        hi[h] = __builtin_bit_cast(uint32_t, hw);
+        const v2f b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi[h], sinv, false);
+        const v2f b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi[h], sinv, true);
+        const float d0 = bf16_to_f32(qa & 0xFFFF) - b01.x, d1 = bf16_to_f32(qa >> 16) - b01.y;
+        const float d2 = bf16_to_f32(qb & 0xFFFF) - b23.x, d3 = bf16_to_f32(qb >> 16) - b23.y;
+        v2s lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, d0, d1, sinv, false);
+        lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, d2, d3, sinv, true);
+        lo[h] = QE ? 0u : __builtin_bit_cast(uint32_t, lw);
+    }
+    return v4i{(int)hi[0], (int)hi[1], (int)lo[0], (int)lo[1]};
+}
+
+// Unit c (values 8 c .. 8 c + 7) of tile-set row r, split, into the QK waves' MFMA B operands at
+// qop: [tile][operand][lane][32 B], operands 0..3 the hi steps, 4..7 the lo steps, 8 the rope
+// step (k-groups 0, 1 carry hi, 2, 3 lo).
+__device__ __forceinline__ void store_unit(uint8_t* qop, int r, int c, const v4i hl)
+{
+    const int t = r >> 4, n16 = r & 15;
+    const int v0 = 8 * c;
+    int op_hi, op_lo, lane_hi, lane_lo, wi;
+    if (v0 < LATENT) {   // latent step st, k-group g: byte v0 % 32 of that lane's operand
+        const int st = v0 >> 7, g = (v0 >> 5) & 3;
+        op_hi = st;
+        op_lo = 4 + st;
+        lane_hi = lane_lo = n16 + 16 * g;
+        wi = v0 & 31;
+    } else {             // rope half: hi in k-group half, lo in k-group 2 + half
+        const int half = (v0 - LATENT) >> 5;
+        op_hi = op_lo = 8;
+        lane_hi = n16 + 16 * half;
+        lane_lo = n16 + 16 * (2 + half);
+        wi = (v0 - LATENT) & 31;
+    }
+    *reinterpret_cast<v2i*>(qop + ((t * 9 + op_hi) * 64 + lane_hi) * 32 + wi) = v2i{hl[0], hl[1]};
+    *reinterpret_cast<v2i*>(qop + ((t * 9 + op_lo) * 64 + lane_lo) * 32 + wi) = v2i{hl[2], hl[3]};
+}
+
 // The staged query rows -> the QK waves' MFMA B operands, by all 512 threads: per row the power
 // of two 2^k with max |q 2^k| <= 448 (k the largest such integer, 0 for a zero row), then the
 // exact E4M3 split hi = E4M3(q 2^k), lo = E4M3(q 2^k - hi) (|q 2^k| <= 448 and |q 2^k - hi| <= 16,
@@ -715,6 +768,70 @@ __device__ __forceinline__ void convert_q(uint8_t* smem, int tid)
     __syncthreads();   // the operands and the row maxima are in LDS
 }
 
+// With one or two tiles each QK wave stages and converts a quarter of the tile set's rows itself,
+// right as they land, while the PV waves issue block 0's row DMAs: the conversion leaves the
+// critical path of the short workloads (with four tiles the staged rows fill slot 1, so the
+// operands must replace them in place, which needs the whole workgroup's barriers). QK wave qw
+// owns rows RW qw .. RW qw + RW - 1 (RW = 4 T), staged at slot 1 + 1152 RW qw, unit c of its row
+// rl at 16 (72 rl + c); the operands go to slot 1 + 18432 T, after every staged row, in the
+// layout above.
+template <int T>
+constexpr bool OWN_Q = T <= 2;
+
+template <int T>
+__device__ inline void stage_q_own(const Params& p, uint8_t* smem, int64_t row0, int qw, int lane)
+{
+    constexpr int RW = 4 * T;
+    constexpr int NU = RW * 72;                       // 16-byte units of the wave's rows
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(p.q + (row0 + RW * qw) * ROW);
+    uint8_t* dst = smem + SLOT + 1152 * RW * qw;
+#pragma unroll
+    for (int i = 0; i < (NU + 63) / 64; i++) {        // 64 units per instruction (the last may be half)
+        const int u = 64 * i + lane;
+        if (u < NU) {
+            const int rl = u / 72, c = u - 72 * rl;
+            dma16(qbase + (int64_t)rl * (2 * ROW) + 16 * c, lds_addr(dst + 1024 * i));
+        }
+    }
+}
+
+template <int T, bool QE>
+__device__ __forceinline__ void convert_q_own(uint8_t* smem, int qw, int lane)
+{
+    using L = Smem<T>;
+    constexpr int RW = 4 * T;
+    constexpr int LPR = 64 / RW;                      // lanes per row: 16 (one tile), 8 (two)
+    constexpr int UPL = (72 + LPR - 1) / LPR;         // units per lane: 5, 9
+    const int rl = lane / LPR, li = lane % LPR;
+    const int r = RW * qw + rl;                       // row of the tile set
+    const uint8_t* src = smem + SLOT + 1152 * r;      // the wave's rows follow one another
+    v4i raw[UPL];
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < UPL; k++) {
+        const int c = li + LPR * k;
+        raw[k] = v4i{0, 0, 0, 0};
+        if (c < 72) {
+            raw[k] = *reinterpret_cast<const v4i*>(src + 16 * c);
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[k][d] & 0xFFFF)));
+                m = fmaxf(m, fabsf(bf16_to_f32((uint32_t)raw[k][d] >> 16)));
+            }
+        }
+    }
+    m = group_max<LPR>(m);
+    if (li == 0)
+        reinterpret_cast<float*>(smem + L::OFF_P)[r] = m;
+    const float sinv = ldexpf(1.f, -row_shift(m));
+#pragma unroll
+    for (int k = 0; k < UPL; k++) {
+        const int c = li + LPR * k;
+        if (c < 72)
+            store_unit(smem + SLOT + 18432 * T, r, c, split_unit<QE>(raw[k], sinv));
+    }
+}
+
 // The nine row DMA sources of subtile 2 pw + h of a block, from PV wave pw's pointer table (entry
 // 16 (k % 2) + 8 (k / 16) + (k % 16) / 2 holds key k of the wave's 32). Latent instruction i moves
 // keys 16 h + 2 i (lanes 0..31) and 16 h + 2 i + 1 (lanes 32..63), chunk (lane % 32) ^ key; the
@@ -780,8 +897,10 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     }
 
     __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's staged Q rows landed
-    lds_sync();                          // Q0: every staged row landed
-    if (w.nblk > 0)
+    if (OWN_Q<T> && w.nblk > 0)
+        convert_q_own<T, QE>(smem, qw, lane);
+    lds_sync();                          // Q0: every staged row (or every operand) is in LDS
+    if (!OWN_Q<T> && w.nblk > 0)
         convert_q<T, QE>(smem, qw * 64 + lane);
 
     // ---- the tiles' B operands (exact E4M3 hi + lo of q * 2^k) and row scales from LDS ----
@@ -793,7 +912,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         if (w.nblk > 0 && active) {
             const int t = qt0 + j;
             auto op = [&](int o) {
-                const int off = SLOT + ((t * 9 + o) * 64 + lane) * 32;
+                const int off = SLOT + (OWN_Q<T> ? 18432 * T : 0) + ((t * 9 + o) * 64 + lane) * 32;
                 return cat(lds_read16(smem, off), lds_read16(smem, off + 16));
             };
 #pragma unroll
@@ -1148,7 +1267,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
             key_ptrs(1, idx1);   // the table's reads for block 0 precede these writes (one wave)
     }
     lds_sync();   // Q0: the QK waves' staged query rows landed
-    if (w.nblk > 0)
+    if (!OWN_Q<T> && w.nblk > 0)
         convert_q<T, QE>(smem, 256 + pw * 64 + lane);
 
     // This lane's transposed V read of column chunk 8 pw + c, key half rb of subtile 2 grp + sp:
@@ -1521,7 +1640,10 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             int li = lane;   // lane-derived offsets are recomputed per item, not kept live
             asm volatile("" : "+v"(li));
             // the query rows go out before the key counts are read (they depend on g and ts only)
-            stage_q<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
+            if (OWN_Q<T>)
+                stage_q_own<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
+            else
+                stage_q<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
             Work w;
             item(pi, g, pre, w);
             if (g > sp.g_lo)
