@@ -609,14 +609,15 @@ __device__ inline int row_shift(float amax)
     return k < 126 ? k : 126;
 }
 
-// Maximum over each aligned group of N lanes (N = 8, 16 or 32; every lane of a group gets it): quad
-// swaps and the half-row mirror (8), the row mirror (16), the 16-lane row swap (32).
+// Maximum over each aligned group of N lanes (N = 4, 8, 16 or 32; every lane of a group gets it):
+// quad swaps (4), the half-row mirror (8), the row mirror (16), the 16-lane row swap (32).
 template <int N>
 __device__ inline float group_max(float v)
 {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
+    if (N >= 8)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
     if (N >= 16)
         v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true)));
     if (N >= 32) {
@@ -768,15 +769,18 @@ __device__ __forceinline__ void convert_q(uint8_t* smem, int tid)
     __syncthreads();   // the operands and the row maxima are in LDS
 }
 
-// With one or two tiles each QK wave stages and converts a quarter of the tile set's rows itself,
-// right as they land, while the PV waves issue block 0's row DMAs: the conversion leaves the
-// critical path of the short workloads (with four tiles the staged rows fill slot 1, so the
-// operands must replace them in place, which needs the whole workgroup's barriers). QK wave qw
-// owns rows RW qw .. RW qw + RW - 1 (RW = 4 T), staged at slot 1 + 1152 RW qw, unit c of its row
-// rl at 16 (72 rl + c); the operands go to slot 1 + 18432 T, after every staged row, in the
-// layout above.
+// Each QK wave stages and converts a quarter of the tile set's rows itself, right as they land,
+// while the PV waves issue block 0's row DMAs, with no workgroup barrier: QK wave qw owns rows
+// RW qw .. RW qw + RW - 1 (RW = 4 T), staged at slot 1 + 1152 RW qw, unit c of its row rl at
+// 16 (72 rl + c). With one or two tiles a wave's rows feed operands spread over the tile, so the
+// operands go to slot 1 + 18432 T, after every staged row. With four tiles a wave's rows are tile
+// qw, whose operands take exactly the bytes its rows were staged in: the wave reads all of them
+// before it writes any, so it converts in place. Not for the dense four-tile kernel: there the
+// 512-thread conversion after Q0 measured faster (its block loop's register allocation moves).
+template <int T, bool DENSE>
+constexpr bool OWN_Q = T <= 2 || !DENSE;
 template <int T>
-constexpr bool OWN_Q = T <= 2;
+constexpr int OPBASE = T == 4 ? 0 : 18432 * T;   // the operands' offset in slot 1
 
 template <int T>
 __device__ inline void stage_q_own(const Params& p, uint8_t* smem, int64_t row0, int qw, int lane)
@@ -800,8 +804,8 @@ __device__ __forceinline__ void convert_q_own(uint8_t* smem, int qw, int lane)
 {
     using L = Smem<T>;
     constexpr int RW = 4 * T;
-    constexpr int LPR = 64 / RW;                      // lanes per row: 16 (one tile), 8 (two)
-    constexpr int UPL = (72 + LPR - 1) / LPR;         // units per lane: 5, 9
+    constexpr int LPR = 64 / RW;                      // lanes per row: 16, 8, 4 (one, two, four tiles)
+    constexpr int UPL = (72 + LPR - 1) / LPR;         // units per lane: 5, 9, 18
     const int rl = lane / LPR, li = lane % LPR;
     const int r = RW * qw + rl;                       // row of the tile set
     const uint8_t* src = smem + SLOT + 1152 * r;      // the wave's rows follow one another
@@ -828,7 +832,7 @@ __device__ __forceinline__ void convert_q_own(uint8_t* smem, int qw, int lane)
     for (int k = 0; k < UPL; k++) {
         const int c = li + LPR * k;
         if (c < 72)
-            store_unit(smem + SLOT + 18432 * T, r, c, split_unit<QE>(raw[k], sinv));
+            store_unit(smem + SLOT + OPBASE<T>, r, c, split_unit<QE>(raw[k], sinv));
     }
 }
 
@@ -897,10 +901,10 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
     }
 
     __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's staged Q rows landed
-    if (OWN_Q<T> && w.nblk > 0)
+    if (OWN_Q<T, DENSE> && w.nblk > 0)
         convert_q_own<T, QE>(smem, qw, lane);
     lds_sync();                          // Q0: every staged row (or every operand) is in LDS
-    if (!OWN_Q<T> && w.nblk > 0)
+    if (!OWN_Q<T, DENSE> && w.nblk > 0)
         convert_q<T, QE>(smem, qw * 64 + lane);
 
     // ---- the tiles' B operands (exact E4M3 hi + lo of q * 2^k) and row scales from LDS ----
@@ -912,7 +916,7 @@ __device__ __forceinline__ void qk_role(const Params& p, uint8_t* smem, const Wo
         if (w.nblk > 0 && active) {
             const int t = qt0 + j;
             auto op = [&](int o) {
-                const int off = SLOT + (OWN_Q<T> ? 18432 * T : 0) + ((t * 9 + o) * 64 + lane) * 32;
+                const int off = SLOT + (OWN_Q<T, DENSE> ? OPBASE<T> : 0) + ((t * 9 + o) * 64 + lane) * 32;
                 return cat(lds_read16(smem, off), lds_read16(smem, off + 16));
             };
 #pragma unroll
@@ -1267,7 +1271,7 @@ __device__ __forceinline__ void pv_role(const Params& p, uint8_t* smem, const Wo
             key_ptrs(1, idx1);   // the table's reads for block 0 precede these writes (one wave)
     }
     lds_sync();   // Q0: the QK waves' staged query rows landed
-    if (!OWN_Q<T> && w.nblk > 0)
+    if (!OWN_Q<T, DENSE> && w.nblk > 0)
         convert_q<T, QE>(smem, 256 + pw * 64 + lane);
 
     // This lane's transposed V read of column chunk 8 pw + c, key half rb of subtile 2 grp + sp:
@@ -1640,7 +1644,7 @@ __global__ __launch_bounds__(THREADS) void mla_decode_kernel(const Params p)
             int li = lane;   // lane-derived offsets are recomputed per item, not kept live
             asm volatile("" : "+v"(li));
             // the query rows go out before the key counts are read (they depend on g and ts only)
-            if (OWN_Q<T>)
+            if (OWN_Q<T, DENSE>)
                 stage_q_own<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
             else
                 stage_q<T>(pi, smem, (int64_t)g * pi.rows_per_group + 16 * ts * T, wave, li);
